@@ -1,0 +1,87 @@
+"""Plain fp64 definition of the exact attention forward pass (oracle; test infrastructure only).
+
+What is computed (FlashAttention-2 digest, "Method — framework overview" flowchart and
+glossary): for each batch b and head h independently,
+
+    S   = scale * Q K^T                      (N x N scores)
+    S_ij = -inf  for j > i                   (causal only; the diagonal stays allowed)
+    m_i = max_j S_ij,  P_ij = exp(S_ij - m_i),  l_i = sum_j P_ij
+    O_i = (sum_j P_ij V_j) / l_i             (one division per row, at the end)
+    LSE_i = m_i + ln(l_i)                    (natural log of the sum of exponentials)
+
+The tiled, online-softmax algorithm on the pages reaches this same result up to
+rounding order (FlashAttention is exact attention, per the digest's title and
+findings), so the oracle is the definition itself: it materialises the full score
+rows in fp64 and never tiles the key axis. Rows are independent, so the work is
+split by query rows only (``row_chunk``) to bound memory; each chunk holds complete
+rows.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _as_f64(x) -> np.ndarray:
+    """Upcast a numpy array or a CPU torch tensor (any float dtype) to fp64 numpy."""
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach().to("cpu")
+        import torch  # local: the oracle works on numpy and only accepts torch inputs
+
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def attention_forward(q, k, v, causal: bool, scale: float, rows=None, heads=None,
+                      row_chunk: int = 1024):
+    """Exact attention forward in fp64.
+
+    Parameters
+    ----------
+    q, k, v : arrays of shape [B, H, N, d] (numpy or CPU torch, any float dtype).
+    causal  : mask keys j > i (query i may see keys 0..i).
+    scale   : the softmax scale, used as given (callers pass the same fp32 value the
+              device uses, upcast exactly).
+    rows    : optional 1-D array of query-row indices to evaluate (default: all rows).
+    heads   : optional list of (b, h) pairs to evaluate (default: all B*H heads).
+    row_chunk : number of query rows materialised at once.
+
+    Returns
+    -------
+    O   : fp64 array [B, H, R, d] (R = len(rows)); heads not requested are NaN.
+    LSE : fp64 array [B, H, R]; natural-log log-sum-exp of the scaled, masked scores.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    if rows.ndim != 1 or (rows.size and (rows.min() < 0 or rows.max() >= N)):
+        raise ValueError("rows must be a 1-D array of indices in [0, N)")
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    scale = float(scale)
+
+    O = np.full((B, H, rows.size, d), np.nan)
+    LSE = np.full((B, H, rows.size), np.nan)
+    key_index = np.arange(N)
+    for b, h in heads:
+        for c0 in range(0, rows.size, row_chunk):
+            r = rows[c0:c0 + row_chunk]
+            S = scale * (q[b, h, r, :] @ k[b, h].T)          # [len(r), N]
+            if causal:
+                S[key_index[None, :] > r[:, None]] = -np.inf
+            m = S.max(axis=1, keepdims=True)
+            P = np.exp(S - m)
+            l = P.sum(axis=1, keepdims=True)
+            O[b, h, c0:c0 + r.size] = (P @ v[b, h]) / l
+            LSE[b, h, c0:c0 + r.size] = (m + np.log(l))[:, 0]
+    return O, LSE
+
+
+def counted_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
+    """Forward FLOP count by the convention the pages' throughput figures use:
+    4*B*H*N^2*d (two N x N x d contractions), halved when causal."""
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
