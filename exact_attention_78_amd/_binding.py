@@ -1,0 +1,160 @@
+"""ctypes binding of libattn.so: the C entry points under the same names.
+
+Argument marshalling only: each function checks that the torch tensors it is given
+match what the C ABI expects (device, dtype, shape, contiguity), hands their device
+pointers and the current HIP stream to the library, and raises ``AttnError`` on a
+non-OK status. No step of the attention computation happens here, and there is no
+fallback: if the library is missing the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+_lib = None
+
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_LAUNCH"}
+
+# Exported symbols and their C signatures (mirrors include/attn.h).
+_P, _I64, _INT, _F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+SIGNATURES = {
+    "attn_fwd_bf16": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
+    "attn_fwd_f16": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
+    "attn_fwd_f32": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
+    "attn_fwd_fp8": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
+    "attn_quant_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
+    "attn_status_string": [_INT],
+    "attn_abi_version": [],
+}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({library().attn_status_string(status).decode()})")
+
+
+def library():
+    """Load libattn.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with exact_attention_78_amd.build.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "attn_status_string" else ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise AttnError(fn, status)
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _qkv_checks(q, k, v, dtype):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+        _require(t.is_cuda, f"{name} must be on a GPU")
+        _require(t.dtype == dtype, f"{name} must be {dtype}")
+        _require(t.dim() == 4 and t.shape == q.shape, f"{name} must be [B, H, N, d] like q")
+        _require(t.is_contiguous(), f"{name} must be contiguous")
+        _require(t.device == q.device, f"{name} must be on q's device")
+
+
+def _fwd(fn: str, dtype, q, k, v, causal: bool, scale, out=None, lse=None):
+    _qkv_checks(q, k, v, dtype)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o.shape == q.shape and o.dtype == dtype and o.is_contiguous() and o.device == q.device, "bad out")
+    _require(L.shape == (B, H, N) and L.dtype == torch.float32 and L.is_contiguous() and L.device == q.device,
+             "bad lse")
+    with torch.cuda.device(q.device):
+        st = getattr(library(), fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(),
+                                    B, H, N, d, int(bool(causal)), float(scale), _stream(q))
+    _check(fn, st)
+    return o, L
+
+
+def attn_fwd_bf16(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """bf16 exact attention forward; returns (O bf16 [B,H,N,d], LSE fp32 [B,H,N])."""
+    return _fwd("attn_fwd_bf16", torch.bfloat16, q, k, v, causal, scale, out, lse)
+
+
+def attn_fwd_f16(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """fp16 exact attention forward; returns (O fp16, LSE fp32)."""
+    return _fwd("attn_fwd_f16", torch.float16, q, k, v, causal, scale, out, lse)
+
+
+def attn_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """fp32 exact attention forward; returns (O fp32, LSE fp32)."""
+    return _fwd("attn_fwd_f32", torch.float32, q, k, v, causal, scale, out, lse)
+
+
+def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Dispatch on q.dtype to attn_fwd_{bf16,f16,f32}."""
+    fn = {torch.bfloat16: attn_fwd_bf16, torch.float16: attn_fwd_f16, torch.float32: attn_fwd_f32}.get(q.dtype)
+    _require(fn is not None, f"unsupported dtype {q.dtype}")
+    return fn(q, k, v, causal, scale, out, lse)
+
+
+def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=None, out=None, lse=None):
+    """fp8 (E4M3FN codes, uint8 tensors) attention forward with per-128-row block scales.
+    Returns (O bf16 [B,H,N,d], LSE fp32 [B,H,N])."""
+    _qkv_checks(q8, k8, v8, torch.uint8)
+    B, H, N, d = q8.shape
+    nblk = (N + 127) // 128
+    for name, s in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _require(s.dtype == torch.float32 and s.shape == (B, H, nblk) and s.is_contiguous() and s.device == q8.device,
+                 f"{name} must be fp32 [B, H, ceil(N/128)] on q8's device")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    _require(o.shape == (B, H, N, d) and o.dtype == torch.bfloat16 and o.is_contiguous(), "bad out")
+    _require(L.shape == (B, H, N) and L.dtype == torch.float32 and L.is_contiguous(), "bad lse")
+    with torch.cuda.device(q8.device):
+        st = library().attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
+                                    k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), L.data_ptr(), B, H, N, d,
+                                    int(bool(causal)), float(scale), _stream(q8))
+    _check("attn_fwd_fp8", st)
+    return o, L
+
+
+def attn_quant_fp8(x, signs=None, out=None, scales=None):
+    """Rotate (if ``signs`` is given) and block-quantise bf16 x [B,H,N,d] to E4M3FN codes.
+    Returns (codes uint8 [B,H,N,d], scales fp32 [B,H,ceil(N/128)])."""
+    _require(isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 4
+             and x.is_contiguous(), "x must be a contiguous bf16 [B, H, N, d] GPU tensor")
+    B, H, N, d = x.shape
+    nblk = (N + 127) // 128
+    if signs is not None:
+        _require(signs.dtype == torch.float32 and signs.shape == (d,) and signs.is_contiguous()
+                 and signs.device == x.device, "signs must be fp32 [d] on x's device")
+    x8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device) if out is None else out
+    sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device) if scales is None else scales
+    with torch.cuda.device(x.device):
+        st = library().attn_quant_fp8(x.data_ptr(), x8.data_ptr(), sc.data_ptr(),
+                                      None if signs is None else signs.data_ptr(), B, H, N, d, _stream(x))
+    _check("attn_quant_fp8", st)
+    return x8, sc

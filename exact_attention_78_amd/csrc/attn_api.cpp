@@ -1,0 +1,145 @@
+// C ABI of the attention library: host-side validation, then dispatch to the launchers.
+// Validation never calls into HIP, so a rejected call touches no device state.
+#include "attn.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by all entry points; writes the element count of one [B,H,N,d] tensor.
+attn_status_t check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int64_t* elems, int64_t* rows) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  int64_t bh, bhn, e;
+  if (__builtin_mul_overflow(B, H, &bh) || __builtin_mul_overflow(bh, N, &bhn) ||
+      __builtin_mul_overflow(bhn, d, &e) || e > INT64_MAX / 8)
+    return ATTN_ERR_INVALID_ARG;
+  if (N > INT32_MAX) return ATTN_ERR_INVALID_ARG;   // kernels index rows with 32-bit ints
+  *elems = e;
+  *rows = bhn;
+  return ATTN_OK;
+}
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+// Validation of the 16/32-bit forward entry points (element size esz bytes).
+attn_status_t check_fwd(const void* q, const void* k, const void* v, const void* o, const void* lse, int64_t B,
+                        int64_t H, int64_t N, int64_t d, float scale, size_t esz,
+                        int64_t (*workgroups)(int64_t, int64_t)) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  int64_t elems, rows;
+  attn_status_t st = check_shape(B, H, N, d, &elems, &rows);
+  if (st != ATTN_OK) return st;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (workgroups(B * H, N) > INT32_MAX) return ATTN_ERR_INVALID_ARG;   // shape checked: no overflow
+  const uintptr_t tb = (uintptr_t)elems * esz;
+  const Range rq{(uintptr_t)q, (uintptr_t)q + tb}, rk{(uintptr_t)k, (uintptr_t)k + tb},
+      rv{(uintptr_t)v, (uintptr_t)v + tb}, ro{(uintptr_t)o, (uintptr_t)o + tb},
+      rl{(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)rows * sizeof(float)};
+  if (overlaps(ro, rq) || overlaps(ro, rk) || overlaps(ro, rv) || overlaps(ro, rl)) return ATTN_ERR_INVALID_ARG;
+  if (overlaps(rl, rq) || overlaps(rl, rk) || overlaps(rl, rv)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                            int64_t N, int64_t d, int causal, float scale, void* stream) {
+  attn_status_t st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, 2, attn::max_workgroups_fwd16);
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, (hipStream_t)stream));
+}
+
+attn_status_t attn_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                           int64_t N, int64_t d, int causal, float scale, void* stream) {
+  attn_status_t st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, 2, attn::max_workgroups_fwd16);
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_fwd_f16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, (hipStream_t)stream));
+}
+
+attn_status_t attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int64_t B, int64_t H,
+                           int64_t N, int64_t d, int causal, float scale, void* stream) {
+  attn_status_t st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, 4, attn::max_workgroups_fwd32);
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_fwd_f32(q, k, v, o, lse, B * H, N, d, causal != 0, scale, (hipStream_t)stream));
+}
+
+attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                           const float* k_scale, const float* v_scale, void* o, float* lse, int64_t B, int64_t H,
+                           int64_t N, int64_t d, int causal, float scale, void* stream) {
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  int64_t elems, rows;
+  attn_status_t st = check_shape(B, H, N, d, &elems, &rows);
+  if (st != ATTN_OK) return st;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  const void* ptrs[8] = {q8, k8, v8, q_scale, k_scale, v_scale, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  if (d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (attn::max_workgroups_fwd8(B * H, N) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  const int64_t nblk = (N + 127) / 128;
+  const uintptr_t sb = (uintptr_t)(B * H * nblk) * sizeof(float);
+  const Range ro{(uintptr_t)o, (uintptr_t)o + (uintptr_t)elems * 2},
+      rl{(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)rows * sizeof(float)};
+  const Range ins[6] = {{(uintptr_t)q8, (uintptr_t)q8 + (uintptr_t)elems},
+                        {(uintptr_t)k8, (uintptr_t)k8 + (uintptr_t)elems},
+                        {(uintptr_t)v8, (uintptr_t)v8 + (uintptr_t)elems},
+                        {(uintptr_t)q_scale, (uintptr_t)q_scale + sb},
+                        {(uintptr_t)k_scale, (uintptr_t)k_scale + sb},
+                        {(uintptr_t)v_scale, (uintptr_t)v_scale + sb}};
+  if (overlaps(ro, rl)) return ATTN_ERR_INVALID_ARG;
+  for (const Range& r : ins)
+    if (overlaps(ro, r) || overlaps(rl, r)) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B * H, N, d, causal != 0, scale,
+                                       (hipStream_t)stream));
+}
+
+attn_status_t attn_quant_fp8(const void* x, uint8_t* x8, float* scales, const float* signs, int64_t B, int64_t H,
+                             int64_t N, int64_t d, void* stream) {
+  if (!x || !x8 || !scales) return ATTN_ERR_INVALID_ARG;
+  int64_t elems, rows;
+  attn_status_t st = check_shape(B, H, N, d, &elems, &rows);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(scales) || (signs && !aligned16(signs)))
+    return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (attn::max_workgroups_quant(B * H, N) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  const int64_t nblk = (N + 127) / 128;
+  const Range rx{(uintptr_t)x, (uintptr_t)x + (uintptr_t)elems * 2}, r8{(uintptr_t)x8, (uintptr_t)x8 + (uintptr_t)elems},
+      rs{(uintptr_t)scales, (uintptr_t)scales + (uintptr_t)(B * H * nblk) * sizeof(float)},
+      rg{(uintptr_t)signs, (uintptr_t)signs + (signs ? (uintptr_t)d * sizeof(float) : 0)};
+  if (overlaps(r8, rx) || overlaps(r8, rs) || overlaps(rs, rx)) return ATTN_ERR_INVALID_ARG;
+  if (signs && (overlaps(rg, r8) || overlaps(rg, rs))) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_quant_fp8(x, x8, scales, signs, B * H, N, d, (hipStream_t)stream));
+}
+
+const char* attn_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types, MFMA and
+// LDS-transpose wrappers, cross-half lane exchange and the XCD-aware workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// Element type tags for the 16-bit paths.
+struct Bf16Tag {};
+struct F16Tag {};
+
+// 32x32x16 MFMA, fp32 accumulate. Lane l holds A[l%32][(l/32)*8 + s] and
+// B[(l/32)*8 + s][l%32] (s = 0..7); the result lane l holds C[(r/4)*8 + (l/32)*4 + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(Bf16Tag, u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(F16Tag, u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 values to one packed 16-bit pair, round to nearest even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack2(Bf16Tag, float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ uint32_t pack2(F16Tag, float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// Combine a value held by lane l with the one held by lane l^32. v_permlane32_swap
+// exchanges the upper 32 lanes of its first register with the lower 32 lanes of its
+// second; with both registers holding x, one ends up with this lane's own value and
+// the other with its partner's, in an order that depends on the half, so only a
+// symmetric combination of the two is used. (Inline asm keeps the two registers
+// distinct: the builtin's result is folded wrongly when both operands are the same.)
+__device__ __forceinline__ void permlane32_swap_pair(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float a = x, b = x;
+  permlane32_swap_pair(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float add_halves(float x) {
+  float a = x, b = x;
+  permlane32_swap_pair(a, b);
+  return a + b;
+}
+
+// LDS transpose read of 4 x 16-bit elements. Within each 16-lane group, lane i receives
+// element (i % 4) of the 8-byte segments addressed by lanes i/4, i/4+4, i/4+8, i/4+12.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup w runs on XCD w % 8).
+// Renumber them so that each XCD walks one contiguous range of logical ids: consecutive
+// logical ids share a (batch, head) and therefore its K/V in that XCD's L2.
+__device__ __forceinline__ int xcd_logical_id(int w, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int xcd = w % 8, loc = w / 8;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+}
+
+}  // namespace attn

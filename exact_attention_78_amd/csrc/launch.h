@@ -1,0 +1,28 @@
+// Internal launchers behind the C ABI. Arguments are already validated by the caller
+// (attn_api.cpp); each returns the hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
+                           int64_t d, bool causal, float scale, hipStream_t stream);
+hipError_t launch_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
+                          int64_t d, bool causal, float scale, hipStream_t stream);
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int64_t BH, int64_t N,
+                          int64_t d, bool causal, float scale, hipStream_t stream);
+hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* sq, const float* sk,
+                          const float* sv, void* o, float* lse, int64_t BH, int64_t N, int64_t d, bool causal,
+                          float scale, hipStream_t stream);
+hipError_t launch_quant_fp8(const void* x, uint8_t* x8, float* scales, const float* signs, int64_t BH, int64_t N,
+                            int64_t d, hipStream_t stream);
+
+// Workgroup counts of the launches above (validated against the 32-bit grid limit).
+int64_t max_workgroups_fwd16(int64_t BH, int64_t N);
+int64_t max_workgroups_fwd32(int64_t BH, int64_t N);
+int64_t max_workgroups_fwd8(int64_t BH, int64_t N);
+int64_t max_workgroups_quant(int64_t BH, int64_t N);
+
+}  // namespace attn

@@ -1,0 +1,111 @@
+/*
+ * attn.h — C ABI of the exact attention forward library for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (all entry points). For every batch b and head h independently, with
+ * Q, K, V the [N, d] slices of that head:
+ *
+ *     O   = softmax(scale * Q K^T [+ causal mask]) V          (row-wise softmax)
+ *     LSE = log(sum_j exp(scale * q_i . k_j))  over the keys row i may see
+ *
+ * This is exact attention as defined in "FlashAttention-2: faster attention with better
+ * parallelism and work partitioning" (digest, irregular6612.github.io): its framework-
+ * overview flowchart streams K/V tiles through an online softmax, rescales once at the
+ * end and writes O plus one log-sum-exp per row; its glossary defines the log-sum-exp
+ * as the log of the sum of exponentials (natural log here). The causal mask lets query
+ * row i see keys j <= i; key tiles entirely above the diagonal are never loaded (the
+ * digest's key-components list: mask only boundary blocks, skip the strictly upper ones).
+ * Inputs are low precision and every contraction accumulates in fp32 ("Triton 07: Flash
+ * Attention v3", Method, item 3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Layout: Q, K, V and O are contiguous row-major [B, H, N, d] (row stride d elements);
+ *    LSE is contiguous fp32 [B, H, N]. Per-block fp8 scales are fp32 [B, H, ceil(N/128)].
+ *  - Ownership: every pointer is caller-owned device memory on the current HIP device.
+ *    The library allocates nothing, frees nothing and keeps no state between calls; calls
+ *    are reentrant. Tensor pointers must be 16-byte aligned.
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without synchronising. A device fault surfaces at the caller's
+ *    next synchronisation on that stream.
+ *  - Validation happens on the host, before any HIP call, and on failure nothing is
+ *    enqueued:
+ *      ATTN_ERR_INVALID_ARG  a NULL pointer, B/H/N < 1, a scale that is not finite and
+ *                            > 0, a pointer not 16-byte aligned, an element count that
+ *                            overflows int64, or an output range overlapping an input
+ *                            or the other output;
+ *      ATTN_ERR_UNSUPPORTED  d not in {64, 128} (fp8 entry points: d = 128 only);
+ *      ATTN_ERR_LAUNCH       the kernel launch itself failed (hipGetLastError).
+ *  - Numbers: inputs with NaN or Inf give undefined outputs (not checked on the device).
+ *    Any N >= 1 is accepted; partial tiles are masked.
+ *  - Scale: pass the softmax scale as the fp32 value the caller wants (1/sqrt(d) is
+ *    usual); it is used as given.
+ */
+#ifndef EXACT_ATTENTION_ATTN_H
+#define EXACT_ATTENTION_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,
+  ATTN_ERR_UNSUPPORTED = 2,
+  ATTN_ERR_LAUNCH = 3
+} attn_status_t;
+
+#define ATTN_ABI_VERSION 1
+
+/* bf16 Q/K/V in, bf16 O out (round to nearest even), fp32 LSE out. P is rounded to
+ * bf16 before the P.V contraction; both contractions accumulate in fp32. */
+attn_status_t attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                            void* stream);
+
+/* fp16 Q/K/V in, fp16 O out; as attn_fwd_bf16 with fp16 in place of bf16. */
+attn_status_t attn_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                           void* stream);
+
+/* fp32 Q/K/V in, fp32 O out: scores, probabilities and both contractions stay in fp32. */
+attn_status_t attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                           void* stream);
+
+/* fp8 attention ("8.3 FlashAttention-3", section 5: fp8 inputs with per-block scales).
+ * q8/k8/v8 are OCP E4M3FN codes [B, H, N, d] (d = 128); q_scale/k_scale/v_scale are the
+ * fp32 scales of each 128-row block, so the value of a code x in block t is
+ * decode(x) * scale[b, h, t]. O is bf16 [B, H, N, d], LSE fp32 [B, H, N]. Scores
+ * accumulate e4m3 x e4m3 products in fp32 and are scaled by q_scale * k_scale * scale;
+ * P is rounded to E4M3 (after a per-head power-of-two prescale that keeps it clear of
+ * the subnormal range) for the P.V contraction, which accumulates in fp32. */
+attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                           const float* q_scale, const float* k_scale, const float* v_scale,
+                           void* o, float* lse,
+                           int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                           void* stream);
+
+/* fp8 input preparation ("8.3 FlashAttention-3", sections 5.1 and 5.2). x is bf16
+ * [B, H, N, d] (d in {64, 128}). If `signs` (fp32 [d], every entry +1 or -1) is not
+ * NULL, each row is first rotated: x <- fp32((x * signs) H_d) * fp32(1/sqrt(d)), with
+ * H_d Sylvester's Hadamard matrix applied as the fast Walsh-Hadamard butterfly in fp32.
+ * With signs == NULL the rows are quantised unrotated (used for V). Then, per block of
+ * 128 rows of one (b, h): scale = fp32(amax / 448) (1 if the block is all zero), and
+ * each code is the E4M3FN value nearest to clamp(fp32(x / scale), -448, 448), ties to
+ * even. Writes x8 (uint8 [B, H, N, d]) and scales (fp32 [B, H, ceil(N/128)]). */
+attn_status_t attn_quant_fp8(const void* x, uint8_t* x8, float* scales, const float* signs,
+                             int64_t B, int64_t H, int64_t N, int64_t d, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* attn_status_string(attn_status_t s);
+
+/* Returns ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_ATTN_H */

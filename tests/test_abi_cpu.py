@@ -1,0 +1,120 @@
+"""The C-ABI library loads on the host, exports every symbol include/attn.h declares,
+and rejects bad arguments on the host before any HIP call (CPU only).
+
+Every call below carries at least one defect that the host-side validation must catch,
+so no kernel is ever launched: the fake addresses are never dereferenced.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import exact_attention_78_amd as ea
+from exact_attention_78_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+
+# These calls use fake addresses: run them only where no GPU is present, so that a
+# validation bug can never turn one into a real launch.
+no_gpu_only = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="fake-pointer validation runs on GPU-less hosts")
+# distinct, 16-byte aligned, far-apart fake device addresses (never dereferenced)
+A = [(i + 1) << 40 for i in range(8)]
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:attn_status_t|const char\*|int)\s+(attn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ea.library()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = header_functions()
+    assert set(names) == {"attn_fwd_bf16", "attn_fwd_f16", "attn_fwd_f32", "attn_fwd_fp8", "attn_quant_fp8",
+                          "attn_status_string", "attn_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _binding.SIGNATURES, n
+
+
+def test_abi_version_and_status_strings(lib):
+    ver = int(re.search(r"#define ATTN_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.attn_abi_version() == ver
+    for s in range(4):
+        assert lib.attn_status_string(s)
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+FWD16 = ["attn_fwd_bf16", "attn_fwd_f16", "attn_fwd_f32"]
+
+
+def call_fwd(lib, fn, q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=2, N=64, d=64, causal=1, scale=0.125):
+    return getattr(lib, fn)(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+
+
+@no_gpu_only
+@pytest.mark.parametrize("fn", FWD16)
+@pytest.mark.parametrize("defect,expect", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
+    (dict(lse=None), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID),
+    (dict(d=0), INVALID), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(d=32), UNSUPPORTED),
+    (dict(scale=0.0), INVALID), (dict(scale=-0.5), INVALID), (dict(scale=math.nan), INVALID),
+    (dict(scale=math.inf), INVALID), (dict(q=A[0] + 2), INVALID), (dict(o=A[3] + 8), INVALID),
+    (dict(lse=A[4] + 4), INVALID), (dict(o=A[0]), INVALID), (dict(o=A[2] + 16), INVALID),
+    (dict(lse=A[1]), INVALID), (dict(lse=A[3] + 64), INVALID),
+    (dict(B=1 << 31, H=1 << 31, N=1 << 20), INVALID), (dict(N=(1 << 31) + 64), INVALID),
+])
+def test_fwd_validation(lib, fn, defect, expect):
+    assert call_fwd(lib, fn, **defect) == expect
+
+
+@no_gpu_only
+@pytest.mark.parametrize("defect,expect", [
+    (dict(q8=None), INVALID), (dict(sk=None), INVALID), (dict(o=None), INVALID), (dict(d=64), UNSUPPORTED),
+    (dict(N=0), INVALID), (dict(scale=0.0), INVALID), (dict(sv=A[5] + 4), INVALID), (dict(o=A[0]), INVALID),
+    (dict(lse=A[3]), INVALID), (dict(o=A[7] - 16), INVALID),
+])
+def test_fp8_validation(lib, defect, expect):
+    args = dict(q8=A[0], k8=A[1], v8=A[2], sq=A[3], sk=A[4], sv=A[5], o=A[6], lse=A[7], B=1, H=1, N=256, d=128,
+                causal=1, scale=0.0884)
+    args.update(defect)
+    assert lib.attn_fwd_fp8(*args.values(), None) == expect
+
+
+@no_gpu_only
+@pytest.mark.parametrize("defect,expect", [
+    (dict(x=None), INVALID), (dict(x8=None), INVALID), (dict(sc=None), INVALID), (dict(d=32), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED), (dict(B=0), INVALID), (dict(signs=A[3] + 4), INVALID), (dict(x8=A[0]), INVALID),
+    (dict(sc=A[1] + 32), INVALID),
+])
+def test_quant_validation(lib, defect, expect):
+    args = dict(x=A[0], x8=A[1], sc=A[2], signs=A[3], B=1, H=1, N=256, d=128)
+    args.update(defect)
+    assert lib.attn_quant_fp8(*args.values(), None) == expect
+
+
+def test_binding_rejects_host_tensors_before_calling():
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.attn_fwd_bf16(x, x, x)
+    with pytest.raises(ValueError):
+        ea.fwd(x.double(), x.double(), x.double())
+    with pytest.raises(ValueError):
+        ea.attn_quant_fp8(x)
+
+
+def test_binding_raises_when_library_missing(monkeypatch):
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", "/nonexistent/libattn.so")
+    with pytest.raises(RuntimeError):
+        _binding.library()

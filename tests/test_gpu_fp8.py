@@ -1,0 +1,154 @@
+"""GPU parity of the fp8 path: the Hadamard + E4M3 block quantiser (bit-exact against
+the oracle's quantiser) and the fp8 attention forward (against the fp64 oracle run on
+the dequantised inputs, O max-abs error <= 1e-1 and |dLSE| <= 1e-3 * max(1, |LSE|)).
+
+The quantiser decides integer codes, so it must match the oracle exactly: both take the
+same fp32 roundings (butterfly adds, the 1/sqrt(d) product, amax/448 and x/scale).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_78_amd import attn_fwd_fp8, attn_quant_fp8, inputs
+from oracle import fp8 as ofp8
+from oracle.attention import attention_forward
+
+pytestmark = pytest.mark.gpu
+
+O_TOL_FP8 = 1e-1
+LSE_REL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_activations(x32):
+    """Round fp32 draws to the bf16 activations both sides consume."""
+    t = inputs.to_torch(x32, "bf16")
+    return t, t.float().numpy()
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("rotate", [True, False])
+@pytest.mark.parametrize("N", [300, 128, 1])
+def test_quantiser_bit_exact(d, rotate, N):
+    say(f"case quant d={d} rotate={rotate} N={N}")
+    q, _, _, signs = inputs.draw_fp8_workload(20 + N % 13, 2, 3, N, d)
+    tx, x = bf16_activations(q)
+    if N >= 256:
+        tx[1, 2, 128:256] = 0                     # an all-zero block
+        x = tx.float().numpy()
+    sg = torch.from_numpy(signs).cuda() if rotate else None
+    codes, scales = attn_quant_fp8(tx.cuda(), sg)
+    torch.cuda.synchronize()
+    xr = ofp8.rotate_f32(x, signs) if rotate else x
+    ref_codes, ref_scales = ofp8.quantize_blocks(xr)
+    np.testing.assert_array_equal(scales.cpu().numpy(), ref_scales)
+    got = codes.cpu().numpy()
+    bad = np.count_nonzero(got != ref_codes)
+    say(f"  codes differing: {bad} of {got.size}")
+    assert bad == 0
+
+
+def test_quantiser_full_size_c5_sampled_heads():
+    w = inputs.WORKLOADS["C5"]
+    say("case quant C5 full size")
+    q, k, v, signs = inputs.draw_fp8_workload(w.wid, w.B, w.H, w.N, w.d)
+    sg = torch.from_numpy(signs).cuda()
+    for name, x32, rot in (("q", q, True), ("k", k, True), ("v", v, False)):
+        tx, x = bf16_activations(x32)
+        codes, scales = attn_quant_fp8(tx.cuda(), sg if rot else None)
+        torch.cuda.synchronize()
+        for b, h in ((0, 0), (w.B - 1, w.H - 1), (1, 5)):
+            xs = x[b:b + 1, h:h + 1]
+            xr = ofp8.rotate_f32(xs, signs) if rot else xs
+            rc, rs = ofp8.quantize_blocks(xr)
+            np.testing.assert_array_equal(scales[b:b + 1, h:h + 1].cpu().numpy(), rs)
+            np.testing.assert_array_equal(codes[b:b + 1, h:h + 1].cpu().numpy(), rc)
+        say(f"  {name}: sampled heads bit-exact")
+
+
+def oracle_inputs(wid, B, H, N, d):
+    q, k, v, signs = inputs.draw_fp8_workload(wid, B, H, N, d)
+    xs = [bf16_activations(t)[1] for t in (q, k, v)]
+    p = ofp8.prepare_fp8(*xs, signs)
+    deq = [ofp8.dequantize_blocks(p[c], p[s]) for c, s in (("q8", "sq"), ("k8", "sk"), ("v8", "sv"))]
+    return p, deq, xs, signs
+
+
+def run_fp8(p, causal, scale):
+    t = {key: torch.from_numpy(np.ascontiguousarray(val)).cuda() for key, val in p.items()}
+    o, lse = attn_fwd_fp8(t["q8"], t["k8"], t["v8"], t["sq"], t["sk"], t["sv"], causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def compare(O, L, Oref, Lref, label):
+    assert np.isfinite(O).all() and np.isfinite(L).all()
+    eo = np.abs(O - Oref).max()
+    el = (np.abs(L - Lref) / np.maximum(1, np.abs(Lref))).max()
+    say(f"  {label}: max|dO|={eo:.3e} max rel dLSE={el:.3e}")
+    assert eo <= O_TOL_FP8
+    assert el <= LSE_REL
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", [(1, 2, 1000, 128), (2, 2, 256, 128), (1, 1, 77, 128), (1, 1, 1, 128)])
+def test_fp8_attention_small(shape, causal):
+    B, H, N, d = shape
+    say(f"case fp8 attention shape={shape} causal={causal}")
+    p, deq, _, _ = oracle_inputs(30 + N % 11, B, H, N, d)
+    scale = inputs.softmax_scale(d)
+    O, L = run_fp8(p, causal, scale)
+    Oref, Lref = attention_forward(*deq, causal, scale)
+    compare(O, L, Oref, Lref, f"fp8 {shape} causal={causal}")
+
+
+def test_fp8_attention_c5_sampled():
+    w = inputs.WORKLOADS["C5"]
+    say("case fp8 attention C5 full size")
+    p, deq, _, _ = oracle_inputs(w.wid, w.B, w.H, w.N, w.d)
+    O, L = run_fp8(p, True, w.scale)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 4095, 4096, w.N - 1], np.random.default_rng(5).integers(0, w.N, 96)]))
+    heads = [(0, 0), (1, 15), (1, 3)]
+    Oref, Lref = attention_forward(*deq, True, w.scale, rows=rows, heads=heads)
+    idx = tuple(np.array(heads).T)
+    compare(O[:, :, rows][idx], L[:, :, rows][idx], Oref[idx], Lref[idx], "C5 sampled")
+
+
+def test_fp8_end_to_end_gpu_quantiser():
+    # GPU quantiser -> GPU fp8 attention, against oracle quantiser -> oracle attention.
+    B, H, N, d = 1, 2, 640, 128
+    p, deq, xs, signs = oracle_inputs(41, B, H, N, d)
+    sg = torch.from_numpy(signs).cuda()
+    tq, tk, tv = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in xs)
+    q8, sq = attn_quant_fp8(tq, sg)
+    k8, sk = attn_quant_fp8(tk, sg)
+    v8, sv = attn_quant_fp8(tv, None)
+    o, lse = attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=True)
+    torch.cuda.synchronize()
+    Oref, Lref = attention_forward(*deq, True, inputs.softmax_scale(d))
+    compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), Oref, Lref, "end-to-end")
+
+
+def test_rotation_lowers_fp8_error_with_outliers():
+    # Direction of the incoherent-processing claim ("8.3 FlashAttention-3", section 5.2):
+    # with outlier channels shared by Q and K, the fp8 path's error against exact
+    # attention on the unquantised inputs is lower with the Hadamard rotation than without.
+    B, H, N, d = 1, 4, 1024, 128
+    q, k, v, signs = inputs.draw_fp8_workload(50, B, H, N, d)
+    xs = [bf16_activations(t)[1] for t in (q, k, v)]
+    scale = inputs.softmax_scale(d)
+    Oexact, _ = attention_forward(*xs, True, scale)
+    errs = {}
+    for rot in (True, False):
+        p = ofp8.prepare_fp8(*xs, signs, rotate=rot)
+        O, _ = run_fp8(p, True, scale)
+        errs[rot] = np.sqrt(np.mean((O - Oexact) ** 2))
+    say(f"  RMSE with rotation {errs[True]:.4e}, without {errs[False]:.4e}, ratio {errs[False] / errs[True]:.2f}")
+    assert errs[True] < errs[False]
