@@ -33,6 +33,7 @@ constexpr int kBM = 128;      // query rows per workgroup
 constexpr int kBN = 64;       // keys per tile
 constexpr int kWaves = 4;     // 32 query rows per wave
 constexpr int kThreads = kWaves * 64;
+constexpr float kTau = 8.0f;  // lazy-rescale threshold for the running max, in log2 units
 
 // LDS swizzles: 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
 // K is read 32 rows x one chunk per instruction; V is read as 8 rows x 4 chunks
@@ -48,13 +49,12 @@ template <> struct Swz<64> {
 };
 
 template <typename Tag, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int total_wg, float scale,
     float c /* scale * log2(e) */) {
   constexpr int NCH = D / 8;                        // 16-byte chunks per row
   constexpr int TILE = kBN * D;                     // elements per K (or V) tile
-  constexpr int CH_PER_THREAD = kBN * NCH / kThreads;
   constexpr int NSTEP = D / 16;                     // MFMA k-steps over the head dim
   constexpr int NKB = kBN / 32;                     // 32-key blocks per tile
   constexpr int NDB = D / 32;                       // 32-wide head-dim blocks of O
@@ -93,37 +93,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const int wave_kt_end = CAUSAL ? min(kt_end, (q0 + 31) / kBN + 1) : kt_end;
   const bool wave_live = q0 < N;
 
-  // Global -> register staging of one K/V tile: thread handles chunks tid + i*kThreads.
-  u32x4 kst[CH_PER_THREAD], vst[CH_PER_THREAD];
-  auto load_tile = [&](int kt) {
+  // Direct global -> LDS loads of one K/V tile (global_load_lds_dwordx4: no VGPR staging).
+  // Each wave instruction fills 1 KiB of LDS, 16 bytes per lane at consecutive addresses;
+  // the lane therefore fetches the global chunk that the swizzle places at its slot.
+  // Rows past the end of the sequence re-read the last row: their scores are masked and
+  // their probabilities are zero, so any finite data will do.
+  constexpr int ROW_BYTES = D * 2;
+  constexpr int LOADS_PER_WAVE = TILE * 2 / 1024 / kWaves;
+  auto issue_tile_loads = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < CH_PER_THREAD; ++i) {
-      const int idx = tid + i * kThreads;
-      const int r = idx / NCH, ch = idx % NCH;
-      const int key = kt * kBN + r;
-      if (key < N) {
-        kst[i] = *(const u32x4*)(Kh + (int64_t)key * D + ch * 8);
-        vst[i] = *(const u32x4*)(Vh + (int64_t)key * D + ch * 8);
-      } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH_PER_THREAD; ++i) {
-      const int idx = tid + i * kThreads;
-      const int r = idx / NCH, ch = idx % NCH;
-      *(u32x4*)(&smem[buf][0][r * D + ((ch ^ Swz<D>::k(r)) * 8)]) = kst[i];
-      *(u32x4*)(&smem[buf][1][r * D + ((ch ^ Swz<D>::v(r)) * 8)]) = vst[i];
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+      const int slot = (wave * LOADS_PER_WAVE + i) * 1024 + lane * 16;   // byte offset in the tile
+      const int r = slot / ROW_BYTES, phys = (slot % ROW_BYTES) / 16;
+      const int key = min(kt * kBN + r, N - 1);
+      const int64_t goff = (int64_t)key * D;
+      const uint16_t* gk = Kh + goff + ((phys ^ Swz<D>::k(r)) * 8);
+      const uint16_t* gv = Vh + goff + ((phys ^ Swz<D>::v(r)) * 8);
+      uint16_t* lk = &smem[buf][0][(wave * LOADS_PER_WAVE + i) * 512];
+      uint16_t* lv = &smem[buf][1][(wave * LOADS_PER_WAVE + i) * 512];
+      __builtin_amdgcn_global_load_lds((const void*)gk, (__attribute__((address_space(3))) void*)lk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)gv, (__attribute__((address_space(3))) void*)lv, 16, 0, 0);
     }
   };
 
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;   // running max of raw scores q.k for this lane's row
+  // Running max in log2 units (score * scale * log2 e). It is raised only when a tile's
+  // max exceeds it by more than kTau, so most tiles skip the O rescale; probabilities are
+  // then bounded by 2^kTau, which bf16/fp16 P and the fp32 sums hold exactly as well.
+  float M = -INFINITY;
   float l_part = 0.f;        // running sum over this lane's half of the keys
 
   // Lane roles in the V transpose reads.
@@ -131,13 +130,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
   const int tr_row = (g16 / 2) * 4 + i16 / 4;          // + kb*32 + t*16 (+8)
   const int tr_col = 16 * (g16 % 2) + 4 * (i16 % 4);   // + db*32
 
-  load_tile(0);
-  store_tile(0);
+  issue_tile_loads(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int kt = 0; kt < kt_end; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < kt_end) load_tile(kt + 1);
+    if (kt + 1 < kt_end) issue_tile_loads(kt + 1, buf ^ 1);
 
     if (wave_live && kt < wave_kt_end) {
       const uint16_t* Ks = smem[buf][0];
@@ -168,17 +167,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
             if (masked) sacc[kb][r] = -INFINITY;
           }
       }
-      // ---- online softmax (exp2, running max, deferred normalisation)
+      // ---- online softmax (exp2, lazily raised running max, deferred normalisation)
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = max_halves(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float mc = m_new * c;
-      const float alpha = fast_exp2(m_run * c - mc);
-      m_run = m_new;
+      mx = max_halves(mx) * c;
+      if (__builtin_amdgcn_ballot_w64(mx > M + kTau) != 0) {
+        const float M_new = fmaxf(M, mx);
+        const float alpha = fast_exp2(M - M_new);
+        M = M_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      }
       float lsum = 0.f;
       u32x4 pk[NKB][2];
 #pragma unroll
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(__builtin_fmaf(sacc[kb][r], c, -mc));
+          p[r] = fast_exp2(__builtin_fmaf(sacc[kb][r], c, -M));
           lsum += p[r];
         }
 #pragma unroll
@@ -194,9 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
           pk[kb][t] = u32x4{pack2(Tag{}, p[t * 8 + 0], p[t * 8 + 1]), pack2(Tag{}, p[t * 8 + 2], p[t * 8 + 3]),
                             pack2(Tag{}, p[t * 8 + 4], p[t * 8 + 5]), pack2(Tag{}, p[t * 8 + 6], p[t * 8 + 7])};
       }
-      l_part = l_part * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      l_part += lsum;
       // ---- O^T += V^T P^T
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       }
     }
 
-    if (kt + 1 < kt_end) store_tile(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(
       u32x2 w = {pack2(Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv), pack2(Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
       *(u32x2*)(Orow + d) = w;
     }
-  if (half == 0) LSE[(int64_t)bh * N + qrow] = m_run * scale + __builtin_log2f(l_tot) * kLn2;
+  if (half == 0) LSE[(int64_t)bh * N + qrow] = (M + __builtin_log2f(l_tot)) * kLn2;
 }
 
 template <typename Tag, int D, bool CAUSAL>

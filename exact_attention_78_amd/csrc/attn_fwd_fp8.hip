@@ -11,14 +11,14 @@
 //   S^T = K Q^T with v_mfma_f32_32x32x64_f8f6f4 on the raw codes; the block scales and
 //   scale*log2(e) are one per-tile factor c_t = scale*log2e*sq*sk applied inside the
 //   exp2 argument (the running max is kept in these log2 units).
-//   P is produced directly pre-multiplied by sv_t * 2^k: exp2(s*c_t - (m - log2(sv_t) - k)).
-//   k is a per-head power of two chosen from that head's largest V scale so that the
-//   largest possible value (P = 1) stays at or below 224, i.e. inside E4M3's range with
-//   room to spare, and small probabilities stay clear of the subnormal range. Those
-//   values are rounded to E4M3 (v_cvt_pk_fp8_f32) and fed to the P.V MFMA against the
-//   raw V codes, so the per-block V scale costs nothing extra. The row sum l is
-//   accumulated from the unrounded fp32 probabilities; the epilogue divides by
-//   l * 2^k once.
+//   P is produced as 2^8 * P, so that the row's largest probability (1) is exactly 256
+//   in E4M3 and the smallest ones stay clear of the subnormal range; it is rounded to
+//   E4M3 (v_cvt_pk_fp8_f32) and fed to the P.V MFMA against the raw V codes. The V block
+//   scale is applied in fp32: the accumulator is kept in units of the current tile's V
+//   scale, so moving to a tile with another scale multiplies it by the old/new ratio,
+//   folded into the online-softmax rescale factor. The row sum l is accumulated from the
+//   unrounded fp32 probabilities; the epilogue multiplies by the last V scale and
+//   divides by l once.
 //   V^T is gathered with ds_read_b64_tr_b8 (8-bit LDS transpose reads) in the key order
 //   the S^T accumulators give P.
 #include "device_common.h"
@@ -32,6 +32,7 @@ constexpr int kBM = 128;
 constexpr int kBN = 64;
 constexpr int kThreads = 256;
 constexpr int kScaleRows = 128;
+constexpr float kPShift = 8.0f;   // P enters the P.V MFMA as 2^8 * P
 
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 
@@ -73,13 +74,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   const uint8_t* Vh = V + head_off;
   const float* sk = SK + (int64_t)bh * nblk;
   const float* sv = SV + (int64_t)bh * nblk;
-
-  // per-head power of two for P: largest V scale of the head
-  float maxsv = 0.f;
-  for (int t = lane; t < nblk; t += 64) maxsv = fmaxf(maxsv, sv[t]);
-#pragma unroll
-  for (int off = 32; off >= 1; off /= 2) maxsv = fmaxf(maxsv, __shfl_xor(maxsv, off));
-  const int kexp = (int)floorf(__builtin_log2f(224.0f / maxsv));
 
   const int q0 = mt * kBM + wave * 32;
   const int qrow = q0 + l32;
@@ -134,7 +128,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;   // running max in log2 units (score * scale * log2e)
-  float l_part = 0.f;
+  float l_part = 0.f;        // sum of 2^8 * P over this lane's half of the keys
+  float sv_cur = 1.f;        // V scale whose units oacc is kept in
 
   // lane roles in the V transpose reads
   const int g16 = lane / 16, i16 = lane % 16;
@@ -156,8 +151,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       const int kblk = (kt * kBN) / kScaleRows;
       const float ct = cq * sk[kblk];
       const float svt = sv[kblk];
-      const float lg = __builtin_log2f(svt) + (float)kexp;     // log2(sv * 2^k)
-      const float inv_svk = 1.0f / (svt * __builtin_ldexpf(1.0f, kexp));
 
       f32x16 sacc[2];
 #pragma unroll
@@ -190,8 +183,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
       mx = max_halves(mx) * ct;
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);
+      const float oscale = alpha * (sv_cur / svt);
+      sv_cur = svt;
       m_run = m_new;
-      const float bias = m_new - lg;
+      const float bias = m_new - kPShift;           // exp2 yields 2^8 * P
       float lsum = 0.f;
       int pb[8];
 #pragma unroll
@@ -207,11 +202,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
           int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
           pb[kb * 4 + q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         }
-      l_part = l_part * alpha + lsum * inv_svk;
+      l_part = l_part * alpha + lsum;
       const i32x8 pop = i32x8{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        oacc[db] *= alpha;
+        oacc[db] *= oscale;
         int av[8];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -233,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
 
   if (!wave_live || qrow >= N) return;
   const float l_tot = add_halves(l_part);
-  const float inv = __builtin_ldexpf(1.0f, -kexp) / l_tot;
+  const float inv = sv_cur / l_tot;
   uint16_t* Orow = O + head_off + (int64_t)qrow * kD;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -245,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
                  pack2(Bf16Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
       *(u32x2*)(Orow + d) = w;
     }
-  if (half == 0) LSE[(int64_t)bh * N + qrow] = (m_run + __builtin_log2f(l_tot)) * kLn2;
+  if (half == 0) LSE[(int64_t)bh * N + qrow] = (m_run + __builtin_log2f(l_tot) - kPShift) * kLn2;
 }
 
 template <bool CAUSAL>
