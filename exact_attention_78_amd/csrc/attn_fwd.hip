@@ -23,6 +23,8 @@
 //                 order inside each MFMA is permuted identically on both sides.
 //   K/V tiles are double-buffered in LDS (2 x 32 KiB at d = 128) and the next tile's
 //   global loads are in flight while the current tile is computed.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -51,14 +53,19 @@ template <> struct Swz<64> {
 template <typename Tag, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int total_wg, float scale,
-    float c /* scale * log2(e) */) {
-  constexpr int NCH = D / 8;                        // 16-byte chunks per row
-  constexpr int TILE = kBN * D;                     // elements per K (or V) tile
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int total_wg, float c /* scale*log2 e */) {
   constexpr int NSTEP = D / 16;                     // MFMA k-steps over the head dim
   constexpr int NKB = kBN / 32;                     // 32-key blocks per tile
   constexpr int NDB = D / 32;                       // 32-wide head-dim blocks of O
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];   // [buffer][K,V]
+  constexpr int ROW = D * 2;                        // bytes per K/V row
+  constexpr int TB = kBN * ROW;                     // bytes per K (or V) tile
+  constexpr int LPW = TB / 1024 / kWaves;           // 1 KiB direct loads per wave per tile
+  // LDS: two K and two V tiles, as four separate objects so that the compiler can tell
+  // the direct loads into one buffer from the reads of another (no needless vmcnt waits).
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[TB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[TB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[TB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[TB];
 
   const int logical = xcd_logical_id(blockIdx.x, total_wg);
   const int bh = logical / n_mtiles;
@@ -79,40 +86,75 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   // Q^T as the B operand, resident for the whole kernel.
   u32x4 qreg[NSTEP];
 #pragma unroll
-  for (int s = 0; s < NSTEP; ++s) {
-    if (qrow < N)
-      qreg[s] = *(const u32x4*)(Qh + (int64_t)qrow * D + s * 16 + half * 8);
-    else
-      qreg[s] = u32x4{0, 0, 0, 0};
-  }
+  for (int s = 0; s < NSTEP; ++s)
+    qreg[s] = qrow < N ? *(const u32x4*)(Qh + (int64_t)qrow * D + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
 
   const int n_ktiles = (N + kBN - 1) / kBN;
-  int kt_end = n_ktiles;
-  if (CAUSAL) kt_end = min(n_ktiles, ((mt + 1) * kBM + kBN - 1) / kBN);
-  // last key tile this wave needs (causal: its last row's diagonal)
-  const int wave_kt_end = CAUSAL ? min(kt_end, (q0 + 31) / kBN + 1) : kt_end;
-  const bool wave_live = q0 < N;
+  const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * kBM + kBN - 1) / kBN) : n_ktiles;
 
-  // Direct global -> LDS loads of one K/V tile (global_load_lds_dwordx4: no VGPR staging).
-  // Each wave instruction fills 1 KiB of LDS, 16 bytes per lane at consecutive addresses;
-  // the lane therefore fetches the global chunk that the swizzle places at its slot.
-  // Rows past the end of the sequence re-read the last row: their scores are masked and
-  // their probabilities are zero, so any finite data will do.
-  constexpr int ROW_BYTES = D * 2;
-  constexpr int LOADS_PER_WAVE = TILE * 2 / 1024 / kWaves;
-  auto issue_tile_loads = [&](int kt, int buf) {
+  // ---- per-lane LDS byte addresses (buffer and row-block offsets are immediates)
+  uint32_t kaddr[NSTEP];
 #pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-      const int slot = (wave * LOADS_PER_WAVE + i) * 1024 + lane * 16;   // byte offset in the tile
-      const int r = slot / ROW_BYTES, phys = (slot % ROW_BYTES) / 16;
-      const int key = min(kt * kBN + r, N - 1);
-      const int64_t goff = (int64_t)key * D;
-      const uint16_t* gk = Kh + goff + ((phys ^ Swz<D>::k(r)) * 8);
-      const uint16_t* gv = Vh + goff + ((phys ^ Swz<D>::v(r)) * 8);
-      uint16_t* lk = &smem[buf][0][(wave * LOADS_PER_WAVE + i) * 512];
-      uint16_t* lv = &smem[buf][1][(wave * LOADS_PER_WAVE + i) * 512];
-      __builtin_amdgcn_global_load_lds((const void*)gk, (__attribute__((address_space(3))) void*)lk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)gv, (__attribute__((address_space(3))) void*)lv, 16, 0, 0);
+  for (int s = 0; s < NSTEP; ++s) kaddr[s] = l32 * ROW + (((2 * s + half) ^ Swz<D>::k(l32)) << 4);
+  const int g16 = lane / 16, i16 = lane % 16;
+  const int tr_row = (g16 / 2) * 4 + i16 / 4;          // + kb*32 + t*16 (+8)
+  const int tr_col = 16 * (g16 % 2) + 4 * (i16 % 4);   // + db*32
+  uint32_t vaddr[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int col = db * 32 + tr_col;
+    vaddr[db] = tr_row * ROW + ((((col >> 3) ^ Swz<D>::v(tr_row))) << 4) + ((col & 7) << 1);
+  }
+
+  // ---- direct global -> LDS loads (global_load_lds_dwordx4, no VGPR staging). Each wave
+  // instruction fills 1 KiB of LDS, 16 bytes per lane at consecutive addresses, so a lane
+  // fetches the global chunk the swizzle places at its slot. Rows past the end of the
+  // sequence re-read the last row: their scores are masked and their probabilities are 0.
+  int ld_row[LPW], ld_kch[LPW], ld_vch[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int slot = (wave * LPW + i) * 1024 + lane * 16;
+    const int r = slot / ROW, phys = (slot % ROW) / 16;
+    ld_row[i] = r;
+    ld_kch[i] = (phys ^ Swz<D>::k(r)) * 8;
+    ld_vch[i] = (phys ^ Swz<D>::v(r)) * 8;
+  }
+  auto buf = [&](auto IDX) -> uint8_t* {
+    constexpr int i = decltype(IDX)::value;
+    if constexpr (i == 0) return lds_k0;
+    else if constexpr (i == 1) return lds_k1;
+    else if constexpr (i == 2) return lds_v0;
+    else return lds_v1;
+  };
+  auto load_k = [&](int kt, auto OFF) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int key = min(kt * kBN + ld_row[i], N - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(Kh + (int64_t)key * D + ld_kch[i]),
+                                       (__attribute__((address_space(3))) void*)(buf(OFF) + (wave * LPW + i) * 1024),
+                                       16, 0, 0);
+    }
+  };
+  auto load_v = [&](int kt, auto OFF) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int key = min(kt * kBN + ld_row[i], N - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(Vh + (int64_t)key * D + ld_vch[i]),
+                                       (__attribute__((address_space(3))) void*)(buf(OFF) + (wave * LPW + i) * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  // ---- S^T = K Q^T from the K tile at byte offset OFF
+  auto qk = [&](auto OFF, f32x16 (&sacc)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        const u32x4 a = *(const u32x4*)(buf(OFF) + kb * 32 * ROW + kaddr[s]);
+        sacc[kb] = mfma32(Tag{}, a, qreg[s], sacc[kb]);
+      }
     }
   };
 
@@ -125,103 +167,90 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
   float M = -INFINITY;
   float l_part = 0.f;        // running sum over this lane's half of the keys
 
-  // Lane roles in the V transpose reads.
-  const int g16 = lane / 16, i16 = lane % 16;
-  const int tr_row = (g16 / 2) * 4 + i16 / 4;          // + kb*32 + t*16 (+8)
-  const int tr_col = 16 * (g16 % 2) + 4 * (i16 % 4);   // + db*32
-
-  issue_tile_loads(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int kt = 0; kt < kt_end; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < kt_end) issue_tile_loads(kt + 1, buf ^ 1);
-
-    if (wave_live && kt < wave_kt_end) {
-      const uint16_t* Ks = smem[buf][0];
-      const uint16_t* Vs = smem[buf][1];
-      // ---- S^T = K Q^T
-      f32x16 sacc[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        sacc[kb] = f32x16{};
-        const int r = kb * 32 + l32;
-#pragma unroll
-        for (int s = 0; s < NSTEP; ++s) {
-          const int ch = s * 2 + half;
-          const u32x4 a = *(const u32x4*)(Ks + r * D + ((ch ^ Swz<D>::k(r)) * 8));
-          sacc[kb] = mfma32(Tag{}, a, qreg[s], sacc[kb]);
-        }
-      }
-      // ---- mask (diagonal tiles and the sequence tail only)
-      const int key0 = kt * kBN;
-      const bool need_mask = (CAUSAL && key0 + kBN - 1 > q0) || (key0 + kBN > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-            const bool masked = (CAUSAL && key > qrow) || key >= N;
-            if (masked) sacc[kb][r] = -INFINITY;
-          }
-      }
-      // ---- online softmax (exp2, lazily raised running max, deferred normalisation)
-      float mx = -INFINITY;
+  // ---- one pipelined step: softmax + P.V of tile t (held in S, V tile at VOFF) while the
+  // MFMAs of S^T for tile t+1 (K tile at KNEXT) are issued; loads for tiles t+2 (K, into
+  // KLOAD) and t+1 (V, into VLOAD) are in flight.
+  f32x16 Sa[NKB], Sb[NKB];
+  auto step = [&](int t, f32x16 (&S)[NKB], f32x16 (&Sn)[NKB], auto KNEXT, auto KLOAD, auto VOFF, auto VLOAD) {
+    if (t + 2 < T) load_k(t + 2, KLOAD);
+    if (t + 1 < T) load_v(t + 1, VLOAD);
+    const int key0 = t * kBN;
+    if ((CAUSAL && key0 + kBN - 1 > q0) || key0 + kBN > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = max_halves(mx) * c;
-      if (__builtin_amdgcn_ballot_w64(mx > M + kTau) != 0) {
-        const float M_new = fmaxf(M, mx);
-        const float alpha = fast_exp2(M - M_new);
-        M = M_new;
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      }
-      float lsum = 0.f;
-      u32x4 pk[NKB][2];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        float p[16];
-#pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(__builtin_fmaf(sacc[kb][r], c, -M));
-          lsum += p[r];
+          const int key = key0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+          if ((CAUSAL && key > qrow) || key >= N) S[kb][r] = -INFINITY;
         }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          pk[kb][t] = u32x4{pack2(Tag{}, p[t * 8 + 0], p[t * 8 + 1]), pack2(Tag{}, p[t * 8 + 2], p[t * 8 + 3]),
-                            pack2(Tag{}, p[t * 8 + 4], p[t * 8 + 5]), pack2(Tag{}, p[t * 8 + 6], p[t * 8 + 7])};
-      }
-      l_part += lsum;
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int row1 = kb * 32 + t * 16 + tr_row;
-            const int row2 = row1 + 8;
-            const int col = db * 32 + tr_col;
-            const u32x2 v1 = lds_read_tr16(Vs + row1 * D + (((col >> 3) ^ Swz<D>::v(row1)) << 3) + (col & 7));
-            const u32x2 v2 = lds_read_tr16(Vs + row2 * D + (((col >> 3) ^ Swz<D>::v(row2)) << 3) + (col & 7));
-            const u32x4 a = u32x4{v1[0], v1[1], v2[0], v2[1]};
-            oacc[db] = mfma32(Tag{}, a, pk[kb][t], oacc[db]);
-          }
-        }
-      }
     }
-
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+    mx = max_halves(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > M + kTau) != 0) {
+      const float M_new = fmaxf(M, mx);
+      const float alpha = fast_exp2(M - M_new);
+      M = M_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
+    qk(KNEXT, Sn);           // independent of the softmax below: the MFMAs overlap its VALU work
+    float lsum = 0.f;
+    u32x4 pk[NKB][2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(__builtin_fmaf(S[kb][r], c, -M));
+        lsum += p[r];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        pk[kb][h] = u32x4{pack2(Tag{}, p[h * 8 + 0], p[h * 8 + 1]), pack2(Tag{}, p[h * 8 + 2], p[h * 8 + 3]),
+                          pack2(Tag{}, p[h * 8 + 4], p[h * 8 + 5]), pack2(Tag{}, p[h * 8 + 6], p[h * 8 + 7])};
+    }
+    l_part += lsum;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint8_t* base = buf(VOFF) + (kb * 32 + h * 16) * ROW + vaddr[db];
+          const u32x2 v1 = lds_read_tr16((const uint16_t*)base);
+          const u32x2 v2 = lds_read_tr16((const uint16_t*)(base + 8 * ROW));
+          oacc[db] = mfma32(Tag{}, u32x4{v1[0], v1[1], v2[0], v2[1]}, pk[kb][h], oacc[db]);
+        }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  using V0 = std::integral_constant<int, 2>;
+  using V1 = std::integral_constant<int, 3>;
+
+  load_k(0, K0{});
+  load_v(0, V0{});
+  if (T > 1) load_k(1, K1{});
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  qk(K0{}, Sa);
+  __syncthreads();                                   // K0 is refilled with tile 2 next
+
+  for (int t = 0; t < T; t += 2) {
+    // even tile t: its scores in Sa, its V in V0; S^T of t+1 from K1 into Sb
+    step(t, Sa, Sb, K1{}, K0{}, V0{}, V1{});
+    if (t + 1 < T) step(t + 1, Sb, Sa, K0{}, K1{}, V1{}, V0{});
   }
 
-  if (!wave_live || qrow >= N) return;
+  if (qrow >= N) return;
   // ---- epilogue: one division per row, O and LSE
   const float l_tot = add_halves(l_part);
   const float inv = 1.0f / l_tot;
@@ -245,7 +274,7 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
   const int64_t total = BH * n_mtiles;
   hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N, n_mtiles,
-                     (int)total, scale, scale * kLog2e);
+                     (int)total, scale * kLog2e);
   return hipGetLastError();
 }
 
