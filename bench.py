@@ -139,8 +139,10 @@ def fp8_leg(torch, ea, inputs, steps, warmup):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # The GPU needs a few tens of milliseconds of sustained load to reach its steady clock;
+    # 100 untimed steps (~60 ms here) get there before the timed region starts.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-extra", action="store_true", help="skip the fp8 leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
