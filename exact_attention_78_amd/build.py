@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -41,13 +42,30 @@ def sources():
     return [os.path.join(CSRC, f) for f in names]
 
 
+def _scratch_warnings(stderr: str):
+    """Kernels that use scratch (private) memory: a dynamically indexed or spilled array
+    costs an order of magnitude in speed, so every such kernel is reported."""
+    out, fn = [], None
+    for line in stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            fn = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            out.append(f"{fn}: {m.group(1)} bytes/lane of scratch")
+    return out
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *lang, *COMMON, *extra, "-c", src, "-o", obj]
+    report = [] if src.endswith(".cpp") else ["-Rpass-analysis=kernel-resource-usage"]
+    cmd = [hipcc(), *lang, *COMMON, *extra, *report, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {os.path.basename(src)}:\n{res.stderr}")
+    for w in _scratch_warnings(res.stderr):
+        print(f"warning: {os.path.basename(src)}: {w}", file=sys.stderr)
     return obj
 
 

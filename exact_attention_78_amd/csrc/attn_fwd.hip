@@ -13,7 +13,8 @@
 // follows the same page's item 4, remapped so that each of the 8 XCDs walks its own
 // contiguous range of heads (their K/V stay in that XCD's L2).
 //
-// gfx950 mapping (per wave, 32 query rows, key tile of BN = 64):
+// gfx950 mapping: 8 waves x 32 query rows per workgroup (two waves per SIMD), key tiles
+// of BN = 64:
 //   S^T = K Q^T   32x32x16 MFMAs: A = K rows from LDS (ds_read_b128), B = Q^T kept in
 //                 VGPRs for the whole kernel. The result puts one query row per lane
 //                 (lane l and l^32 share a row, each holding half of the keys), so the
@@ -21,8 +22,11 @@
 //   O^T += V^T P^T  A = V^T via ds_read_b64_tr_b16 (LDS transpose read of row-major V),
 //                 B = P rounded to 16 bits straight from the S^T accumulators. The key
 //                 order inside each MFMA is permuted identically on both sides.
-//   K/V tiles are double-buffered in LDS (2 x 32 KiB at d = 128) and the next tile's
-//   global loads are in flight while the current tile is computed.
+//   The S^T MFMAs of tile t+1 are issued in the same block as the softmax of tile t, so
+//   the matrix core works while the VALU computes exponentials (the intra-warpgroup
+//   overlap of "8.3 FlashAttention-3", section 4, inside one wave).
+//   K/V tiles sit in a 3-slot LDS ring (3 x 32 KiB at d = 128), filled by direct
+//   global->LDS loads (global_load_lds_dwordx4) two steps ahead of their use.
 #include <type_traits>
 
 #include "device_common.h"
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     ld_kch[i] = (phys ^ Swz<D>::k(r)) * 8;
     ld_vch[i] = (phys ^ Swz<D>::v(r)) * 8;
   }
-  auto buf = [&](auto IDX) -> uint8_t* {       // 0..2: K ring, 3..5: V ring
+  auto buf = [&](auto IDX) __attribute__((always_inline)) -> uint8_t* {       // 0..2: K ring, 3..5: V ring
     constexpr int i = decltype(IDX)::value;
     if constexpr (i == 0) return lds_k0;
     else if constexpr (i == 1) return lds_k1;
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     ld_koff[i] = (ld_row[i] * D + ld_kch[i]) * 2;
     ld_voff[i] = (ld_row[i] * D + ld_vch[i]) * 2;
   }
-  auto load_tile = [&](const uint16_t* src, const int (&off)[LPW], const int (&ch)[LPW], int kt, uint8_t* dst) {
+  auto load_tile = [&](const uint16_t* src, const int (&off)[LPW], const int (&ch)[LPW], int kt, uint8_t* dst) __attribute__((always_inline)) {
     if (kt * kBN + kBN <= N) {
       const uint8_t* base = (const uint8_t*)(src + (int64_t)kt * kBN * D);
 #pragma unroll
@@ -191,11 +195,11 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       }
     }
   };
-  auto load_k = [&](int kt, auto OFF) { load_tile(Kh, ld_koff, ld_kch, kt, buf(OFF)); };
-  auto load_v = [&](int kt, auto OFF) { load_tile(Vh, ld_voff, ld_vch, kt, buf(OFF)); };
+  auto load_k = [&](int kt, auto OFF) __attribute__((always_inline)) { load_tile(Kh, ld_koff, ld_kch, kt, buf(OFF)); };
+  auto load_v = [&](int kt, auto OFF) __attribute__((always_inline)) { load_tile(Vh, ld_voff, ld_vch, kt, buf(OFF)); };
 
   // ---- S^T = K Q^T from the K tile in ring slot OFF; each K fragment feeds every row block
-  auto qk = [&](auto OFF, f32x16 (&sacc)[RB][NKB]) {
+  auto qk = [&](auto OFF, f32x16 (&sacc)[RB][NKB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   // last tile and never read, which keeps the number of loads per step fixed.
   f32x16 Sa[RB][NKB], Sb[RB][NKB];
   auto step = [&](int t, f32x16 (&S)[RB][NKB], f32x16 (&Sn)[RB][NKB], auto KNEXT, auto KLOAD, auto VOFF,
-                  auto VLOAD) {
+                  auto VLOAD) __attribute__((always_inline)) {
     load_v(min(t + 2, T - 1), VLOAD);
     load_k(min(t + 3, T - 1), KLOAD);
     const int key0 = t * kBN;
