@@ -30,6 +30,14 @@ COMMON = [
 ]
 
 
+# Per-source flags. The 16-bit attention kernel is written in issue order (its main loop
+# interleaves MFMAs, LDS reads and softmax VALU work by hand), so the machine scheduler
+# is switched off for that file.
+FILE_FLAGS = {
+    "attn_fwd.hip": ["-mllvm", "-enable-misched=0", "-mllvm", "-enable-post-misched=0"],
+}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -60,7 +68,8 @@ def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     report = [] if src.endswith(".cpp") else ["-Rpass-analysis=kernel-resource-usage"]
-    cmd = [hipcc(), *lang, *COMMON, *extra, *report, "-c", src, "-o", obj]
+    per_file = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc(), *lang, *COMMON, *per_file, *extra, *report, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {os.path.basename(src)}:\n{res.stderr}")

@@ -22,11 +22,13 @@
 //   O^T += V^T P^T  A = V^T via ds_read_b64_tr_b16 (LDS transpose read of row-major V),
 //                 B = P rounded to 16 bits straight from the S^T accumulators. The key
 //                 order inside each MFMA is permuted identically on both sides.
-//   The S^T MFMAs of tile t+1 are issued in the same block as the softmax of tile t, so
-//   the matrix core works while the VALU computes exponentials (the intra-warpgroup
-//   overlap of "8.3 FlashAttention-3", section 4, inside one wave).
-//   K/V tiles sit in a 3-slot LDS ring (3 x 32 KiB at d = 128), filled by direct
-//   global->LDS loads (global_load_lds_dwordx4) two steps ahead of their use.
+//   Software pipeline three tiles deep: step t issues the P.V MFMAs of tile t, the
+//   softmax of tile t+1 and the S^T MFMAs of tile t+2, which do not depend on each other,
+//   so the matrix core and the VALU work side by side (the intra-warpgroup overlap of
+//   "8.3 FlashAttention-3", section 4, taken one stage further inside one wave). The
+//   step's MFMAs, LDS reads and VALU work are written in the order they are issued.
+//   K and V tiles sit in two 4-slot LDS rings (128 KiB at d = 128), filled by direct
+//   global->LDS loads (global_load_lds_dwordx4) two or three steps ahead of their use.
 #include <type_traits>
 
 #include "device_common.h"
@@ -35,20 +37,11 @@
 namespace attn {
 namespace {
 
-#ifndef ATTN_WAVES
-#define ATTN_WAVES 8
-#endif
-#ifndef ATTN_ROW_BLOCKS
-#define ATTN_ROW_BLOCKS 1
-#endif
-constexpr int kBN = 64;                    // keys per tile
-constexpr int kWaves = ATTN_WAVES;         // waves per workgroup
-constexpr int kRowBlocks = ATTN_ROW_BLOCKS;  // 32-row query blocks per wave
-#ifndef ATTN_PIPE
-#define ATTN_PIPE 1
-#endif
-constexpr bool kPipe = ATTN_PIPE;          // issue S^T of tile t+1 alongside the softmax of tile t
-constexpr float kTau = 8.0f;  // lazy-rescale threshold for the running max, in log2 units
+constexpr int kBN = 64;        // keys per tile
+constexpr int kWaves = 8;      // waves per workgroup (32 query rows each)
+constexpr int kKD = 4;         // S^T MFMAs by which a K fragment read runs ahead
+constexpr int kVD = 2;         // P.V MFMAs by which a V fragment read runs ahead
+constexpr float kTau = 8.0f;   // lazy-rescale threshold for the running max, in log2 units
 
 // LDS swizzles: 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
 // K is read 32 rows x one chunk per instruction; V is read as 8 rows x 4 chunks
@@ -72,6 +65,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Byte address of a __shared__ object in the LDS aperture.
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// One 16-byte-per-lane global->LDS DMA (global_load_lds_dwordx4): lane i's 16 bytes land
+// at LDS byte lds_base + 16*i; lds_base must be wave-uniform (it goes through M0). The load
+// is written as inline assembly so that the compiler does not see an LDS write it would
+// guard with a full vmcnt(0) drain before every later LDS read: completion is tracked by
+// hand with wait_vmcnt<>() and barrier_lds(). No compiler-generated code in this kernel
+// uses M0, so setting it here is safe.
+__device__ __forceinline__ void dma_load16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_base) : "memory");
+}
+
 // Workgroup barrier for LDS hand-over only: LDS reads of this wave are complete, then
 // s_barrier. Unlike __syncthreads() it does not drain this wave's outstanding global
 // loads, so a load for a later tile can stay in flight across it.
@@ -79,27 +88,23 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <typename Tag, int D, bool CAUSAL, int W, int RB, bool PIPE>
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+template <typename Tag, int D, bool CAUSAL, int W>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int total_wg, float c /* scale*log2 e */) {
-  constexpr int BM = W * RB * 32;                   // query rows per workgroup
+  constexpr int BM = W * 32;                        // query rows per workgroup
   constexpr int NSTEP = D / 16;                     // MFMA k-steps over the head dim
   constexpr int NKB = kBN / 32;                     // 32-key blocks per tile
   constexpr int NDB = D / 32;                       // 32-wide head-dim blocks of O
   constexpr int ROW = D * 2;                        // bytes per K/V row
   constexpr int TB = kBN * ROW;                     // bytes per K (or V) tile
   constexpr int LPW = TB / 1024 / W;                // 1 KiB direct loads per wave per tile
+  constexpr int NS = 4;                             // ring slots per operand
   static_assert(LPW >= 1 && LPW * 1024 * W == TB, "tile must split into whole 1 KiB loads per wave");
-  // LDS: three K and three V tiles (a ring: tile t lives in buffer t % 3), as six separate
-  // objects so that the compiler can tell the direct loads into one buffer from the reads
-  // of another (no needless vmcnt waits).
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[TB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[TB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k2[TB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[TB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[TB];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v2[TB];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];   // K ring, then V ring
 
   const int logical = xcd_logical_id(blockIdx.x, total_wg);
   const int bh = logical / n_mtiles;
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   if (CAUSAL) mt = n_mtiles - 1 - mt;               // longest query tiles first
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // wave-uniform: lives in an SGPR
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64;
   const int half = lane / 32, l32 = lane % 32;
   const int64_t head_off = (int64_t)bh * N * D;
@@ -115,31 +120,22 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   const uint16_t* Kh = K + head_off;
   const uint16_t* Vh = V + head_off;
 
-  // This wave owns RB blocks of 32 query rows; each lane holds one row of each block.
-  const int q0 = mt * BM + wave * RB * 32;
-  int qrow[RB];
+  const int q0 = mt * BM + wave * 32;               // this wave's 32 rows; one per lane (and lane^32)
+  const int qrow = q0 + l32;
+  u32x4 qreg[NSTEP];                                // Q^T as the B operand, resident
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) qrow[rb] = q0 + rb * 32 + l32;
-
-  // Q^T as the B operand, resident for the whole kernel.
-  u32x4 qreg[RB][NSTEP];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s)
-      qreg[rb][s] = qrow[rb] < N ? *(const u32x4*)(Qh + (int64_t)qrow[rb] * D + s * 16 + half * 8)
-                                 : u32x4{0, 0, 0, 0};
+  for (int s = 0; s < NSTEP; ++s)
+    qreg[s] = qrow < N ? *(const u32x4*)(Qh + (int64_t)qrow * D + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
 
   const int n_ktiles = (N + kBN - 1) / kBN;
   const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * BM + kBN - 1) / kBN) : n_ktiles;
 
-  // ---- per-lane LDS byte addresses (buffer and row-block offsets are immediates)
   uint32_t kaddr[NSTEP];
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) kaddr[s] = l32 * ROW + (((2 * s + half) ^ Swz<D>::k(l32)) << 4);
   const int g16 = lane / 16, i16 = lane % 16;
-  const int tr_row = (g16 / 2) * 4 + i16 / 4;          // + kb*32 + t*16 (+8)
-  const int tr_col = 16 * (g16 % 2) + 4 * (i16 % 4);   // + db*32
+  const int tr_row = (g16 / 2) * 4 + i16 / 4;
+  const int tr_col = 16 * (g16 % 2) + 4 * (i16 % 4);
   uint32_t vaddr[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
@@ -147,11 +143,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     vaddr[db] = tr_row * ROW + ((((col >> 3) ^ Swz<D>::v(tr_row))) << 4) + ((col & 7) << 1);
   }
 
-  // ---- direct global -> LDS loads (global_load_lds_dwordx4, no VGPR staging). Each wave
-  // instruction fills 1 KiB of LDS, 16 bytes per lane at consecutive addresses, so a lane
-  // fetches the global chunk the swizzle places at its slot. Rows past the end of the
-  // sequence re-read the last row: their scores are masked and their probabilities are 0.
-  int ld_row[LPW], ld_kch[LPW], ld_vch[LPW];
+  int ld_row[LPW], ld_kch[LPW], ld_vch[LPW], ld_koff[LPW], ld_voff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int slot = (wave * LPW + i) * 1024 + lane * 16;
@@ -159,224 +151,218 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     ld_row[i] = r;
     ld_kch[i] = (phys ^ Swz<D>::k(r)) * 8;
     ld_vch[i] = (phys ^ Swz<D>::v(r)) * 8;
-  }
-  auto buf = [&](auto IDX) __attribute__((always_inline)) -> uint8_t* {       // 0..2: K ring, 3..5: V ring
-    constexpr int i = decltype(IDX)::value;
-    if constexpr (i == 0) return lds_k0;
-    else if constexpr (i == 1) return lds_k1;
-    else if constexpr (i == 2) return lds_k2;
-    else if constexpr (i == 3) return lds_v0;
-    else if constexpr (i == 4) return lds_v1;
-    else return lds_v2;
-  };
-  // Full tiles: a uniform tile base plus a per-lane 32-bit byte offset (no per-lane 64-bit
-  // address arithmetic). The tile that crosses the end of the sequence clamps rows.
-  int ld_koff[LPW], ld_voff[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
     ld_koff[i] = (ld_row[i] * D + ld_kch[i]) * 2;
     ld_voff[i] = (ld_row[i] * D + ld_vch[i]) * 2;
   }
-  auto load_tile = [&](const uint16_t* src, const int (&off)[LPW], const int (&ch)[LPW], int kt, uint8_t* dst) __attribute__((always_inline)) {
+  auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* { return lds + decltype(SLOT)::value * TB; };
+  auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* {
+    return lds + (NS + decltype(SLOT)::value) * TB;
+  };
+  auto load_tile = [&](const uint16_t* src, const int (&off)[LPW], const int (&ch)[LPW], int kt, uint8_t* dst)
+                       __attribute__((always_inline)) {
     if (kt * kBN + kBN <= N) {
       const uint8_t* base = (const uint8_t*)(src + (int64_t)kt * kBN * D);
 #pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(base + off[i]),
-                                         (__attribute__((address_space(3))) void*)(dst + (wave * LPW + i) * 1024), 16,
-                                         0, 0);
+      for (int i = 0; i < LPW; ++i) dma_load16(base + off[i], lds_u32(dst) + (wave * LPW + i) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int key = min(kt * kBN + ld_row[i], N - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)key * D + ch[i]),
-                                         (__attribute__((address_space(3))) void*)(dst + (wave * LPW + i) * 1024), 16,
-                                         0, 0);
+        dma_load16(src + (int64_t)key * D + ch[i], lds_u32(dst) + (wave * LPW + i) * 1024);
       }
     }
   };
-  auto load_k = [&](int kt, auto OFF) __attribute__((always_inline)) { load_tile(Kh, ld_koff, ld_kch, kt, buf(OFF)); };
-  auto load_v = [&](int kt, auto OFF) __attribute__((always_inline)) { load_tile(Vh, ld_voff, ld_vch, kt, buf(OFF)); };
 
-  // ---- S^T = K Q^T from the K tile in ring slot OFF; each K fragment feeds every row block
-  auto qk = [&](auto OFF, f32x16 (&sacc)[RB][NKB]) __attribute__((always_inline)) {
+  auto qk = [&](auto SLOT, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      S[kb] = f32x16{};
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        const u32x4 a = *(const u32x4*)(buf(OFF) + kb * 32 * ROW + kaddr[s]);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) sacc[rb][kb] = mfma32(Tag{}, a, qreg[rb][s], sacc[rb][kb]);
-      }
+      for (int s = 0; s < NSTEP; ++s)
+        S[kb] = mfma32(Tag{}, *(const u32x4*)(kbuf(SLOT) + kb * 32 * ROW + kaddr[s]), qreg[s], S[kb]);
     }
   };
-
-  f32x16 oacc[RB][NDB];
+  f32x16 oacc[NDB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[rb][db] = f32x16{};
-  // Running max in log2 units (score * scale * log2 e). It is raised only when a tile's
-  // max exceeds it by more than kTau, so most tiles skip the O rescale; probabilities are
-  // then bounded by 2^kTau, which bf16/fp16 P and the fp32 sums hold exactly as well.
-  float M[RB], l_part[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    M[rb] = -INFINITY;
-    l_part[rb] = 0.f;        // running sum over this lane's half of the keys
-  }
-
-  // ---- one pipelined step: softmax + P.V of tile t (scores in S, V in ring slot t % 3)
-  // while the S^T MFMAs of tile t+1 (K in slot (t+1) % 3) are issued. Loads of V for
-  // tile t+2 and K for tile t+3 go out at the start of the step; each has two steps to
-  // land, so the wait at the end of the step leaves this step's loads in flight. Near
-  // the end the tile index is clamped: a slot past the last tile is refilled with the
-  // last tile and never read, which keeps the number of loads per step fixed.
-  f32x16 Sa[RB][NKB], Sb[RB][NKB];
-  auto step = [&](int t, f32x16 (&S)[RB][NKB], f32x16 (&Sn)[RB][NKB], auto KNEXT, auto KLOAD, auto VOFF,
-                  auto VLOAD) __attribute__((always_inline)) {
-    load_v(min(t + 2, T - 1), VLOAD);
-    load_k(min(t + 3, T - 1), KLOAD);
-    const int key0 = t * kBN;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if ((CAUSAL && key0 + kBN - 1 > q0 + rb * 32) || key0 + kBN > N) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-            if ((CAUSAL && key > qrow[rb]) || key >= N) S[rb][kb][r] = -INFINITY;
-          }
-      }
-    }
-    float mx[RB];
-    bool grow = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      // four independent max chains (v_max3), then combined: short dependency chains
-      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  // Running max M (log2 units; raised only when a tile's max exceeds it by more than
+  // kTau, so that probabilities stay below 2^kTau), this lane's partial row sum of the
+  // rounded probabilities, and a pending O rescale factor.
+  float M = -INFINITY, l_part = 0.f, alpha_pend = 1.f;
+  // Scores of tile u that lie above the diagonal or past the end of the sequence -> -inf.
+  auto mask_tile = [&](int u, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
+    const int key0 = u * kBN;
+    if ((CAUSAL && key0 + kBN - 1 > q0) || key0 + kBN > N) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) m4[(r / 2) % 4] = fmaxf(m4[(r / 2) % 4], fmaxf(S[rb][kb][r], S[rb][kb][r + 1]));
-      mx[rb] = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
-      grow |= mx[rb] > M[rb] + kTau;
-    }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float M_new = fmaxf(M[rb], mx[rb]);
-        const float alpha = fast_exp2(M[rb] - M_new);
-        M[rb] = M_new;
-        l_part[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[rb][db] *= alpha;
-      }
-    }
-    if constexpr (PIPE) qk(KNEXT, Sn);   // independent of the softmax below: the MFMAs overlap its VALU work
-    u32x4 pk[RB][NKB][2];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(__builtin_fmaf(S[rb][kb][r], c, -M[rb]));
-          lsum += p[r];
+          const int key = key0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+          if ((CAUSAL && key > qrow) || key >= N) S[kb][r] = -INFINITY;
         }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          pk[rb][kb][h] = u32x4{pack2(Tag{}, p[h * 8 + 0], p[h * 8 + 1]), pack2(Tag{}, p[h * 8 + 2], p[h * 8 + 3]),
-                                pack2(Tag{}, p[h * 8 + 4], p[h * 8 + 5]), pack2(Tag{}, p[h * 8 + 6], p[h * 8 + 7])};
-      }
-      l_part[rb] += lsum;
     }
-    // O^T += V^T P^T; each V fragment feeds every row block
+  };
+  // Row max of a tile's (masked) scores: max_pairs folds the score pairs in [e_begin,
+  // e_end) into four v_maximum3 chains (seeded with scores 0..3); max_final combines the
+  // chains and the partner lane l^32 and scales to log2 units.
+  auto max_pairs = [&](float (&m4)[4], const f32x16 (&S)[NKB], int e_begin, int e_end) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int e = e_begin; e < e_end; e += 2)
+      m4[(e / 2) % 4] = max3f(m4[(e / 2) % 4], S[e / 16][e % 16], S[e / 16][e % 16 + 1]);
+  };
+  // Raise M when some row of the wave grew by more than kTau (branch-free, so that the
+  // exponentials can share a basic block with the MFMAs); l is rescaled at once, O at
+  // the start of the next step. Returns whether M moved (wave-uniform).
+  auto max_final = [&](const float (&m4)[4]) __attribute__((always_inline)) -> bool {
+    const float mx = max_halves(max3f(m4[0], m4[1], __builtin_elementwise_maximum(m4[2], m4[3]))) * c;
+    const bool grow = __builtin_amdgcn_ballot_w64(mx > M + kTau) != 0;
+    const float M_new = grow ? __builtin_elementwise_maximum(M, mx) : M;
+    const float alpha = grow ? fast_exp2(M - M_new) : 1.f;
+    M = M_new;
+    l_part *= alpha;
+    alpha_pend *= alpha;
+    return grow;
+  };
+  // Probabilities of scores e in [e0, e1): P = 2^(S*c - M) in fp32, added to the row sum
+  // (two chains) before rounding, then rounded to 16 bits and packed in pairs into the
+  // B operand of P.V.
+  auto exps = [&](const f32x16 (&S)[NKB], u32x4 (&P)[NKB][2], float (&pe)[NKB * 16], float (&lsum)[2], int e0,
+                  int e1) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    for (int e = e0; e < e1; ++e) {
+      pe[e] = fast_exp2(__builtin_fmaf(S[e / 16][e % 16], c, -M));
+      lsum[e % 2] += pe[e];
+      if (e % 2 == 1) P[e / 16][(e % 16) / 8][(e % 8) / 2] = pack2(Tag{}, pe[e - 1], pe[e]);
+    }
+  };
+  auto rescale_o = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint8_t* base = buf(VOFF) + (kb * 32 + h * 16) * ROW + vaddr[db];
-          const u32x2 v1 = lds_read_tr16((const uint16_t*)base);
-          const u32x2 v2 = lds_read_tr16((const uint16_t*)(base + 8 * ROW));
-          const u32x4 a = u32x4{v1[0], v1[1], v2[0], v2[1]};
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha_pend;
+    alpha_pend = 1.f;
+  };
+
+  f32x16 Sa[NKB], Sb[NKB];
+  u32x4 Pa[NKB][2], Pb[NKB][2];
+  bool pend = false;     // wave-uniform: an O rescale is owed
+
+  // Step t (j = t mod 4 fixes every register set and ring slot at compile time):
+  //   S(t+1) in S_soft, S(t+2) -> S_new, P(t) in P_use, P(t+1) -> P_new,
+  //   K(t+2) in K slot (t+2)%4, V(t) in V slot t%4; loads: K(t+4) -> K slot t%4,
+  //   V(t+3) -> V slot (t+3)%4. Past the last tile the loads are clamped (never read),
+  //   and the scores of tile T (if computed) are fully masked, so P(T) = 0 adds nothing.
+  auto step = [&](int t, f32x16 (&S_soft)[NKB], f32x16 (&S_new)[NKB], const u32x4 (&P_use)[NKB][2],
+                  u32x4 (&P_new)[NKB][2], auto KRD, auto VRD, auto KLD, auto VLD) __attribute__((always_inline)) {
+    load_tile(Kh, ld_koff, ld_kch, min(t + 4, T - 1), kbuf(KLD));
+    load_tile(Vh, ld_voff, ld_vch, min(t + 3, T - 1), vbuf(VLD));
+    if (pend) rescale_o();
+    mask_tile(t + 1, S_soft);
+    // Main block, written in issue order (this file is compiled without the machine
+    // scheduler): 16 S^T MFMAs (K fragments read KD ahead) then 16 P.V MFMAs (V^T
+    // fragments read VD ahead); the softmax VALU work of tile t+1 is spread between them:
+    // the row max over the first five S^T MFMAs, then the exponentials, one or two per MFMA.
+    constexpr int NQ = NKB * NSTEP, NP = NDB * NKB * 2, KD = kKD, VD = kVD;
+    constexpr int NSLOT = NQ + NP - 5;                 // MFMAs that carry exponentials
+    u32x4 kf[NQ], vf[NP];
+    auto kread = [&](int i) __attribute__((always_inline)) {   // i = s * NKB + kb
+      kf[i] = *(const u32x4*)(kbuf(KRD) + (i % NKB) * 32 * ROW + kaddr[i / NKB]);
+    };
+    auto vread = [&](int i) __attribute__((always_inline)) {   // i = (kb * 2 + h) * NDB + db
+      const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
+      const uint8_t* base = vbuf(VRD) + (kb * 32 + h * 16) * ROW + vaddr[db];
+      const u32x2 v1 = lds_read_tr16((const uint16_t*)base);
+      const u32x2 v2 = lds_read_tr16((const uint16_t*)(base + 8 * ROW));
+      vf[i] = u32x4{v1[0], v1[1], v2[0], v2[1]};
+    };
+    float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
+    float lsum[2] = {0.f, 0.f};
+    float pe[NKB * 16];
+    auto exps_slot = [&](int slot) __attribute__((always_inline)) {
+      exps(S_soft, P_new, pe, lsum, slot * (NKB * 16) / NSLOT, (slot + 1) * (NKB * 16) / NSLOT);
+    };
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) oacc[rb][db] = mfma32(Tag{}, a, pk[rb][kb][h], oacc[rb][db]);
-        }
-    if constexpr (!PIPE) qk(KNEXT, Sn);  // scores of tile t+1, once P of tile t no longer needs S
-    wait_vmcnt<2 * LPW>();   // tiles t+1 (V) and t+2 (K), issued a step earlier, have landed
+    for (int i = 0; i < KD; ++i) kread(i);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      if (i + KD < NQ) kread(i + KD);
+      if (i + KD >= NQ && i + KD - NQ < VD) vread(i + KD - NQ);
+      const int kb = i % NKB, s = i / NKB;
+      S_new[kb] = mfma32(Tag{}, kf[i], qreg[s], s == 0 ? f32x16{} : S_new[kb]);
+      if (i < 4)
+        max_pairs(m4, S_soft, 4 + i * 8, min(4 + (i + 1) * 8, NKB * 16));
+      else if (i == 4)
+        pend = max_final(m4);
+      else
+        exps_slot(i - 5);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (i + VD < NP) vread(i + VD);
+      const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
+      oacc[db] = mfma32(Tag{}, vf[i], P_use[kb][h], oacc[db]);
+      exps_slot(NQ - 5 + i);
+    }
+    l_part += lsum[0] + lsum[1];
+    wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
     barrier_lds();
   };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  using I4 = std::integral_constant<int, 4>;
-  using I5 = std::integral_constant<int, 5>;
-
-  load_k(0, I0{});
-  load_v(0, I3{});
-  if (T > 1) load_k(1, I1{});
-  if (T > 1) load_v(1, I4{});
-  if (T > 2) load_k(2, I2{});
+  // Prologue: K tiles 0..3 and V tiles 0..2; S(0), softmax of tile 0, S(1).
+  load_tile(Kh, ld_koff, ld_kch, 0, kbuf(IC<0>{}));
+  load_tile(Kh, ld_koff, ld_kch, min(1, T - 1), kbuf(IC<1>{}));
+  load_tile(Kh, ld_koff, ld_kch, min(2, T - 1), kbuf(IC<2>{}));
+  load_tile(Kh, ld_koff, ld_kch, min(3, T - 1), kbuf(IC<3>{}));
+  load_tile(Vh, ld_voff, ld_vch, 0, vbuf(IC<0>{}));
+  load_tile(Vh, ld_voff, ld_vch, min(1, T - 1), vbuf(IC<1>{}));
+  load_tile(Vh, ld_voff, ld_vch, min(2, T - 1), vbuf(IC<2>{}));
   wait_vmcnt<0>();
   barrier_lds();
-  qk(I0{}, Sa);
-  barrier_lds();                                     // K slot 0 is refilled with tile 3 next
-
-  // Six steps per trip: ring slots repeat every 3 tiles, score registers every 2.
-  for (int t = 0; t < T; t += 6) {
-    step(t, Sa, Sb, I1{}, I0{}, I3{}, I5{});
-    if (t + 1 < T) step(t + 1, Sb, Sa, I2{}, I1{}, I4{}, I3{});
-    if (t + 2 < T) step(t + 2, Sa, Sb, I0{}, I2{}, I5{}, I4{});
-    if (t + 3 < T) step(t + 3, Sb, Sa, I1{}, I0{}, I3{}, I5{});
-    if (t + 4 < T) step(t + 4, Sa, Sb, I2{}, I1{}, I4{}, I3{});
-    if (t + 5 < T) step(t + 5, Sb, Sa, I0{}, I2{}, I5{}, I4{});
+  qk(IC<0>{}, Sa);
+  {
+    mask_tile(0, Sa);
+    float m4[4] = {Sa[0][0], Sa[0][1], Sa[0][2], Sa[0][3]};
+    max_pairs(m4, Sa, 4, NKB * 16);
+    max_final(m4);
+    alpha_pend = 1.f;            // O is still zero: no rescale owed
+    float pe[NKB * 16], lsum[2] = {0.f, 0.f};
+    exps(Sa, Pa, pe, lsum, 0, NKB * 16);
+    l_part += lsum[0] + lsum[1];
   }
-  wait_vmcnt<0>();           // no load may still target this workgroup's LDS when it exits
+  qk(IC<1>{}, Sb);
+  barrier_lds();                 // K slots 0 and 1 are refilled from step 0 on
 
-  // ---- epilogue: one division per row, O and LSE
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l_tot = add_halves(l_part[rb]);
-    if (qrow[rb] >= N) continue;
-    const float inv = 1.0f / l_tot;
-    uint16_t* Orow = O + head_off + (int64_t)qrow[rb] * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + g * 8 + half * 4;
-        const f32x16 a = oacc[rb][db];
-        u32x2 w = {pack2(Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv),
-                   pack2(Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
-        *(u32x2*)(Orow + d) = w;
-      }
-    if (half == 0) LSE[(int64_t)bh * N + qrow[rb]] = (M[rb] + __builtin_log2f(l_tot)) * kLn2;
+  for (int t = 0; t < T; t += 4) {
+    step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{});
+    if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{});
+    if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{});
+    if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{});
   }
+  wait_vmcnt<0>();               // no load may still target this workgroup's LDS when it exits
+  if (pend) rescale_o();
+
+  const float l_tot = add_halves(l_part);
+  if (qrow >= N) return;
+  const float inv = 1.0f / l_tot;
+  uint16_t* Orow = O + head_off + (int64_t)qrow * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + g * 8 + half * 4;
+      const f32x16 a = oacc[db];
+      u32x2 w = {pack2(Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv),
+                 pack2(Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
+      *(u32x2*)(Orow + d) = w;
+    }
+  if (half == 0) LSE[(int64_t)bh * N + qrow] = (M + __builtin_log2f(l_tot)) * kLn2;
 }
-
-// Launch shape per head dim: waves per workgroup and 32-row blocks per wave.
-template <int D> struct Cfg;
-template <> struct Cfg<128> { static constexpr int W = kWaves, RB = kRowBlocks; static constexpr bool PIPE = kPipe; };
-template <> struct Cfg<64> { static constexpr int W = kWaves, RB = kRowBlocks; static constexpr bool PIPE = kPipe; };
 
 template <typename Tag, int D, bool CAUSAL>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
                       float scale, hipStream_t stream) {
-  constexpr int W = Cfg<D>::W, RB = Cfg<D>::RB, BM = W * RB * 32;
-  constexpr bool PIPE = Cfg<D>::PIPE;
+  constexpr int BM = kWaves * 32;
   const int n_mtiles = (int)((N + BM - 1) / BM);
   const int64_t total = BH * n_mtiles;
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, RB, PIPE>), dim3((unsigned)total), dim3(W * 64), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, kWaves>), dim3((unsigned)total), dim3(kWaves * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N, n_mtiles,
                      (int)total, scale * kLog2e);
   return hipGetLastError();
@@ -405,7 +391,7 @@ hipError_t launch_fwd_f16(const void* q, const void* k, const void* v, void* o, 
 }
 
 int64_t max_workgroups_fwd16(int64_t BH, int64_t N) {
-  constexpr int BM = kWaves * kRowBlocks * 32;   // the smallest tile of any head dim
+  constexpr int BM = kWaves * 32;
   return BH * ((N + BM - 1) / BM);
 }
 

@@ -59,10 +59,15 @@ __device__ __forceinline__ uint32_t pack2(F16Tag, float a, float b) {
 __device__ __forceinline__ void permlane32_swap_pair(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+// IEEE-754 2019 maximum (NaN-propagating): one v_maximum3_f32, with no canonicalising
+// v_max of each input as fmaxf needs.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+}
 __device__ __forceinline__ float max_halves(float x) {
   float a = x, b = x;
   permlane32_swap_pair(a, b);
-  return fmaxf(a, b);
+  return __builtin_elementwise_maximum(a, b);
 }
 __device__ __forceinline__ float add_halves(float x) {
   float a = x, b = x;
