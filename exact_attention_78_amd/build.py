@@ -30,11 +30,12 @@ COMMON = [
 ]
 
 
-# Per-source flags. The 16-bit attention kernel is written in issue order (its main loop
-# interleaves MFMAs, LDS reads and softmax VALU work by hand), so the machine scheduler
-# is switched off for that file.
+# Per-source flags. The attention kernels are written in issue order (their main loops
+# interleave MFMAs, LDS reads and softmax VALU work by hand), so the machine scheduler
+# is switched off for those files.
 FILE_FLAGS = {
     "attn_fwd.hip": ["-mllvm", "-enable-misched=0", "-mllvm", "-enable-post-misched=0"],
+    "attn_fwd_fp8.hip": ["-mllvm", "-enable-misched=0", "-mllvm", "-enable-post-misched=0"],
 }
 
 

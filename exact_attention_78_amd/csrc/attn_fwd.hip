@@ -56,41 +56,6 @@ template <> struct Swz<64> {
   static __device__ __forceinline__ int v(int r) { return ((r >> 1) & 1) << 2; }
 };
 
-// Wait until at most N vector-memory loads of this wave are outstanding.
-// (s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at
-// their maxima; the builtin keeps the compiler's own counter tracking informed.)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Byte address of a __shared__ object in the LDS aperture.
-__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-
-// One 16-byte-per-lane global->LDS DMA (global_load_lds_dwordx4): lane i's 16 bytes land
-// at LDS byte lds_base + 16*i; lds_base must be wave-uniform (it goes through M0). The load
-// is written as inline assembly so that the compiler does not see an LDS write it would
-// guard with a full vmcnt(0) drain before every later LDS read: completion is tracked by
-// hand with wait_vmcnt<>() and barrier_lds(). No compiler-generated code in this kernel
-// uses M0, so setting it here is safe.
-__device__ __forceinline__ void dma_load16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gptr), "s"(lds_base) : "memory");
-}
-
-// Workgroup barrier for LDS hand-over only: LDS reads of this wave are complete, then
-// s_barrier. Unlike __syncthreads() it does not drain this wave's outstanding global
-// loads, so a load for a later tile can stay in flight across it.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <int I>
-using IC = std::integral_constant<int, I>;
-
 template <typename Tag, int D, bool CAUSAL, int W>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,

@@ -2,23 +2,27 @@
 //
 // Inputs are E4M3 codes with one fp32 scale per 128-row block of each (batch, head)
 // ("8.3 FlashAttention-3", section 5.1: block quantisation; section 5: fp8 operands,
-// fp32 accumulation). The tiling is the one of the 16-bit kernel (FlashAttention-2
-// digest, framework-overview flowchart: online softmax over streamed K/V tiles, one
-// final rescale, O and LSE written; split-Q waves; causal tiles above the diagonal
-// skipped, masks only on diagonal / tail tiles).
+// fp32 accumulation). The tiling and pipeline are those of the 16-bit kernel
+// (FlashAttention-2 digest, framework-overview flowchart: online softmax over streamed
+// K/V tiles, one final rescale, O and LSE written; split-Q waves of 32 rows, 8 waves per
+// workgroup; causal tiles above the diagonal skipped, masks only on diagonal / tail
+// tiles; step t issues P.V of tile t, the softmax of tile t+1 and S^T of tile t+2, with
+// MFMAs, LDS reads and VALU work written in issue order).
 //
 // Per tile of 64 keys (inside one 128-row scale block of K and V):
-//   S^T = K Q^T with v_mfma_f32_32x32x64_f8f6f4 on the raw codes; the block scales and
-//   scale*log2(e) are one per-tile factor c_t = scale*log2e*sq*sk applied inside the
-//   exp2 argument (the running max is kept in these log2 units).
-//   P is produced as 2^8 * P, so that the row's largest probability (1) is exactly 256
-//   in E4M3 and the smallest ones stay clear of the subnormal range; it is rounded to
-//   E4M3 (v_cvt_pk_fp8_f32) and fed to the P.V MFMA against the raw V codes. The V block
-//   scale is applied in fp32: the accumulator is kept in units of the current tile's V
-//   scale, so moving to a tile with another scale multiplies it by the old/new ratio,
-//   folded into the online-softmax rescale factor. The row sum l is accumulated from the
-//   unrounded fp32 probabilities; the epilogue multiplies by the last V scale and
-//   divides by l once.
+//   S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 on the raw codes (two per 32 keys);
+//   the block scales and scale*log2(e) form one factor c_t = scale*log2e*sq*sk applied
+//   inside the exp2 argument (the running max M is kept in these log2 units).
+//   P enters the P.V MFMA as E4M3 codes of P' = 2^kPShift * 2^(s - M): the running max
+//   is raised lazily (by more than kTau only), so P' <= 2^(kPShift+kTau) = 256 stays below
+//   the E4M3 maximum (448) while probabilities down to 2^-15 of the max stay
+//   representable. The accumulator is kept in units of the current V block scale: when
+//   the tiles move to the next 128-key block (every second tile) it is multiplied by
+//   sv_old / sv_new, together with any owed running-max rescale.
+//   O is normalised by the sum of the *rounded* P' codes, accumulated by one more MFMA
+//   per tile whose A operand is all ones (E4M3 1.0): numerator and denominator then use
+//   the same weights, so a row dominated by one key returns that key's V row however
+//   P' rounds. The LSE uses the sum of the unrounded fp32 probabilities.
 //   V^T is gathered with ds_read_b64_tr_b8 (8-bit LDS transpose reads) in the key order
 //   the S^T accumulators give P.
 #include "device_common.h"
@@ -28,11 +32,13 @@ namespace attn {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kBM = 128;
 constexpr int kBN = 64;
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kBM = kWaves * 32;
 constexpr int kScaleRows = 128;
-constexpr float kPShift = 8.0f;   // P enters the P.V MFMA as 2^8 * P
+constexpr float kPShift = 6.0f;   // P' = 2^6 * P
+constexpr float kTau = 2.0f;      // lazy-rescale threshold (log2 units): P' <= 2^(6+2) = 256
+static_assert(kScaleRows % kBN == 0 && kBM % kScaleRows == 0, "tiles nest inside scale blocks");
 
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 
@@ -47,26 +53,32 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(p));
 }
 
-// 16-byte chunk c (of 8 per 128-byte row) of tile row r lives at chunk c ^ swz(r).
-__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz_v(int r) { return (r >> 1) & 7; }
+// 16-byte chunk c (of 8 per 128-byte row) of tile row r lives at chunk c ^ swz(r); K and V
+// tiles use the same swizzle. It depends on row bits 1..3 only.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
+__global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int nblk, int total_wg, float c_base) {
-  constexpr int NCH = kD / 16;                                  // 16-byte chunks per row (8)
-  constexpr int TILE = kBN * kD;                                // bytes per K (or V) tile
-  constexpr int CPT = kBN * NCH / kThreads;                     // chunks per thread per tile (2)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][TILE];
+  constexpr int ROW = kD;                            // bytes per K/V row
+  constexpr int TB = kBN * ROW;                      // bytes per K (or V) tile: 8 KiB
+  constexpr int LPW = TB / 1024 / kWaves;            // 1 KiB direct loads per wave per tile
+  constexpr int NS = 4;                              // ring slots per operand
+  constexpr int NKB = kBN / 32;                      // 32-key blocks per tile
+  constexpr int NDB = kD / 32;                       // 32-wide head-dim blocks of O
+  static_assert(LPW == 1, "one direct load per wave per tile");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];   // K ring, then V ring
 
   const int logical = xcd_logical_id(blockIdx.x, total_wg);
   const int bh = logical / n_mtiles;
   int mt = logical % n_mtiles;
-  if (CAUSAL) mt = n_mtiles - 1 - mt;
+  if (CAUSAL) mt = n_mtiles - 1 - mt;                // longest query tiles first
 
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
   const int half = lane / 32, l32 = lane % 32;
   const int64_t head_off = (int64_t)bh * N * kD;
   const uint8_t* Qh = Q + head_off;
@@ -75,9 +87,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   const float* sk = SK + (int64_t)bh * nblk;
   const float* sv = SV + (int64_t)bh * nblk;
 
-  const int q0 = mt * kBM + wave * 32;
+  const int q0 = mt * kBM + wave * 32;               // this wave's 32 rows (inside one Q scale block)
   const int qrow = q0 + l32;
-  const float cq = c_base * SQ[(int64_t)bh * nblk + mt];       // BM = 128: the tile is one Q scale block
+  const float cq = c_base * SQ[(int64_t)bh * nblk + min(q0 / kScaleRows, nblk - 1)];
 
   // Q^T as the B operand: for MFMA m (head-dim half), bytes [m*64 + half*32, +32) of the row.
   i32x8 qreg[2];
@@ -93,145 +105,231 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
   }
 
   const int n_ktiles = (N + kBN - 1) / kBN;
-  int kt_end = n_ktiles;
-  if (CAUSAL) kt_end = min(n_ktiles, ((mt + 1) * kBM + kBN - 1) / kBN);
-  const int wave_kt_end = CAUSAL ? min(kt_end, (q0 + 31) / kBN + 1) : kt_end;
-  const bool wave_live = q0 < N;
+  const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * kBM + kBN - 1) / kBN) : n_ktiles;
 
-  i32x4 kst[CPT], vst[CPT];
-  auto load_tile = [&](int kt) {
+  // K fragment (kb, m): row kb*32 + l32, chunks m*4 + half*2 and +1 (32 bytes).
+  uint32_t kaddr[2];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * kThreads;
-      const int r = idx / NCH, ch = idx % NCH;
-      const int key = kt * kBN + r;
-      if (key < N) {
-        kst[i] = *(const i32x4*)(Kh + (int64_t)key * kD + ch * 16);
-        vst[i] = *(const i32x4*)(Vh + (int64_t)key * kD + ch * 16);
-      } else {
-        kst[i] = i32x4{0, 0, 0, 0};
-        vst[i] = i32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * kThreads;
-      const int r = idx / NCH, ch = idx % NCH;
-      *(i32x4*)(&smem[buf][0][r * kD + ((ch ^ swz_k(r)) * 16)]) = kst[i];
-      *(i32x4*)(&smem[buf][1][r * kD + ((ch ^ swz_v(r)) * 16)]) = vst[i];
-    }
-  };
-
-  f32x16 oacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;   // running max in log2 units (score * scale * log2e)
-  float l_part = 0.f;        // sum of 2^8 * P over this lane's half of the keys
-  float sv_cur = 1.f;        // V scale whose units oacc is kept in
-
-  // lane roles in the V transpose reads
+  for (int m = 0; m < 2; ++m) kaddr[m] = l32 * ROW + (((m * 4 + half * 2) ^ swz(l32)) << 4);
+  // V^T fragment (db): four 8-byte transpose reads; read m covers the keys
+  // (m/2)*32 + ((m%2)*2 + j/4)*8 + tr_h*4 + j%4, the order of this lane's P bytes. The
+  // row offsets of m (multiples of 16) leave the swizzle unchanged.
   const int g16 = lane / 16, i16 = lane % 16;
-  const int tr_h = g16 / 2;                       // key set (which half of the k-slots)
+  const int tr_h = g16 / 2, tr_j = i16 >> 1;
+  const int tr_row = (tr_j / 4) * 8 + tr_h * 4 + (tr_j % 4);
   const int tr_col = 16 * (g16 % 2) + 8 * (i16 & 1);
-  const int tr_j = i16 >> 1;                      // slot j this lane addresses as a source
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < kt_end; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < kt_end) load_tile(kt + 1);
-
-    if (wave_live && kt < wave_kt_end) {
-      const uint8_t* Ks = smem[buf][0];
-      const uint8_t* Vs = smem[buf][1];
-      const int kblk = (kt * kBN) / kScaleRows;
-      const float ct = cq * sk[kblk];
-      const float svt = sv[kblk];
-
-      f32x16 sacc[2];
+  uint32_t vaddr[NDB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-        const int r = kb * 32 + l32;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int c0 = m * 4 + half * 2;
-          const i32x4 a0 = *(const i32x4*)(Ks + r * kD + ((c0 ^ swz_k(r)) * 16));
-          const i32x4 a1 = *(const i32x4*)(Ks + r * kD + (((c0 + 1) ^ swz_k(r)) * 16));
-          sacc[kb] = mfma_fp8(i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}, qreg[m], sacc[kb]);
-        }
-      }
-      const int key0 = kt * kBN;
-      if ((CAUSAL && key0 + kBN - 1 > q0) || (key0 + kBN > N)) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-            if ((CAUSAL && key > qrow) || key >= N) sacc[kb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = max_halves(mx) * ct;
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      const float oscale = alpha * (sv_cur / svt);
-      sv_cur = svt;
-      m_run = m_new;
-      const float bias = m_new - kPShift;           // exp2 yields 2^8 * P
-      float lsum = 0.f;
-      int pb[8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float p[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = fast_exp2(__builtin_fmaf(sacc[kb][q4 * 4 + e], ct, -bias));
-            lsum += p[e];
-          }
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-          pb[kb * 4 + q4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-        }
-      l_part = l_part * alpha + lsum;
-      const i32x8 pop = i32x8{pb[0], pb[1], pb[2], pb[3], pb[4], pb[5], pb[6], pb[7]};
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        oacc[db] *= oscale;
-        int av[8];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          // slot 8m + j  <->  key (m/2)*32 + ((m%2)*2 + j/4)*8 + h*4 + j%4
-          const int j = tr_j;
-          const int row = (m / 2) * 32 + ((m % 2) * 2 + j / 4) * 8 + tr_h * 4 + (j % 4);
-          const int col = db * 32 + tr_col;
-          const i32x2 t = lds_read_tr8(Vs + row * kD + (((col >> 4) ^ swz_v(row)) << 4) + (col & 15));
-          av[2 * m] = t[0];
-          av[2 * m + 1] = t[1];
-        }
-        oacc[db] = mfma_fp8(i32x8{av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]}, pop, oacc[db]);
-      }
-    }
-
-    if (kt + 1 < kt_end) store_tile(buf ^ 1);
-    __syncthreads();
+  for (int db = 0; db < NDB; ++db) {
+    const int col = db * 32 + tr_col;
+    vaddr[db] = tr_row * ROW + (((col >> 4) ^ swz(tr_row)) << 4) + (col & 15);
   }
 
-  if (!wave_live || qrow >= N) return;
-  const float l_tot = add_halves(l_part);
-  const float inv = sv_cur / l_tot;
+  // Direct global -> LDS loads: wave w fills bytes [w*1024, +1024) of a tile, 16 per lane.
+  const int ld_slot = wave * 1024 + lane * 16;
+  const int ld_row = ld_slot / ROW;
+  const int ld_ch = ((ld_slot % ROW) / 16) ^ swz(ld_row);
+  const int ld_off = ld_row * ROW + ld_ch * 16;
+  auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* { return lds + decltype(SLOT)::value * TB; };
+  auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* {
+    return lds + (NS + decltype(SLOT)::value) * TB;
+  };
+  auto load_tile = [&](const uint8_t* src, int kt, uint8_t* dst) __attribute__((always_inline)) {
+    if (kt * kBN + kBN <= N) {
+      dma_load16(src + (int64_t)kt * TB + ld_off, lds_u32(dst) + wave * 1024);
+    } else {   // rows past the end re-read the last row (masked scores, P = 0)
+      const int key = min(kt * kBN + ld_row, N - 1);
+      dma_load16(src + (int64_t)key * ROW + ld_ch * 16, lds_u32(dst) + wave * 1024);
+    }
+  };
+  auto kfrag = [&](const uint8_t* kb_base, int kb, int m) __attribute__((always_inline)) -> i32x8 {
+    const uint8_t* p = kb_base + kb * 32 * ROW + kaddr[m];
+    const i32x4 a0 = *(const i32x4*)p;
+    const i32x4 a1 = *(const i32x4*)(kb_base + kb * 32 * ROW + (kaddr[m] ^ 16));
+    return i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  };
+  auto qk = [&](auto SLOT, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      S[kb] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) S[kb] = mfma_fp8(kfrag(kbuf(SLOT), kb, m), qreg[m], S[kb]);
+    }
+  };
+
+  f32x16 oacc[NDB], lacc = f32x16{};   // P'.V (in units of the current V scale) and sum of rounded P'
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  // Running max M (log2 units), this lane's partial row sum of the unrounded
+  // probabilities (for the LSE), and a pending rescale factor of the accumulators.
+  float M = -INFINITY, l_part = 0.f, alpha_pend = 1.f;
+
+  // Per-tile constants of tile u: score factor and V block scale.
+  auto tile_c = [&](int u) __attribute__((always_inline)) { return cq * sk[min(u * kBN / kScaleRows, nblk - 1)]; };
+  auto tile_sv = [&](int u) __attribute__((always_inline)) { return sv[min(u * kBN / kScaleRows, nblk - 1)]; };
+
+  auto mask_tile = [&](int u, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
+    const int key0 = u * kBN;
+    if ((CAUSAL && key0 + kBN - 1 > q0) || key0 + kBN > N) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+          if ((CAUSAL && key > qrow) || key >= N) S[kb][r] = -INFINITY;
+        }
+    }
+  };
+  auto max_pairs = [&](float (&m4)[4], const f32x16 (&S)[NKB], int e_begin, int e_end) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = e_begin; e < e_end; e += 2)
+      m4[(e / 2) % 4] = max3f(m4[(e / 2) % 4], S[e / 16][e % 16], S[e / 16][e % 16 + 1]);
+  };
+  // Raise M when some row of the wave grew by more than kTau (branch-free); l is
+  // rescaled at once, O at the start of the next step. Returns whether M moved.
+  auto max_final = [&](const float (&m4)[4], float ct) __attribute__((always_inline)) -> bool {
+    const float mx = max_halves(max3f(m4[0], m4[1], __builtin_elementwise_maximum(m4[2], m4[3]))) * ct;
+    const bool grow = __builtin_amdgcn_ballot_w64(mx > M + kTau) != 0;
+    const float M_new = grow ? __builtin_elementwise_maximum(M, mx) : M;
+    const float alpha = grow ? fast_exp2(M - M_new) : 1.f;
+    M = M_new;
+    l_part *= alpha;
+    alpha_pend *= alpha;
+    return grow;
+  };
+  // P' of scores [e0, e1): fp32, summed (two chains), rounded to E4M3 four per word.
+  auto exps = [&](const f32x16 (&S)[NKB], int (&P)[8], float (&pe)[NKB * 16], float (&lsum)[2], float ct,
+                  float bias, int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) {
+      pe[e] = fast_exp2(__builtin_fmaf(S[e / 16][e % 16], ct, -bias));
+      lsum[e % 2] += pe[e];
+      if (e % 4 == 1) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(pe[e - 1], pe[e], 0, false);
+      if (e % 4 == 3) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(pe[e - 1], pe[e], P[e / 4], true);
+    }
+  };
+  // Owed running-max rescale, and (at the first tile of a V scale block) the change of
+  // V units sv_old / sv_new of the P.V accumulator.
+  auto rescale = [&](float sv_ratio) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha_pend * sv_ratio;
+    lacc *= alpha_pend;
+    alpha_pend = 1.f;
+  };
+
+  f32x16 Sa[NKB], Sb[NKB];
+  int Pa[8], Pb[8];
+  bool pend = false;     // wave-uniform: an O rescale is owed
+
+  // Step t: S(t+1) in S_soft, S(t+2) -> S_new, P(t) in P_use, P(t+1) -> P_new;
+  // K(t+2) in K slot (t+2)%4, V(t) in V slot t%4; loads K(t+4) -> K slot t%4 and
+  // V(t+3) -> V slot (t+3)%4 (clamped past the last tile, never read; the scores of tile
+  // T, if computed, are fully masked).
+  auto step = [&](int t, f32x16 (&S_soft)[NKB], f32x16 (&S_new)[NKB], const int (&P_use)[8], int (&P_new)[8],
+                  auto KRD, auto VRD, auto KLD, auto VLD) __attribute__((always_inline)) {
+    load_tile(Kh, min(t + 4, T - 1), kbuf(KLD));
+    load_tile(Vh, min(t + 3, T - 1), vbuf(VLD));
+    static_assert(kScaleRows == 2 * kBN, "a V scale block spans two tiles");
+    if constexpr (decltype(VRD)::value % 2 == 0) {   // t even: tile t opens a V scale block
+      rescale(t > 0 ? tile_sv(t - 1) * __builtin_amdgcn_rcpf(tile_sv(t)) : 1.f);
+    } else {
+      if (pend) rescale(1.f);
+    }
+    mask_tile(t + 1, S_soft);
+    const float ct = tile_c(t + 1);
+    // Main block in issue order: 4 S^T MFMAs (K fragments one MFMA ahead) and 4 P.V
+    // MFMAs (V^T fragments one MFMA ahead); the row max runs beside the first two S^T
+    // MFMAs, the exponentials beside the other six.
+    i32x8 kf[4], vf[NDB];
+    auto kread = [&](int i) __attribute__((always_inline)) { kf[i] = kfrag(kbuf(KRD), i % NKB, i / NKB); };
+    auto vread = [&](int db) __attribute__((always_inline)) {
+      int av[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const i32x2 x = lds_read_tr8(vbuf(VRD) + ((m / 2) * 32 + (m % 2) * 16) * ROW + vaddr[db]);
+        av[2 * m] = x[0];
+        av[2 * m + 1] = x[1];
+      }
+      vf[db] = i32x8{av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
+    };
+    float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
+    float lsum[2] = {0.f, 0.f}, pe[NKB * 16], bias = 0.f;
+    kread(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {               // i = m * NKB + kb
+      if (i + 1 < 4) kread(i + 1);
+      else vread(0);
+      const int kb = i % NKB, m = i / NKB;
+      S_new[kb] = mfma_fp8(kf[i], qreg[m], m == 0 ? f32x16{} : S_new[kb]);
+      if (i == 0) {
+        max_pairs(m4, S_soft, 4, 18);
+      } else if (i == 1) {
+        max_pairs(m4, S_soft, 18, NKB * 16);
+        pend = max_final(m4, ct);
+        bias = M - kPShift;
+      } else {
+        exps(S_soft, P_new, pe, lsum, ct, bias, (i - 2) * 5, (i - 1) * 5);   // scores 0..9
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      if (db + 1 < NDB) vread(db + 1);
+      const i32x8 pb = {P_use[0], P_use[1], P_use[2], P_use[3], P_use[4], P_use[5], P_use[6], P_use[7]};
+      oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
+      if (db == NDB - 1) {
+        // all-ones A operand (E4M3 1.0), built here from a value tied to t so that it is
+        // not kept live across the loop (t < 2^30, so the shift adds 0)
+        const int one4 = 0x38383838 + (t >> 30);
+        lacc = mfma_fp8(i32x8{one4, one4, one4, one4, one4, one4, one4, one4}, pb, lacc);
+      }
+      exps(S_soft, P_new, pe, lsum, ct, bias, 10 + db * 22 / 4, 10 + (db + 1) * 22 / 4);   // scores 10..31
+    }
+    l_part += lsum[0] + lsum[1];
+    wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
+    barrier_lds();
+  };
+
+  // Prologue: K tiles 0..3 and V tiles 0..2; S(0), softmax of tile 0, S(1).
+  load_tile(Kh, 0, kbuf(IC<0>{}));
+  load_tile(Kh, min(1, T - 1), kbuf(IC<1>{}));
+  load_tile(Kh, min(2, T - 1), kbuf(IC<2>{}));
+  load_tile(Kh, min(3, T - 1), kbuf(IC<3>{}));
+  load_tile(Vh, 0, vbuf(IC<0>{}));
+  load_tile(Vh, min(1, T - 1), vbuf(IC<1>{}));
+  load_tile(Vh, min(2, T - 1), vbuf(IC<2>{}));
+  wait_vmcnt<0>();
+  barrier_lds();
+  qk(IC<0>{}, Sa);
+  {
+    mask_tile(0, Sa);
+    const float ct = tile_c(0);
+    float m4[4] = {Sa[0][0], Sa[0][1], Sa[0][2], Sa[0][3]};
+    max_pairs(m4, Sa, 4, NKB * 16);
+    max_final(m4, ct);
+    alpha_pend = 1.f;            // O is still zero: no rescale owed
+    const float bias = M - kPShift;
+    float pe[NKB * 16], lsum[2] = {0.f, 0.f};
+    exps(Sa, Pa, pe, lsum, ct, bias, 0, NKB * 16);
+    l_part += lsum[0] + lsum[1];
+  }
+  qk(IC<1>{}, Sb);
+  barrier_lds();                 // K slots 0 and 1 are refilled from step 0 on
+
+  for (int t = 0; t < T; t += 4) {
+    step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{});
+    if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{});
+    if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{});
+    if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{});
+  }
+  wait_vmcnt<0>();               // no load may still target this workgroup's LDS when it exits
+  if (pend) rescale(1.f);
+
+  const float l_tot = add_halves(l_part) * (1.f / (1 << (int)kPShift));   // sum of probabilities
+  if (qrow >= N) return;
+  const float inv = tile_sv(T - 1) / lacc[0];    // accumulator is in units of the last tile's V scale
   uint16_t* Orow = O + head_off + (int64_t)qrow * kD;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = db * 32 + g * 8 + half * 4;
@@ -240,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(
                  pack2(Bf16Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
       *(u32x2*)(Orow + d) = w;
     }
-  if (half == 0) LSE[(int64_t)bh * N + qrow] = (m_run + __builtin_log2f(l_tot) - kPShift) * kLn2;
+  if (half == 0) LSE[(int64_t)bh * N + qrow] = (M + __builtin_log2f(l_tot)) * kLn2;
 }
 
 template <bool CAUSAL>
@@ -249,8 +347,8 @@ hipError_t launch(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const
   const int n_mtiles = (int)((N + kBM - 1) / kBM);
   const int nblk = (int)((N + kScaleRows - 1) / kScaleRows);
   const int64_t total = BH * n_mtiles;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL>), dim3((unsigned)total), dim3(kThreads), 0, stream, q8, k8, v8, sq,
-                     sk, sv, (uint16_t*)o, lse, (int)N, n_mtiles, nblk, (int)total, scale * kLog2e);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL>), dim3((unsigned)total), dim3(kWaves * 64), 0, stream, q8, k8, v8,
+                     sq, sk, sv, (uint16_t*)o, lse, (int)N, n_mtiles, nblk, (int)total, scale * kLog2e);
   return hipGetLastError();
 }
 
