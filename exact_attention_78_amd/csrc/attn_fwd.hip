@@ -69,7 +69,10 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   constexpr int LPW = TB / 1024 / W;                // 1 KiB direct loads per wave per tile
   constexpr int NS = 4;                             // ring slots per operand
   static_assert(LPW >= 1 && LPW * 1024 * W == TB, "tile must split into whole 1 KiB loads per wave");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];   // K ring, then V ring
+  // V ring first, then K ring: the 32 V transpose reads of a step then fit the 16-bit
+  // immediate offset of ds_read (< 64 KiB) with no address add; the K reads need one add
+  // per head-dim step.
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];
 
   const int logical = xcd_logical_id(blockIdx.x, total_wg);
   const int bh = logical / n_mtiles;
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
 
   uint32_t kaddr[NSTEP];
 #pragma unroll
-  for (int s = 0; s < NSTEP; ++s) kaddr[s] = l32 * ROW + (((2 * s + half) ^ Swz<D>::k(l32)) << 4);
+  for (int s = 0; s < NSTEP; ++s) kaddr[s] = NS * TB + l32 * ROW + (((2 * s + half) ^ Swz<D>::k(l32)) << 4);
   const int g16 = lane / 16, i16 = lane % 16;
   const int tr_row = (g16 / 2) * 4 + i16 / 4;
   const int tr_col = 16 * (g16 % 2) + 4 * (i16 % 4);
@@ -119,10 +122,15 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     ld_koff[i] = (ld_row[i] * D + ld_kch[i]) * 2;
     ld_voff[i] = (ld_row[i] * D + ld_vch[i]) * 2;
   }
-  auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* { return lds + decltype(SLOT)::value * TB; };
-  auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* {
+  // K slot SLOT is at lds + (NS + SLOT) * TB; reads add the ring base through kaddr (a
+  // register), so that only SLOT * TB + the 32-key block offset is an immediate.
+  auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* {
     return lds + (NS + decltype(SLOT)::value) * TB;
   };
+  auto kread_base = [&](auto SLOT) __attribute__((always_inline)) -> const uint8_t* {
+    return lds + decltype(SLOT)::value * TB;
+  };
+  auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* { return lds + decltype(SLOT)::value * TB; };
   auto load_tile = [&](const uint16_t* src, const int (&off)[LPW], const int (&ch)[LPW], int kt, uint8_t* dst)
                        __attribute__((always_inline)) {
     if (kt * kBN + kBN <= N) {
@@ -144,7 +152,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       S[kb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s)
-        S[kb] = mfma32(Tag{}, *(const u32x4*)(kbuf(SLOT) + kb * 32 * ROW + kaddr[s]), qreg[s], S[kb]);
+        S[kb] = mfma32(Tag{}, *(const u32x4*)(kread_base(SLOT) + kb * 32 * ROW + kaddr[s]), qreg[s], S[kb]);
     }
   };
   f32x16 oacc[NDB];
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     constexpr int NSLOT = NQ + NP - 5;                 // MFMAs that carry exponentials
     u32x4 kf[NQ], vf[NP];
     auto kread = [&](int i) __attribute__((always_inline)) {   // i = s * NKB + kb
-      kf[i] = *(const u32x4*)(kbuf(KRD) + (i % NKB) * 32 * ROW + kaddr[i / NKB]);
+      kf[i] = *(const u32x4*)(kread_base(KRD) + (i % NKB) * 32 * ROW + kaddr[i / NKB]);
     };
     auto vread = [&](int i) __attribute__((always_inline)) {   // i = (kb * 2 + h) * NDB + db
       const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
