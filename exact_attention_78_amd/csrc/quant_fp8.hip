@@ -1,18 +1,19 @@
 // fp8 input preparation on gfx950: optional Hadamard rotation of each row, then
 // per-128-row-block E4M3 quantisation ("8.3 FlashAttention-3", sections 5.1 and 5.2).
 //
-// One workgroup owns one (batch*head, 128-row block). Each lane holds 16-byte chunks
-// (8 consecutive elements) of the block, so a row of d elements spans d/8 neighbouring
-// lanes. The fast Walsh-Hadamard butterfly runs in fp32: the spans 1, 2, 4 combine
-// elements inside a lane, the spans 8 .. d/2 combine a lane with the lane whose chunk
-// index differs in one bit, fetched with DPP lane moves. Every butterfly output is one
-// rounded fp32 add or subtract of the same two operands at every stage, so the result
-// does not depend on how the stages are scheduled. The scale of a block is
-// fp32(amax / 448) (1 for an all-zero block); each element becomes the nearest E4M3FN
-// code to clamp(fp32(x / scale), -448, 448) via v_cvt_pk_fp8_f32 (round to nearest
-// even on gfx950; out-of-range inputs would give NaN, hence the clamp).
+// One workgroup owns one (batch*head, 128-row block). Each lane holds a 32-element
+// segment of a row (64 contiguous bytes), so a row of d elements spans d/32 neighbouring
+// lanes. The fast Walsh-Hadamard butterfly runs in fp32 with its stages in the usual
+// order (spans 1, 2, 4, ..., d/2): the spans 1..16 combine elements inside a lane, the
+// spans 32 and 64 combine a lane with its neighbour (lane xor 1, xor 2) through a DPP
+// quad permutation. Every butterfly output is one rounded fp32 add or subtract of the
+// same two operands as in the textbook network, so the result does not depend on how
+// the elements are laid out. The scale of a block is fp32(amax / 448) (1 for an
+// all-zero block); each element becomes the nearest E4M3FN code to
+// clamp(fp32(x / scale), -448, 448) via v_cvt_pk_fp8_f32 (round to nearest even on
+// gfx950; out-of-range inputs would give NaN, hence the clamp).
 //
-// The kernel is bound by HBM: it reads 2 bytes and writes 1 byte per element.
+// The kernel reads 2 bytes and writes 1 byte per element.
 #include "device_common.h"
 #include "launch.h"
 
@@ -22,37 +23,11 @@ namespace {
 constexpr int kRowsPerBlock = 128;
 constexpr int kThreads = 256;
 
-// DPP lane moves within 16-lane rows (controls: quad_perm, row_shl, row_shr).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-
-// Value held by the lane whose index differs in bit b (b = 0..3), same slot.
+// Value held by lane (this lane xor 1) or (xor 2): DPP quad permutations.
 template <int B>
-__device__ __forceinline__ float xor_lane(float x, int lane) {
-  if constexpr (B == 0) return dpp<0xB1>(x);                          // quad_perm [1,0,3,2]
-  else if constexpr (B == 1) return dpp<0x4E>(x);                     // quad_perm [2,3,0,1]
-  else if constexpr (B == 2) {
-    const float up = dpp<0x104>(x);                                   // row_shl:4 -> lane+4
-    const float dn = dpp<0x114>(x);                                   // row_shr:4 -> lane-4
-    return (lane & 4) ? dn : up;
-  } else {
-    const float up = dpp<0x108>(x);                                   // row_shl:8 -> lane+8
-    const float dn = dpp<0x118>(x);                                   // row_shr:8 -> lane-8
-    return (lane & 8) ? dn : up;
-  }
-}
-
-// One cross-lane butterfly stage over all 8 slots of a chunk: chunk-index bit B.
-template <int B>
-__device__ __forceinline__ void cross_stage(float (&x)[8], int lane) {
-  const bool upper = (lane >> B) & 1;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float p = xor_lane<B>(x[e], lane);
-    x[e] = upper ? (p - x[e]) : (x[e] + p);
-  }
+__device__ __forceinline__ float xor_lane(float x) {
+  constexpr int ctrl = B == 0 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
@@ -62,58 +37,74 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __r
                                                              float* __restrict__ scales,
                                                              const float* __restrict__ signs, int N, int nblk,
                                                              float inv_sqrt_d) {
-  constexpr int NCH = D / 8;                                   // chunks per row
-  constexpr int CPT = kRowsPerBlock * NCH / kThreads;          // chunks per thread
+  constexpr int EPL = 32;                                      // elements per lane segment
+  constexpr int LPR = D / EPL;                                 // lanes per row (4 or 2)
+  constexpr int RPP = kThreads / LPR;                          // rows per pass
+  constexpr int PASSES = kRowsPerBlock / RPP;                  // 2 or 1
   __shared__ float wave_max[kThreads / 64];
 
   const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
   const int tid = threadIdx.x, lane = tid % 64;
-  const int c = tid % NCH;                                     // this lane's chunk within a row
+  const int seg = tid % LPR;                                   // this lane's segment of a row
   const int64_t base = ((int64_t)bh * N + (int64_t)blk * kRowsPerBlock) * D;
 
-  float sg[8];
+  float sg[EPL];
   if constexpr (ROTATE) {
-    const f32x4 s0 = *(const f32x4*)(signs + c * 8), s1 = *(const f32x4*)(signs + c * 8 + 4);
-    sg[0] = s0[0]; sg[1] = s0[1]; sg[2] = s0[2]; sg[3] = s0[3];
-    sg[4] = s1[0]; sg[5] = s1[1]; sg[6] = s1[2]; sg[7] = s1[3];
+#pragma unroll
+    for (int i = 0; i < EPL / 4; ++i) {
+      const f32x4 v = *(const f32x4*)(signs + seg * EPL + i * 4);
+      sg[4 * i] = v[0]; sg[4 * i + 1] = v[1]; sg[4 * i + 2] = v[2]; sg[4 * i + 3] = v[3];
+    }
   }
+  // +1 for the lower, -1 for the upper lane of a cross-lane pair: out = partner + sign * own
+  float lane_sign[2];
+  lane_sign[0] = (seg & 1) ? -1.f : 1.f;
+  lane_sign[1] = (seg & 2) ? -1.f : 1.f;
 
-  float x[CPT][8];
+  float x[PASSES][EPL];
   float amax = 0.f;
 #pragma unroll
-  for (int p = 0; p < CPT; ++p) {
-    const int idx = tid + p * kThreads;
-    const int row = idx / NCH;
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = tid / LPR + p * RPP;
     const bool valid = blk * kRowsPerBlock + row < N;
-    u32x4 raw = valid ? *(const u32x4*)(X + base + (int64_t)row * D + c * 8) : u32x4{0, 0, 0, 0};
+    const uint16_t* src = X + base + (int64_t)row * D + seg * EPL;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[p][2 * e] = bf16_to_f32(raw[e] & 0xFFFFu);
-      x[p][2 * e + 1] = bf16_to_f32(raw[e] >> 16);
+    for (int i = 0; i < EPL / 8; ++i) {
+      const u32x4 raw = valid ? *(const u32x4*)(src + i * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[p][i * 8 + 2 * e] = bf16_to_f32(raw[e] & 0xFFFFu);
+        x[p][i * 8 + 2 * e + 1] = bf16_to_f32(raw[e] >> 16);
+      }
     }
     if constexpr (ROTATE) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[p][e] *= sg[e];
-      // spans 1, 2, 4: inside the lane
+      for (int e = 0; e < EPL; ++e) x[p][e] *= sg[e];          // exact (+-1)
+      // spans 1 .. 16: inside the lane
 #pragma unroll
-      for (int h = 1; h < 8; h *= 2)
+      for (int h = 1; h < EPL; h *= 2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < EPL; ++e)
           if (!(e & h)) {
             const float a = x[p][e], b = x[p][e + h];
             x[p][e] = a + b;
             x[p][e + h] = a - b;
           }
-      // spans 8 .. D/2: across lanes
-      cross_stage<0>(x[p], lane);
-      cross_stage<1>(x[p], lane);
-      cross_stage<2>(x[p], lane);
-      if constexpr (D == 128) cross_stage<3>(x[p], lane);
+      // spans 32, 64: across lanes; the upper lane of a pair gets partner - own, the
+      // lower own + partner, each one rounded fp32 operation (fma with a +-1 factor)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[p][e] *= inv_sqrt_d;
+      for (int e = 0; e < EPL; ++e) x[p][e] = __builtin_fmaf(lane_sign[0], x[p][e], xor_lane<0>(x[p][e]));
+      if constexpr (LPR == 4) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[p][e] = __builtin_fmaf(lane_sign[1], x[p][e], xor_lane<1>(x[p][e]));
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[p][e] *= inv_sqrt_d;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[p][e]));
+    for (int e = 0; e < EPL; e += 2)
+      amax = __builtin_elementwise_maximum(amax, __builtin_elementwise_maximum(__builtin_fabsf(x[p][e]),
+                                                                                __builtin_fabsf(x[p][e + 1])));
   }
 
   // block amax: wave reduction, then across the 4 waves
@@ -123,20 +114,35 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __r
   __syncthreads();
   amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
   const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+  // x / s, correctly rounded, from the correctly rounded reciprocal y = 1/s (one IEEE
+  // division per thread) and one FMA correction per element (Markstein's division
+  // theorem: with y within half an ulp of 1/s and q0 = RN(x*y) close to x/s, the residual
+  // r = x - s*q0 is exact and RN(q0 + r*y) is the correctly rounded quotient; checked
+  // against exact rational arithmetic on the CPU and bit-exactly against the oracle).
+  const float y_rcp = 1.0f / s;
 
 #pragma unroll
-  for (int p = 0; p < CPT; ++p) {
-    const int idx = tid + p * kThreads;
-    const int row = idx / NCH;
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = tid / LPR + p * RPP;
     if (blk * kRowsPerBlock + row >= N) continue;
-    float y[8];
+    int w[EPL / 4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(x[p][e] / s, -448.0f), 448.0f);
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
-    *(u32x2*)(X8 + base + (int64_t)row * D + c * 8) = u32x2{(uint32_t)w0, (uint32_t)w1};
+    for (int e = 0; e < EPL; e += 2) {
+      float y[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float xv = x[p][e + k];
+        const float q0 = xv * y_rcp;
+        // (copysign keeps the sign of a zero input: -0 / s is -0, but the correction sums +0 and -0)
+        const float q = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, xv), y_rcp, q0), xv);
+        y[k] = fminf(fmaxf(q, -448.0f), 448.0f);
+      }
+      if (e % 4 == 0) w[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      else w[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], w[e / 4], true);
+    }
+    uint8_t* dst = X8 + base + (int64_t)row * D + seg * EPL;
+    *(u32x4*)dst = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
+    *(u32x4*)(dst + 16) = u32x4{(uint32_t)w[4], (uint32_t)w[5], (uint32_t)w[6], (uint32_t)w[7]};
   }
   if (tid == 0) scales[(int64_t)bh * nblk + blk] = s;
 }
