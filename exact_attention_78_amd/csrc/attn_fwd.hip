@@ -196,16 +196,20 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     alpha_pend *= alpha;
     return grow;
   };
-  // Probabilities of scores e in [e0, e1): P = 2^(S*c - M) in fp32, added to the row sum
-  // (two chains) before rounding, then rounded to 16 bits and packed in pairs into the
-  // B operand of P.V.
-  auto exps = [&](const f32x16 (&S)[NKB], u32x4 (&P)[NKB][2], float (&pe)[NKB * 16], float (&lsum)[2], int e0,
-                  int e1) __attribute__((always_inline)) {
+  // Probabilities of scores e in [e0, e1): P = 2^(S*c - M) in fp32, written over the
+  // scores (exps); later, so that the exponentials' latency is covered, their row sum
+  // (two chains, before rounding) and the rounding to 16 bits, packed in pairs into the
+  // B operand of P.V (finish).
+  auto exps = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = fast_exp2(__builtin_fmaf(S[e / 16][e % 16], c, -M));
+  };
+  auto finish = [&](const f32x16 (&S)[NKB], u32x4 (&P)[NKB][2], float (&lsum)[2], int e0, int e1)
+                    __attribute__((always_inline)) {
 #pragma unroll
     for (int e = e0; e < e1; ++e) {
-      pe[e] = fast_exp2(__builtin_fmaf(S[e / 16][e % 16], c, -M));
-      lsum[e % 2] += pe[e];
-      if (e % 2 == 1) P[e / 16][(e % 16) / 8][(e % 8) / 2] = pack2(Tag{}, pe[e - 1], pe[e]);
+      lsum[e % 2] += S[e / 16][e % 16];
+      if (e % 2 == 1) P[e / 16][(e % 16) / 8][(e % 8) / 2] = pack2(Tag{}, S[e / 16][e % 16 - 1], S[e / 16][e % 16]);
     }
   };
   auto rescale_o = [&]() __attribute__((always_inline)) {
@@ -248,9 +252,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     };
     float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
     float lsum[2] = {0.f, 0.f};
-    float pe[NKB * 16];
-    auto exps_slot = [&](int slot) __attribute__((always_inline)) {
-      exps(S_soft, P_new, pe, lsum, slot * (NKB * 16) / NSLOT, (slot + 1) * (NKB * 16) / NSLOT);
+    auto exps_slot = [&](int slot) __attribute__((always_inline)) {   // exps of this slot, finish of the last
+      exps(S_soft, slot * (NKB * 16) / NSLOT, (slot + 1) * (NKB * 16) / NSLOT);
+      if (slot > 0) finish(S_soft, P_new, lsum, (slot - 1) * (NKB * 16) / NSLOT, slot * (NKB * 16) / NSLOT);
     };
 #pragma unroll
     for (int i = 0; i < KD; ++i) kread(i);
@@ -274,6 +278,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       oacc[db] = mfma32(Tag{}, vf[i], P_use[kb][h], oacc[db]);
       exps_slot(NQ - 5 + i);
     }
+    finish(S_soft, P_new, lsum, (NSLOT - 1) * (NKB * 16) / NSLOT, NKB * 16);
     l_part += lsum[0] + lsum[1];
     wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
     barrier_lds();
@@ -296,8 +301,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     max_pairs(m4, Sa, 4, NKB * 16);
     max_final(m4);
     alpha_pend = 1.f;            // O is still zero: no rescale owed
-    float pe[NKB * 16], lsum[2] = {0.f, 0.f};
-    exps(Sa, Pa, pe, lsum, 0, NKB * 16);
+    float lsum[2] = {0.f, 0.f};
+    exps(Sa, 0, NKB * 16);
+    finish(Sa, Pa, lsum, 0, NKB * 16);
     l_part += lsum[0] + lsum[1];
   }
   qk(IC<1>{}, Sb);
