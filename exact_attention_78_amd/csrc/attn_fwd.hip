@@ -200,9 +200,13 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   // scores (exps); later, so that the exponentials' latency is covered, their row sum
   // (two chains, before rounding) and the rounding to 16 bits, packed in pairs into the
   // B operand of P.V (finish).
-  auto exps = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {
+  auto args = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {   // S*c - M
 #pragma unroll
-    for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = fast_exp2(__builtin_fmaf(S[e / 16][e % 16], c, -M));
+    for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = __builtin_fmaf(S[e / 16][e % 16], c, -M);
+  };
+  auto exps = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {     // 2^(S*c - M)
+#pragma unroll
+    for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = fast_exp2(S[e / 16][e % 16]);
   };
   auto finish = [&](const f32x16 (&S)[NKB], u32x4 (&P)[NKB][2], float (&lsum)[2], int e0, int e1)
                     __attribute__((always_inline)) {
@@ -252,9 +256,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     };
     float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
     float lsum[2] = {0.f, 0.f};
-    auto exps_slot = [&](int slot) __attribute__((always_inline)) {   // exps of this slot, finish of the last
-      exps(S_soft, slot * (NKB * 16) / NSLOT, (slot + 1) * (NKB * 16) / NSLOT);
-      if (slot > 0) finish(S_soft, P_new, lsum, (slot - 1) * (NKB * 16) / NSLOT, slot * (NKB * 16) / NSLOT);
+    // slot k: arguments of slot k+1, exponentials of slot k, sums and packing of slot k-1
+    auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
+    auto exps_slot = [&](int slot) __attribute__((always_inline)) {
+      if (slot + 1 < NSLOT) args(S_soft, lo(slot + 1), lo(slot + 2));
+      exps(S_soft, lo(slot), lo(slot + 1));
+      if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
     };
 #pragma unroll
     for (int i = 0; i < KD; ++i) kread(i);
@@ -266,8 +273,10 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       S_new[kb] = mfma32(Tag{}, kf[i], qreg[s], s == 0 ? f32x16{} : S_new[kb]);
       if (i < 4)
         max_pairs(m4, S_soft, 4 + i * 8, min(4 + (i + 1) * 8, NKB * 16));
-      else if (i == 4)
+      else if (i == 4) {
         pend = max_final(m4);
+        args(S_soft, lo(0), lo(1));
+      }
       else
         exps_slot(i - 5);
     }
@@ -278,7 +287,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       oacc[db] = mfma32(Tag{}, vf[i], P_use[kb][h], oacc[db]);
       exps_slot(NQ - 5 + i);
     }
-    finish(S_soft, P_new, lsum, (NSLOT - 1) * (NKB * 16) / NSLOT, NKB * 16);
+    finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
     l_part += lsum[0] + lsum[1];
     wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
     barrier_lds();
@@ -302,6 +311,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     max_final(m4);
     alpha_pend = 1.f;            // O is still zero: no rescale owed
     float lsum[2] = {0.f, 0.f};
+    args(Sa, 0, NKB * 16);
     exps(Sa, 0, NKB * 16);
     finish(Sa, Pa, lsum, 0, NKB * 16);
     l_part += lsum[0] + lsum[1];
