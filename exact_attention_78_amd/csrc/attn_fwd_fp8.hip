@@ -197,15 +197,25 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     alpha_pend *= alpha;
     return grow;
   };
-  // P' of scores [e0, e1): fp32, summed (two chains), rounded to E4M3 four per word.
-  auto exps = [&](const f32x16 (&S)[NKB], int (&P)[8], float (&pe)[NKB * 16], float (&lsum)[2], float ct,
-                  float bias, int e0, int e1) __attribute__((always_inline)) {
+  // P' of scores [e0, e1), in three passes issued apart so that no VALU op waits on the
+  // one before it: the exp2 arguments (args), the exponentials, written over the scores
+  // (exps), then the row sums (two chains) and the rounding to E4M3, four per word (finish).
+  auto args = [&](f32x16 (&S)[NKB], float ct, float bias, int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = __builtin_fmaf(S[e / 16][e % 16], ct, -bias);
+  };
+  auto exps = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = fast_exp2(S[e / 16][e % 16]);
+  };
+  auto finish = [&](const f32x16 (&S)[NKB], int (&P)[8], float (&lsum)[2], int e0, int e1)
+                    __attribute__((always_inline)) {
 #pragma unroll
     for (int e = e0; e < e1; ++e) {
-      pe[e] = fast_exp2(__builtin_fmaf(S[e / 16][e % 16], ct, -bias));
-      lsum[e % 2] += pe[e];
-      if (e % 4 == 1) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(pe[e - 1], pe[e], 0, false);
-      if (e % 4 == 3) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(pe[e - 1], pe[e], P[e / 4], true);
+      const float pe = S[e / 16][e % 16];
+      lsum[e % 2] += pe;
+      if (e % 4 == 1) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(S[e / 16][e % 16 - 1], pe, 0, false);
+      if (e % 4 == 3) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(S[e / 16][e % 16 - 1], pe, P[e / 4], true);
     }
   };
   // Owed running-max rescale, and (at the first tile of a V scale block) the change of
@@ -253,7 +263,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
       vf[db] = i32x8{av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
     };
     float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
-    float lsum[2] = {0.f, 0.f}, pe[NKB * 16], bias = 0.f;
+    float lsum[2] = {0.f, 0.f}, bias = 0.f;
+    // six slots (S^T MFMAs 2, 3 and the four P.V MFMAs) share the 32 scores; slot k issues
+    // the arguments of slot k+1, the exponentials of slot k and the sums of slot k-1
+    constexpr int NSLOT = 6;
+    auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
+    auto exps_slot = [&](int slot) __attribute__((always_inline)) {
+      if (slot + 1 < NSLOT) args(S_soft, ct, bias, lo(slot + 1), lo(slot + 2));
+      exps(S_soft, lo(slot), lo(slot + 1));
+      if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
+    };
     kread(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {               // i = m * NKB + kb
@@ -267,8 +286,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
         max_pairs(m4, S_soft, 18, NKB * 16);
         pend = max_final(m4, ct);
         bias = M - kPShift;
+        args(S_soft, ct, bias, lo(0), lo(1));
       } else {
-        exps(S_soft, P_new, pe, lsum, ct, bias, (i - 2) * 5, (i - 1) * 5);   // scores 0..9
+        exps_slot(i - 2);
       }
     }
 #pragma unroll
@@ -282,8 +302,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
         const int one4 = 0x38383838 + (t >> 30);
         lacc = mfma_fp8(i32x8{one4, one4, one4, one4, one4, one4, one4, one4}, pb, lacc);
       }
-      exps(S_soft, P_new, pe, lsum, ct, bias, 10 + db * 22 / 4, 10 + (db + 1) * 22 / 4);   // scores 10..31
+      exps_slot(2 + db);
     }
+    finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
     l_part += lsum[0] + lsum[1];
     wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
     barrier_lds();
@@ -308,8 +329,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     max_final(m4, ct);
     alpha_pend = 1.f;            // O is still zero: no rescale owed
     const float bias = M - kPShift;
-    float pe[NKB * 16], lsum[2] = {0.f, 0.f};
-    exps(Sa, Pa, pe, lsum, ct, bias, 0, NKB * 16);
+    float lsum[2] = {0.f, 0.f};
+    args(Sa, ct, bias, 0, NKB * 16);
+    exps(Sa, 0, NKB * 16);
+    finish(Sa, Pa, lsum, 0, NKB * 16);
     l_part += lsum[0] + lsum[1];
   }
   qk(IC<1>{}, Sb);
