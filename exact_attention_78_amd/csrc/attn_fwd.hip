@@ -235,60 +235,64 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
                   u32x4 (&P_new)[NKB][2], auto KRD, auto VRD, auto KLD, auto VLD) __attribute__((always_inline)) {
     load_tile(Kh, ld_koff, ld_kch, min(t + 4, T - 1), kbuf(KLD));
     load_tile(Vh, ld_voff, ld_vch, min(t + 3, T - 1), vbuf(VLD));
-    if (pend) rescale_o();
-    mask_tile(t + 1, S_soft);
-    // Main block, written in issue order (this file is compiled without the machine
-    // scheduler): 16 S^T MFMAs (K fragments read KD ahead) then 16 P.V MFMAs (V^T
-    // fragments read VD ahead); the softmax VALU work of tile t+1 is spread between them:
-    // the row max over the first five S^T MFMAs, then the exponentials, one or two per MFMA.
-    constexpr int NQ = NKB * NSTEP, NP = NDB * NKB * 2, KD = kKD, VD = kVD;
-    constexpr int NSLOT = NQ + NP - 5;                 // MFMAs that carry exponentials
-    u32x4 kf[NQ], vf[NP];
-    auto kread = [&](int i) __attribute__((always_inline)) {   // i = s * NKB + kb
-      kf[i] = *(const u32x4*)(kread_base(KRD) + (i % NKB) * 32 * ROW + kaddr[i / NKB]);
-    };
-    auto vread = [&](int i) __attribute__((always_inline)) {   // i = (kb * 2 + h) * NDB + db
-      const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
-      const uint8_t* base = vbuf(VRD) + (kb * 32 + h * 16) * ROW + vaddr[db];
-      const u32x2 v1 = lds_read_tr16((const uint16_t*)base);
-      const u32x2 v2 = lds_read_tr16((const uint16_t*)(base + 8 * ROW));
-      vf[i] = u32x4{v1[0], v1[1], v2[0], v2[1]};
-    };
-    float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
-    float lsum[2] = {0.f, 0.f};
-    // slot k: arguments of slot k+1, exponentials of slot k, sums and packing of slot k-1
-    auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
-    auto exps_slot = [&](int slot) __attribute__((always_inline)) {
-      if (slot + 1 < NSLOT) args(S_soft, lo(slot + 1), lo(slot + 2));
-      exps(S_soft, lo(slot), lo(slot + 1));
-      if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
-    };
+    // Causal: once the tile's first key lies past this wave's last row, this and every
+    // later tile are fully masked for the wave; it only keeps up its loads and barriers.
+    if (!CAUSAL || t * kBN <= q0 + 31) {
+      if (pend) rescale_o();
+      mask_tile(t + 1, S_soft);
+      // Main block, written in issue order (this file is compiled without the machine
+      // scheduler): 16 S^T MFMAs (K fragments read KD ahead) then 16 P.V MFMAs (V^T
+      // fragments read VD ahead); the softmax VALU work of tile t+1 is spread between them:
+      // the row max over the first five S^T MFMAs, then the exponentials, one or two per MFMA.
+      constexpr int NQ = NKB * NSTEP, NP = NDB * NKB * 2, KD = kKD, VD = kVD;
+      constexpr int NSLOT = NQ + NP - 5;                 // MFMAs that carry exponentials
+      u32x4 kf[NQ], vf[NP];
+      auto kread = [&](int i) __attribute__((always_inline)) {   // i = s * NKB + kb
+        kf[i] = *(const u32x4*)(kread_base(KRD) + (i % NKB) * 32 * ROW + kaddr[i / NKB]);
+      };
+      auto vread = [&](int i) __attribute__((always_inline)) {   // i = (kb * 2 + h) * NDB + db
+        const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
+        const uint8_t* base = vbuf(VRD) + (kb * 32 + h * 16) * ROW + vaddr[db];
+        const u32x2 v1 = lds_read_tr16((const uint16_t*)base);
+        const u32x2 v2 = lds_read_tr16((const uint16_t*)(base + 8 * ROW));
+        vf[i] = u32x4{v1[0], v1[1], v2[0], v2[1]};
+      };
+      float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
+      float lsum[2] = {0.f, 0.f};
+      // slot k: arguments of slot k+1, exponentials of slot k, sums and packing of slot k-1
+      auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
+      auto exps_slot = [&](int slot) __attribute__((always_inline)) {
+        if (slot + 1 < NSLOT) args(S_soft, lo(slot + 1), lo(slot + 2));
+        exps(S_soft, lo(slot), lo(slot + 1));
+        if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
+      };
 #pragma unroll
-    for (int i = 0; i < KD; ++i) kread(i);
+      for (int i = 0; i < KD; ++i) kread(i);
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      if (i + KD < NQ) kread(i + KD);
-      if (i + KD >= NQ && i + KD - NQ < VD) vread(i + KD - NQ);
-      const int kb = i % NKB, s = i / NKB;
-      S_new[kb] = mfma32(Tag{}, kf[i], qreg[s], s == 0 ? f32x16{} : S_new[kb]);
-      if (i < 4)
-        max_pairs(m4, S_soft, 4 + i * 8, min(4 + (i + 1) * 8, NKB * 16));
-      else if (i == 4) {
-        pend = max_final(m4);
-        args(S_soft, lo(0), lo(1));
+      for (int i = 0; i < NQ; ++i) {
+        if (i + KD < NQ) kread(i + KD);
+        if (i + KD >= NQ && i + KD - NQ < VD) vread(i + KD - NQ);
+        const int kb = i % NKB, s = i / NKB;
+        S_new[kb] = mfma32(Tag{}, kf[i], qreg[s], s == 0 ? f32x16{} : S_new[kb]);
+        if (i < 4)
+          max_pairs(m4, S_soft, 4 + i * 8, min(4 + (i + 1) * 8, NKB * 16));
+        else if (i == 4) {
+          pend = max_final(m4);
+          args(S_soft, lo(0), lo(1));
+        }
+        else
+          exps_slot(i - 5);
       }
-      else
-        exps_slot(i - 5);
-    }
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      if (i + VD < NP) vread(i + VD);
-      const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
-      oacc[db] = mfma32(Tag{}, vf[i], P_use[kb][h], oacc[db]);
-      exps_slot(NQ - 5 + i);
+      for (int i = 0; i < NP; ++i) {
+        if (i + VD < NP) vread(i + VD);
+        const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
+        oacc[db] = mfma32(Tag{}, vf[i], P_use[kb][h], oacc[db]);
+        exps_slot(NQ - 5 + i);
+      }
+      finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
+      l_part += lsum[0] + lsum[1];
     }
-    finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
-    l_part += lsum[0] + lsum[1];
     wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
     barrier_lds();
   };

@@ -163,6 +163,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   // Running max M (log2 units), this lane's partial row sum of the unrounded
   // probabilities (for the LSE), and a pending rescale factor of the accumulators.
   float M = -INFINITY, l_part = 0.f, alpha_pend = 1.f;
+  float sv_units = 1.f;      // the V block scale the P.V accumulator is expressed in
 
   // Per-tile constants of tile u: score factor and V block scale.
   auto tile_c = [&](int u) __attribute__((always_inline)) { return cq * sk[min(u * kBN / kScaleRows, nblk - 1)]; };
@@ -240,72 +241,78 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     load_tile(Kh, min(t + 4, T - 1), kbuf(KLD));
     load_tile(Vh, min(t + 3, T - 1), vbuf(VLD));
     static_assert(kScaleRows == 2 * kBN, "a V scale block spans two tiles");
-    if constexpr (decltype(VRD)::value % 2 == 0) {   // t even: tile t opens a V scale block
-      rescale(t > 0 ? tile_sv(t - 1) * __builtin_amdgcn_rcpf(tile_sv(t)) : 1.f);
-    } else {
-      if (pend) rescale(1.f);
-    }
-    mask_tile(t + 1, S_soft);
-    const float ct = tile_c(t + 1);
-    // Main block in issue order: 4 S^T MFMAs (K fragments one MFMA ahead) and 4 P.V
-    // MFMAs (V^T fragments one MFMA ahead); the row max runs beside the first two S^T
-    // MFMAs, the exponentials beside the other six.
-    i32x8 kf[4], vf[NDB];
-    auto kread = [&](int i) __attribute__((always_inline)) { kf[i] = kfrag(kbuf(KRD), i % NKB, i / NKB); };
-    auto vread = [&](int db) __attribute__((always_inline)) {
-      int av[8];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const i32x2 x = lds_read_tr8(vbuf(VRD) + ((m / 2) * 32 + (m % 2) * 16) * ROW + vaddr[db]);
-        av[2 * m] = x[0];
-        av[2 * m + 1] = x[1];
-      }
-      vf[db] = i32x8{av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
-    };
-    float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
-    float lsum[2] = {0.f, 0.f}, bias = 0.f;
-    // six slots (S^T MFMAs 2, 3 and the four P.V MFMAs) share the 32 scores; slot k issues
-    // the arguments of slot k+1, the exponentials of slot k and the sums of slot k-1
-    constexpr int NSLOT = 6;
-    auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
-    auto exps_slot = [&](int slot) __attribute__((always_inline)) {
-      if (slot + 1 < NSLOT) args(S_soft, ct, bias, lo(slot + 1), lo(slot + 2));
-      exps(S_soft, lo(slot), lo(slot + 1));
-      if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
-    };
-    kread(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {               // i = m * NKB + kb
-      if (i + 1 < 4) kread(i + 1);
-      else vread(0);
-      const int kb = i % NKB, m = i / NKB;
-      S_new[kb] = mfma_fp8(kf[i], qreg[m], m == 0 ? f32x16{} : S_new[kb]);
-      if (i == 0) {
-        max_pairs(m4, S_soft, 4, 18);
-      } else if (i == 1) {
-        max_pairs(m4, S_soft, 18, NKB * 16);
-        pend = max_final(m4, ct);
-        bias = M - kPShift;
-        args(S_soft, ct, bias, lo(0), lo(1));
+    // Causal: once the tile's first key lies past this wave's last row, this and every
+    // later tile are fully masked for the wave; it only keeps up its loads and barriers.
+    if (!CAUSAL || t * kBN <= q0 + 31) {
+      if constexpr (decltype(VRD)::value % 2 == 0) {   // t even: tile t opens a V scale block
+        const float sv_new = tile_sv(t);
+        rescale(t > 0 ? sv_units * __builtin_amdgcn_rcpf(sv_new) : 1.f);
+        sv_units = sv_new;
       } else {
-        exps_slot(i - 2);
+        if (pend) rescale(1.f);
       }
-    }
+      mask_tile(t + 1, S_soft);
+      const float ct = tile_c(t + 1);
+      // Main block in issue order: 4 S^T MFMAs (K fragments one MFMA ahead) and 4 P.V
+      // MFMAs (V^T fragments one MFMA ahead); the row max runs beside the first two S^T
+      // MFMAs, the exponentials beside the other six.
+      i32x8 kf[4], vf[NDB];
+      auto kread = [&](int i) __attribute__((always_inline)) { kf[i] = kfrag(kbuf(KRD), i % NKB, i / NKB); };
+      auto vread = [&](int db) __attribute__((always_inline)) {
+        int av[8];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      if (db + 1 < NDB) vread(db + 1);
-      const i32x8 pb = {P_use[0], P_use[1], P_use[2], P_use[3], P_use[4], P_use[5], P_use[6], P_use[7]};
-      oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
-      if (db == NDB - 1) {
-        // all-ones A operand (E4M3 1.0), built here from a value tied to t so that it is
-        // not kept live across the loop (t < 2^30, so the shift adds 0)
-        const int one4 = 0x38383838 + (t >> 30);
-        lacc = mfma_fp8(i32x8{one4, one4, one4, one4, one4, one4, one4, one4}, pb, lacc);
+        for (int m = 0; m < 4; ++m) {
+          const i32x2 x = lds_read_tr8(vbuf(VRD) + ((m / 2) * 32 + (m % 2) * 16) * ROW + vaddr[db]);
+          av[2 * m] = x[0];
+          av[2 * m + 1] = x[1];
+        }
+        vf[db] = i32x8{av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
+      };
+      float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
+      float lsum[2] = {0.f, 0.f}, bias = 0.f;
+      // six slots (S^T MFMAs 2, 3 and the four P.V MFMAs) share the 32 scores; slot k issues
+      // the arguments of slot k+1, the exponentials of slot k and the sums of slot k-1
+      constexpr int NSLOT = 6;
+      auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
+      auto exps_slot = [&](int slot) __attribute__((always_inline)) {
+        if (slot + 1 < NSLOT) args(S_soft, ct, bias, lo(slot + 1), lo(slot + 2));
+        exps(S_soft, lo(slot), lo(slot + 1));
+        if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
+      };
+      kread(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {               // i = m * NKB + kb
+        if (i + 1 < 4) kread(i + 1);
+        else vread(0);
+        const int kb = i % NKB, m = i / NKB;
+        S_new[kb] = mfma_fp8(kf[i], qreg[m], m == 0 ? f32x16{} : S_new[kb]);
+        if (i == 0) {
+          max_pairs(m4, S_soft, 4, 18);
+        } else if (i == 1) {
+          max_pairs(m4, S_soft, 18, NKB * 16);
+          pend = max_final(m4, ct);
+          bias = M - kPShift;
+          args(S_soft, ct, bias, lo(0), lo(1));
+        } else {
+          exps_slot(i - 2);
+        }
       }
-      exps_slot(2 + db);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        if (db + 1 < NDB) vread(db + 1);
+        const i32x8 pb = {P_use[0], P_use[1], P_use[2], P_use[3], P_use[4], P_use[5], P_use[6], P_use[7]};
+        oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
+        if (db == NDB - 1) {
+          // all-ones A operand (E4M3 1.0), built here from a value tied to t so that it is
+          // not kept live across the loop (t < 2^30, so the shift adds 0)
+          const int one4 = 0x38383838 + (t >> 30);
+          lacc = mfma_fp8(i32x8{one4, one4, one4, one4, one4, one4, one4, one4}, pb, lacc);
+        }
+        exps_slot(2 + db);
+      }
+      finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
+      l_part += lsum[0] + lsum[1];
     }
-    finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
-    l_part += lsum[0] + lsum[1];
     wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
     barrier_lds();
   };
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
 
   const float l_tot = add_halves(l_part) * (1.f / (1 << (int)kPShift));   // sum of probabilities
   if (qrow >= N) return;
-  const float inv = tile_sv(T - 1) / lacc[0];    // accumulator is in units of the last tile's V scale
+  const float inv = sv_units / lacc[0];
   uint16_t* Orow = O + head_off + (int64_t)qrow * kD;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
