@@ -109,6 +109,17 @@ def test_full_size_sampled(name, causal, dtype):
     check(cpu, gpu, dtype, causal, rows=sample_rows(w.N), heads=heads)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_long_sequence_sampled(causal):
+    # One long head, N = 65536 + 33 (bf16, d = 128): 1025 key tiles with a ragged last
+    # one, 257 query tiles, rows on both sides of 2^15 and 2^16.
+    N = 65536 + 33
+    say(f"case long sequence N={N} causal={causal}")
+    cpu, gpu = make(31, 1, 1, N, 128, "bf16")
+    rows = np.unique(np.concatenate([sample_rows(N, n_random=40, seed=3), np.array([32767, 32768, 65535, 65536])]))
+    check(cpu, gpu, "bf16", causal, rows=rows, heads=[(0, 0)])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_q_zero_closed_form(causal, dtype):
