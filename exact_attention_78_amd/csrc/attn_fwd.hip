@@ -42,6 +42,15 @@ constexpr int kWaves = 8;      // waves per workgroup (32 query rows each)
 constexpr int kKD = 4;         // S^T MFMAs by which a K fragment read runs ahead
 constexpr int kVD = 2;         // P.V MFMAs by which a V fragment read runs ahead
 constexpr float kTau = 8.0f;   // lazy-rescale threshold for the running max, in log2 units
+// Two launches per call. The fast pass computes no per-tile row max: every tile uses the
+// max of the first tile, which softmax allows (the result does not depend on the
+// reference value) as long as the probabilities stay finite. A row whose probabilities
+// reach 2^64 relative to it (a partial row sum above kGuard, or not finite) marks its
+// wave's LSE with NaN; the exact pass then redoes, with a per-tile max, every query tile
+// that carries a mark and leaves the others untouched. Below 2^64, P, l and O stay far
+// inside the fp32 / bf16 / fp16 ranges.
+constexpr float kGuard = 18446744073709551616.0f;   // 2^64
+constexpr int kFixupWorkgroups = 256;               // exact pass: one workgroup per CU
 
 // LDS swizzles: 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
 // K is read 32 rows x one chunk per instruction; V is read as 8 rows x 4 chunks
@@ -56,7 +65,7 @@ template <> struct Swz<64> {
   static __device__ __forceinline__ int v(int r) { return ((r >> 1) & 1) << 2; }
 };
 
-template <typename Tag, int D, bool CAUSAL, int W>
+template <typename Tag, int D, bool CAUSAL, int W, bool FAST>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int total_wg, float c /* scale*log2 e */) {
@@ -73,280 +82,313 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   // immediate offset of ds_read (< 64 KiB) with no address add; the K reads need one add
   // per head-dim step.
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];
+  __shared__ int marked;                            // exact pass: this tile carries a mark
 
-  const int logical = xcd_logical_id(blockIdx.x, total_wg);
-  const int bh = logical / n_mtiles;
-  int mt = logical % n_mtiles;
-  if (CAUSAL) mt = n_mtiles - 1 - mt;               // longest query tiles first
+  // One query tile (batch*head, m-tile) of the grid. The fast pass runs one tile per
+  // workgroup; the exact pass is a persistent grid that walks all tiles and redoes the
+  // marked ones.
+  auto tile = [&](const int logical) __attribute__((always_inline)) {
+    const int bh = logical / n_mtiles;
+    int mt = logical % n_mtiles;
+    if (CAUSAL) mt = n_mtiles - 1 - mt;               // longest query tiles first
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int lane = tid % 64;
-  const int half = lane / 32, l32 = lane % 32;
-  const int64_t head_off = (int64_t)bh * N * D;
-  const uint16_t* Qh = Q + head_off;
-  const uint16_t* Kh = K + head_off;
-  const uint16_t* Vh = V + head_off;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64;
+    const int half = lane / 32, l32 = lane % 32;
+    const int64_t head_off = (int64_t)bh * N * D;
+    const uint16_t* Qh = Q + head_off;
+    const uint16_t* Kh = K + head_off;
+    const uint16_t* Vh = V + head_off;
 
-  const int q0 = mt * BM + wave * 32;               // this wave's 32 rows; one per lane (and lane^32)
-  const int qrow = q0 + l32;
-  u32x4 qreg[NSTEP];                                // Q^T as the B operand, resident
-#pragma unroll
-  for (int s = 0; s < NSTEP; ++s)
-    qreg[s] = qrow < N ? *(const u32x4*)(Qh + (int64_t)qrow * D + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
-
-  const int n_ktiles = (N + kBN - 1) / kBN;
-  const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * BM + kBN - 1) / kBN) : n_ktiles;
-
-  uint32_t kaddr[NSTEP];
-#pragma unroll
-  for (int s = 0; s < NSTEP; ++s) kaddr[s] = NS * TB + l32 * ROW + (((2 * s + half) ^ Swz<D>::k(l32)) << 4);
-  const int g16 = lane / 16, i16 = lane % 16;
-  const int tr_row = (g16 / 2) * 4 + i16 / 4;
-  const int tr_col = 16 * (g16 % 2) + 4 * (i16 % 4);
-  uint32_t vaddr[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int col = db * 32 + tr_col;
-    vaddr[db] = tr_row * ROW + ((((col >> 3) ^ Swz<D>::v(tr_row))) << 4) + ((col & 7) << 1);
-  }
-
-  int ld_row[LPW], ld_kch[LPW], ld_vch[LPW], ld_koff[LPW], ld_voff[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int slot = (wave * LPW + i) * 1024 + lane * 16;
-    const int r = slot / ROW, phys = (slot % ROW) / 16;
-    ld_row[i] = r;
-    ld_kch[i] = (phys ^ Swz<D>::k(r)) * 8;
-    ld_vch[i] = (phys ^ Swz<D>::v(r)) * 8;
-    ld_koff[i] = (ld_row[i] * D + ld_kch[i]) * 2;
-    ld_voff[i] = (ld_row[i] * D + ld_vch[i]) * 2;
-  }
-  // K slot SLOT is at lds + (NS + SLOT) * TB; reads add the ring base through kaddr (a
-  // register), so that only SLOT * TB + the 32-key block offset is an immediate.
-  auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* {
-    return lds + (NS + decltype(SLOT)::value) * TB;
-  };
-  auto kread_base = [&](auto SLOT) __attribute__((always_inline)) -> const uint8_t* {
-    return lds + decltype(SLOT)::value * TB;
-  };
-  auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* { return lds + decltype(SLOT)::value * TB; };
-  auto load_tile = [&](const uint16_t* src, const int (&off)[LPW], const int (&ch)[LPW], int kt, uint8_t* dst)
-                       __attribute__((always_inline)) {
-    if (kt * kBN + kBN <= N) {
-      const uint8_t* base = (const uint8_t*)(src + (int64_t)kt * kBN * D);
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) dma_load16(base + off[i], lds_u32(dst) + (wave * LPW + i) * 1024);
-    } else {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int key = min(kt * kBN + ld_row[i], N - 1);
-        dma_load16(src + (int64_t)key * D + ch[i], lds_u32(dst) + (wave * LPW + i) * 1024);
-      }
+    const int q0 = mt * BM + wave * 32;               // this wave's 32 rows; one per lane (and lane^32)
+    const int qrow = q0 + l32;
+    if constexpr (!FAST) {
+      // Exact pass: only query tiles that the fast pass marked (a NaN LSE) are redone. The
+      // first barrier also keeps the next tile's loads from overwriting LDS that a slower
+      // wave still reads for the previous one.
+      __syncthreads();
+      if (tid == 0) marked = 0;
+      __syncthreads();
+      const bool mine = half == 0 && qrow < N && __builtin_isnan(LSE[(int64_t)bh * N + qrow]);
+      if (__builtin_amdgcn_ballot_w64(mine) != 0 && lane == 0) marked = 1;
+      __syncthreads();
+      if (marked == 0) return;
     }
-  };
+    u32x4 qreg[NSTEP];                                // Q^T as the B operand, resident
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s)
+      qreg[s] = qrow < N ? *(const u32x4*)(Qh + (int64_t)qrow * D + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
 
-  auto qk = [&](auto SLOT, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
+    const int n_ktiles = (N + kBN - 1) / kBN;
+    const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * BM + kBN - 1) / kBN) : n_ktiles;
+
+    uint32_t kaddr[NSTEP];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      S[kb] = f32x16{};
+    for (int s = 0; s < NSTEP; ++s) kaddr[s] = NS * TB + l32 * ROW + (((2 * s + half) ^ Swz<D>::k(l32)) << 4);
+    const int g16 = lane / 16, i16 = lane % 16;
+    const int tr_row = (g16 / 2) * 4 + i16 / 4;
+    const int tr_col = 16 * (g16 % 2) + 4 * (i16 % 4);
+    uint32_t vaddr[NDB];
 #pragma unroll
-      for (int s = 0; s < NSTEP; ++s)
-        S[kb] = mfma32(Tag{}, *(const u32x4*)(kread_base(SLOT) + kb * 32 * ROW + kaddr[s]), qreg[s], S[kb]);
+    for (int db = 0; db < NDB; ++db) {
+      const int col = db * 32 + tr_col;
+      vaddr[db] = tr_row * ROW + ((((col >> 3) ^ Swz<D>::v(tr_row))) << 4) + ((col & 7) << 1);
     }
-  };
-  f32x16 oacc[NDB];
+
+    int ld_row[LPW], ld_kch[LPW], ld_vch[LPW], ld_koff[LPW], ld_voff[LPW];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  // Running max M (log2 units; raised only when a tile's max exceeds it by more than
-  // kTau, so that probabilities stay below 2^kTau), this lane's partial row sum of the
-  // rounded probabilities, and a pending O rescale factor.
-  float M = -INFINITY, l_part = 0.f, alpha_pend = 1.f;
-  // Scores of tile u that lie above the diagonal or past the end of the sequence -> -inf.
-  auto mask_tile = [&](int u, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
-    const int key0 = u * kBN;
-    if ((CAUSAL && key0 + kBN - 1 > q0) || key0 + kBN > N) {
+    for (int i = 0; i < LPW; ++i) {
+      const int slot = (wave * LPW + i) * 1024 + lane * 16;
+      const int r = slot / ROW, phys = (slot % ROW) / 16;
+      ld_row[i] = r;
+      ld_kch[i] = (phys ^ Swz<D>::k(r)) * 8;
+      ld_vch[i] = (phys ^ Swz<D>::v(r)) * 8;
+      ld_koff[i] = (ld_row[i] * D + ld_kch[i]) * 2;
+      ld_voff[i] = (ld_row[i] * D + ld_vch[i]) * 2;
+    }
+    // K slot SLOT is at lds + (NS + SLOT) * TB; reads add the ring base through kaddr (a
+    // register), so that only SLOT * TB + the 32-key block offset is an immediate.
+    auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* {
+      return lds + (NS + decltype(SLOT)::value) * TB;
+    };
+    auto kread_base = [&](auto SLOT) __attribute__((always_inline)) -> const uint8_t* {
+      return lds + decltype(SLOT)::value * TB;
+    };
+    auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* { return lds + decltype(SLOT)::value * TB; };
+    auto load_tile = [&](const uint16_t* src, const int (&off)[LPW], const int (&ch)[LPW], int kt, uint8_t* dst)
+                         __attribute__((always_inline)) {
+      if (kt * kBN + kBN <= N) {
+        const uint8_t* base = (const uint8_t*)(src + (int64_t)kt * kBN * D);
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int i = 0; i < LPW; ++i) dma_load16(base + off[i], lds_u32(dst) + (wave * LPW + i) * 1024);
+      } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-          if ((CAUSAL && key > qrow) || key >= N) S[kb][r] = -INFINITY;
+        for (int i = 0; i < LPW; ++i) {
+          const int key = min(kt * kBN + ld_row[i], N - 1);
+          dma_load16(src + (int64_t)key * D + ch[i], lds_u32(dst) + (wave * LPW + i) * 1024);
         }
-    }
-  };
-  // Row max of a tile's (masked) scores: max_pairs folds the score pairs in [e_begin,
-  // e_end) into four v_maximum3 chains (seeded with scores 0..3); max_final combines the
-  // chains and the partner lane l^32 and scales to log2 units.
-  auto max_pairs = [&](float (&m4)[4], const f32x16 (&S)[NKB], int e_begin, int e_end) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = e_begin; e < e_end; e += 2)
-      m4[(e / 2) % 4] = max3f(m4[(e / 2) % 4], S[e / 16][e % 16], S[e / 16][e % 16 + 1]);
-  };
-  // Raise M when some row of the wave grew by more than kTau (branch-free, so that the
-  // exponentials can share a basic block with the MFMAs); l is rescaled at once, O at
-  // the start of the next step. Returns whether M moved (wave-uniform).
-  auto max_final = [&](const float (&m4)[4]) __attribute__((always_inline)) -> bool {
-    const float mx = max_halves(max3f(m4[0], m4[1], __builtin_elementwise_maximum(m4[2], m4[3]))) * c;
-    const bool grow = __builtin_amdgcn_ballot_w64(mx > M + kTau) != 0;
-    const float M_new = grow ? __builtin_elementwise_maximum(M, mx) : M;
-    const float alpha = grow ? fast_exp2(M - M_new) : 1.f;
-    M = M_new;
-    l_part *= alpha;
-    alpha_pend *= alpha;
-    return grow;
-  };
-  // Probabilities of scores e in [e0, e1): P = 2^(S*c - M) in fp32, written over the
-  // scores (exps); later, so that the exponentials' latency is covered, their row sum
-  // (two chains, before rounding) and the rounding to 16 bits, packed in pairs into the
-  // B operand of P.V (finish).
-  auto args = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {   // S*c - M
-#pragma unroll
-    for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = __builtin_fmaf(S[e / 16][e % 16], c, -M);
-  };
-  auto exps = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {     // 2^(S*c - M)
-#pragma unroll
-    for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = fast_exp2(S[e / 16][e % 16]);
-  };
-  auto finish = [&](const f32x16 (&S)[NKB], u32x4 (&P)[NKB][2], float (&lsum)[2], int e0, int e1)
-                    __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = e0; e < e1; ++e) {
-      lsum[e % 2] += S[e / 16][e % 16];
-      if (e % 2 == 1) P[e / 16][(e % 16) / 8][(e % 8) / 2] = pack2(Tag{}, S[e / 16][e % 16 - 1], S[e / 16][e % 16]);
-    }
-  };
-  auto rescale_o = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha_pend;
-    alpha_pend = 1.f;
-  };
+      }
+    };
 
-  f32x16 Sa[NKB], Sb[NKB];
-  u32x4 Pa[NKB][2], Pb[NKB][2];
-  bool pend = false;     // wave-uniform: an O rescale is owed
+    auto qk = [&](auto SLOT, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        S[kb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s)
+          S[kb] = mfma32(Tag{}, *(const u32x4*)(kread_base(SLOT) + kb * 32 * ROW + kaddr[s]), qreg[s], S[kb]);
+      }
+    };
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    // Running max M (log2 units; raised only when a tile's max exceeds it by more than
+    // kTau, so that probabilities stay below 2^kTau), this lane's partial row sum of the
+    // rounded probabilities, and a pending O rescale factor.
+    float M = -INFINITY, l_part = 0.f, alpha_pend = 1.f;
+    // Scores of tile u that lie above the diagonal or past the end of the sequence -> -inf.
+    auto mask_tile = [&](int u, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
+      const int key0 = u * kBN;
+      if ((CAUSAL && key0 + kBN - 1 > q0) || key0 + kBN > N) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+            if ((CAUSAL && key > qrow) || key >= N) S[kb][r] = -INFINITY;
+          }
+      }
+    };
+    // Row max of a tile's (masked) scores: max_pairs folds the score pairs in [e_begin,
+    // e_end) into four v_maximum3 chains (seeded with scores 0..3); max_final combines the
+    // chains and the partner lane l^32 and scales to log2 units.
+    auto max_pairs = [&](float (&m4)[4], const f32x16 (&S)[NKB], int e_begin, int e_end) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = e_begin; e < e_end; e += 2)
+        m4[(e / 2) % 4] = max3f(m4[(e / 2) % 4], S[e / 16][e % 16], S[e / 16][e % 16 + 1]);
+    };
+    // Raise M when some row of the wave grew by more than kTau (branch-free, so that the
+    // exponentials can share a basic block with the MFMAs); l is rescaled at once, O at
+    // the start of the next step. Returns whether M moved (wave-uniform).
+    auto max_final = [&](const float (&m4)[4]) __attribute__((always_inline)) -> bool {
+      const float mx = max_halves(max3f(m4[0], m4[1], __builtin_elementwise_maximum(m4[2], m4[3]))) * c;
+      const bool grow = __builtin_amdgcn_ballot_w64(mx > M + kTau) != 0;
+      const float M_new = grow ? __builtin_elementwise_maximum(M, mx) : M;
+      const float alpha = grow ? fast_exp2(M - M_new) : 1.f;
+      M = M_new;
+      l_part *= alpha;
+      alpha_pend *= alpha;
+      return grow;
+    };
+    // Probabilities of scores e in [e0, e1): P = 2^(S*c - M) in fp32, written over the
+    // scores (exps); later, so that the exponentials' latency is covered, their row sum
+    // (two chains, before rounding) and the rounding to 16 bits, packed in pairs into the
+    // B operand of P.V (finish).
+    auto args = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {   // S*c - M
+#pragma unroll
+      for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = __builtin_fmaf(S[e / 16][e % 16], c, -M);
+    };
+    auto exps = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {     // 2^(S*c - M)
+#pragma unroll
+      for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = fast_exp2(S[e / 16][e % 16]);
+    };
+    auto finish = [&](const f32x16 (&S)[NKB], u32x4 (&P)[NKB][2], float (&lsum)[2], int e0, int e1)
+                      __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        lsum[e % 2] += S[e / 16][e % 16];
+        if (e % 2 == 1) P[e / 16][(e % 16) / 8][(e % 8) / 2] = pack2(Tag{}, S[e / 16][e % 16 - 1], S[e / 16][e % 16]);
+      }
+    };
+    auto rescale_o = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha_pend;
+      alpha_pend = 1.f;
+    };
 
-  // Step t (j = t mod 4 fixes every register set and ring slot at compile time):
-  //   S(t+1) in S_soft, S(t+2) -> S_new, P(t) in P_use, P(t+1) -> P_new,
-  //   K(t+2) in K slot (t+2)%4, V(t) in V slot t%4; loads: K(t+4) -> K slot t%4,
-  //   V(t+3) -> V slot (t+3)%4. Past the last tile the loads are clamped (never read),
-  //   and the scores of tile T (if computed) are fully masked, so P(T) = 0 adds nothing.
-  auto step = [&](int t, f32x16 (&S_soft)[NKB], f32x16 (&S_new)[NKB], const u32x4 (&P_use)[NKB][2],
-                  u32x4 (&P_new)[NKB][2], auto KRD, auto VRD, auto KLD, auto VLD) __attribute__((always_inline)) {
-    load_tile(Kh, ld_koff, ld_kch, min(t + 4, T - 1), kbuf(KLD));
-    load_tile(Vh, ld_voff, ld_vch, min(t + 3, T - 1), vbuf(VLD));
-    // Causal: once the tile's first key lies past this wave's last row, this and every
-    // later tile are fully masked for the wave; it only keeps up its loads and barriers.
-    if (!CAUSAL || t * kBN <= q0 + 31) {
-      if (pend) rescale_o();
-      mask_tile(t + 1, S_soft);
-      // Main block, written in issue order (this file is compiled without the machine
-      // scheduler): 16 S^T MFMAs (K fragments read KD ahead) then 16 P.V MFMAs (V^T
-      // fragments read VD ahead); the softmax VALU work of tile t+1 is spread between them:
-      // the row max over the first five S^T MFMAs, then the exponentials, one or two per MFMA.
-      constexpr int NQ = NKB * NSTEP, NP = NDB * NKB * 2, KD = kKD, VD = kVD;
-      constexpr int NSLOT = NQ + NP - 5;                 // MFMAs that carry exponentials
-      u32x4 kf[NQ], vf[NP];
-      auto kread = [&](int i) __attribute__((always_inline)) {   // i = s * NKB + kb
-        kf[i] = *(const u32x4*)(kread_base(KRD) + (i % NKB) * 32 * ROW + kaddr[i / NKB]);
-      };
-      auto vread = [&](int i) __attribute__((always_inline)) {   // i = (kb * 2 + h) * NDB + db
-        const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
-        const uint8_t* base = vbuf(VRD) + (kb * 32 + h * 16) * ROW + vaddr[db];
-        const u32x2 v1 = lds_read_tr16((const uint16_t*)base);
-        const u32x2 v2 = lds_read_tr16((const uint16_t*)(base + 8 * ROW));
-        vf[i] = u32x4{v1[0], v1[1], v2[0], v2[1]};
-      };
-      float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
+    f32x16 Sa[NKB], Sb[NKB];
+    u32x4 Pa[NKB][2], Pb[NKB][2];
+    bool pend = false;     // wave-uniform: an O rescale is owed
+    bool ovf = false;      // fast pass: a probability of this lane reached the guard
+
+    // Step t (j = t mod 4 fixes every register set and ring slot at compile time):
+    //   S(t+1) in S_soft, S(t+2) -> S_new, P(t) in P_use, P(t+1) -> P_new,
+    //   K(t+2) in K slot (t+2)%4, V(t) in V slot t%4; loads: K(t+4) -> K slot t%4,
+    //   V(t+3) -> V slot (t+3)%4. Past the last tile the loads are clamped (never read),
+    //   and the scores of tile T (if computed) are fully masked, so P(T) = 0 adds nothing.
+    auto step = [&](int t, f32x16 (&S_soft)[NKB], f32x16 (&S_new)[NKB], const u32x4 (&P_use)[NKB][2],
+                    u32x4 (&P_new)[NKB][2], auto KRD, auto VRD, auto KLD, auto VLD) __attribute__((always_inline)) {
+      load_tile(Kh, ld_koff, ld_kch, min(t + 4, T - 1), kbuf(KLD));
+      load_tile(Vh, ld_voff, ld_vch, min(t + 3, T - 1), vbuf(VLD));
+      // Causal: once the tile's first key lies past this wave's last row, this and every
+      // later tile are fully masked for the wave; it only keeps up its loads and barriers.
+      if (!CAUSAL || t * kBN <= q0 + 31) {
+        if constexpr (!FAST) {
+          if (pend) rescale_o();
+        }
+        mask_tile(t + 1, S_soft);
+        // Main block, written in issue order (this file is compiled without the machine
+        // scheduler): 16 S^T MFMAs (K fragments read KD ahead) then 16 P.V MFMAs (V^T
+        // fragments read VD ahead); the softmax VALU work of tile t+1 is spread between them:
+        // (exact pass) the row max over the first five S^T MFMAs, then the exponentials,
+        // one or two per MFMA; (fast pass) the exponentials from the second MFMA on.
+        constexpr int NQ = NKB * NSTEP, NP = NDB * NKB * 2, KD = kKD, VD = kVD;
+        constexpr int NMAX = FAST ? 1 : 5;                 // MFMAs before the first exponential
+        constexpr int NSLOT = NQ + NP - NMAX;              // MFMAs that carry exponentials
+        u32x4 kf[NQ], vf[NP];
+        auto kread = [&](int i) __attribute__((always_inline)) {   // i = s * NKB + kb
+          kf[i] = *(const u32x4*)(kread_base(KRD) + (i % NKB) * 32 * ROW + kaddr[i / NKB]);
+        };
+        auto vread = [&](int i) __attribute__((always_inline)) {   // i = (kb * 2 + h) * NDB + db
+          const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
+          const uint8_t* base = vbuf(VRD) + (kb * 32 + h * 16) * ROW + vaddr[db];
+          const u32x2 v1 = lds_read_tr16((const uint16_t*)base);
+          const u32x2 v2 = lds_read_tr16((const uint16_t*)(base + 8 * ROW));
+          vf[i] = u32x4{v1[0], v1[1], v2[0], v2[1]};
+        };
+        float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
+        float lsum[2] = {0.f, 0.f};
+        // slot k: arguments of slot k+1, exponentials of slot k, sums and packing of slot k-1
+        auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
+        auto exps_slot = [&](int slot) __attribute__((always_inline)) {
+          if (slot + 1 < NSLOT) args(S_soft, lo(slot + 1), lo(slot + 2));
+          exps(S_soft, lo(slot), lo(slot + 1));
+          if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
+        };
+#pragma unroll
+        for (int i = 0; i < KD; ++i) kread(i);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+          if (i + KD < NQ) kread(i + KD);
+          if (i + KD >= NQ && i + KD - NQ < VD) vread(i + KD - NQ);
+          const int kb = i % NKB, s = i / NKB;
+          S_new[kb] = mfma32(Tag{}, kf[i], qreg[s], s == 0 ? f32x16{} : S_new[kb]);
+          if (i < NMAX - 1) {
+            max_pairs(m4, S_soft, 4 + i * 8, min(4 + (i + 1) * 8, NKB * 16));
+          } else if (i == NMAX - 1) {
+            if constexpr (!FAST) pend = max_final(m4);
+            args(S_soft, lo(0), lo(1));
+          } else {
+            exps_slot(i - NMAX);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          if (i + VD < NP) vread(i + VD);
+          const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
+          oacc[db] = mfma32(Tag{}, vf[i], P_use[kb][h], oacc[db]);
+          exps_slot(NQ - NMAX + i);
+        }
+        finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
+        const float lt = lsum[0] + lsum[1];
+        l_part += lt;
+        if constexpr (FAST) ovf |= !(lt <= kGuard);
+      }
+      wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
+      barrier_lds();
+    };
+
+    // Prologue: K tiles 0..3 and V tiles 0..2; S(0), softmax of tile 0, S(1).
+    load_tile(Kh, ld_koff, ld_kch, 0, kbuf(IC<0>{}));
+    load_tile(Kh, ld_koff, ld_kch, min(1, T - 1), kbuf(IC<1>{}));
+    load_tile(Kh, ld_koff, ld_kch, min(2, T - 1), kbuf(IC<2>{}));
+    load_tile(Kh, ld_koff, ld_kch, min(3, T - 1), kbuf(IC<3>{}));
+    load_tile(Vh, ld_voff, ld_vch, 0, vbuf(IC<0>{}));
+    load_tile(Vh, ld_voff, ld_vch, min(1, T - 1), vbuf(IC<1>{}));
+    load_tile(Vh, ld_voff, ld_vch, min(2, T - 1), vbuf(IC<2>{}));
+    wait_vmcnt<0>();
+    barrier_lds();
+    qk(IC<0>{}, Sa);
+    {
+      mask_tile(0, Sa);
+      float m4[4] = {Sa[0][0], Sa[0][1], Sa[0][2], Sa[0][3]};
+      max_pairs(m4, Sa, 4, NKB * 16);
+      max_final(m4);
+      alpha_pend = 1.f;            // O is still zero: no rescale owed
       float lsum[2] = {0.f, 0.f};
-      // slot k: arguments of slot k+1, exponentials of slot k, sums and packing of slot k-1
-      auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
-      auto exps_slot = [&](int slot) __attribute__((always_inline)) {
-        if (slot + 1 < NSLOT) args(S_soft, lo(slot + 1), lo(slot + 2));
-        exps(S_soft, lo(slot), lo(slot + 1));
-        if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
-      };
-#pragma unroll
-      for (int i = 0; i < KD; ++i) kread(i);
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) {
-        if (i + KD < NQ) kread(i + KD);
-        if (i + KD >= NQ && i + KD - NQ < VD) vread(i + KD - NQ);
-        const int kb = i % NKB, s = i / NKB;
-        S_new[kb] = mfma32(Tag{}, kf[i], qreg[s], s == 0 ? f32x16{} : S_new[kb]);
-        if (i < 4)
-          max_pairs(m4, S_soft, 4 + i * 8, min(4 + (i + 1) * 8, NKB * 16));
-        else if (i == 4) {
-          pend = max_final(m4);
-          args(S_soft, lo(0), lo(1));
-        }
-        else
-          exps_slot(i - 5);
-      }
-#pragma unroll
-      for (int i = 0; i < NP; ++i) {
-        if (i + VD < NP) vread(i + VD);
-        const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
-        oacc[db] = mfma32(Tag{}, vf[i], P_use[kb][h], oacc[db]);
-        exps_slot(NQ - 5 + i);
-      }
-      finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
+      args(Sa, 0, NKB * 16);
+      exps(Sa, 0, NKB * 16);
+      finish(Sa, Pa, lsum, 0, NKB * 16);
       l_part += lsum[0] + lsum[1];
     }
-    wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
-    barrier_lds();
-  };
+    qk(IC<1>{}, Sb);
+    barrier_lds();                 // K slots 0 and 1 are refilled from step 0 on
 
-  // Prologue: K tiles 0..3 and V tiles 0..2; S(0), softmax of tile 0, S(1).
-  load_tile(Kh, ld_koff, ld_kch, 0, kbuf(IC<0>{}));
-  load_tile(Kh, ld_koff, ld_kch, min(1, T - 1), kbuf(IC<1>{}));
-  load_tile(Kh, ld_koff, ld_kch, min(2, T - 1), kbuf(IC<2>{}));
-  load_tile(Kh, ld_koff, ld_kch, min(3, T - 1), kbuf(IC<3>{}));
-  load_tile(Vh, ld_voff, ld_vch, 0, vbuf(IC<0>{}));
-  load_tile(Vh, ld_voff, ld_vch, min(1, T - 1), vbuf(IC<1>{}));
-  load_tile(Vh, ld_voff, ld_vch, min(2, T - 1), vbuf(IC<2>{}));
-  wait_vmcnt<0>();
-  barrier_lds();
-  qk(IC<0>{}, Sa);
-  {
-    mask_tile(0, Sa);
-    float m4[4] = {Sa[0][0], Sa[0][1], Sa[0][2], Sa[0][3]};
-    max_pairs(m4, Sa, 4, NKB * 16);
-    max_final(m4);
-    alpha_pend = 1.f;            // O is still zero: no rescale owed
-    float lsum[2] = {0.f, 0.f};
-    args(Sa, 0, NKB * 16);
-    exps(Sa, 0, NKB * 16);
-    finish(Sa, Pa, lsum, 0, NKB * 16);
-    l_part += lsum[0] + lsum[1];
-  }
-  qk(IC<1>{}, Sb);
-  barrier_lds();                 // K slots 0 and 1 are refilled from step 0 on
-
-  for (int t = 0; t < T; t += 4) {
-    step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{});
-    if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{});
-    if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{});
-    if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{});
-  }
-  wait_vmcnt<0>();               // no load may still target this workgroup's LDS when it exits
-  if (pend) rescale_o();
-
-  const float l_tot = add_halves(l_part);
-  if (qrow >= N) return;
-  const float inv = 1.0f / l_tot;
-  uint16_t* Orow = O + head_off + (int64_t)qrow * D;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = db * 32 + g * 8 + half * 4;
-      const f32x16 a = oacc[db];
-      u32x2 w = {pack2(Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv),
-                 pack2(Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
-      *(u32x2*)(Orow + d) = w;
+    for (int t = 0; t < T; t += 4) {
+      step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{});
+      if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{});
+      if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{});
+      if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{});
     }
-  if (half == 0) LSE[(int64_t)bh * N + qrow] = (M + __builtin_log2f(l_tot)) * kLn2;
+    wait_vmcnt<0>();               // no load may still target this workgroup's LDS when it exits
+    if (pend) rescale_o();
+
+    const float l_tot = add_halves(l_part);
+    if (qrow >= N) return;
+    const float inv = 1.0f / l_tot;
+    uint16_t* Orow = O + head_off + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + g * 8 + half * 4;
+        const f32x16 a = oacc[db];
+        u32x2 w = {pack2(Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv),
+                   pack2(Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
+        *(u32x2*)(Orow + d) = w;
+      }
+    float lse = (M + __builtin_log2f(l_tot)) * kLn2;
+    if constexpr (FAST) {
+      if (__builtin_amdgcn_ballot_w64(ovf) != 0) lse = __builtin_nanf("");   // mark: redo in the exact pass
+    }
+    if (half == 0) LSE[(int64_t)bh * N + qrow] = lse;
+  };
+  if constexpr (FAST) {
+    tile(xcd_logical_id(blockIdx.x, total_wg));
+  } else {
+    for (int lg = blockIdx.x; lg < total_wg; lg += gridDim.x) tile(lg);
+  }
 }
 
 template <typename Tag, int D, bool CAUSAL>
@@ -355,9 +397,13 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
   constexpr int BM = kWaves * 32;
   const int n_mtiles = (int)((N + BM - 1) / BM);
   const int64_t total = BH * n_mtiles;
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, kWaves>), dim3((unsigned)total), dim3(kWaves * 64), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N, n_mtiles,
-                     (int)total, scale * kLog2e);
+  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, kWaves, true>), dim3((unsigned)total), dim3(kWaves * 64), 0,
+                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
+                     n_mtiles, (int)total, scale * kLog2e);
+  const int64_t fixup_wg = total < kFixupWorkgroups ? total : kFixupWorkgroups;
+  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, kWaves, false>), dim3((unsigned)fixup_wg), dim3(kWaves * 64), 0,
+                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
+                     n_mtiles, (int)total, scale * kLog2e);
   return hipGetLastError();
 }
 

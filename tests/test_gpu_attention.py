@@ -167,6 +167,21 @@ def test_large_key_shift_is_stable(causal):
     assert lse_err(L, Lref) <= LSE_REL
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_jumping_past_the_first_tile_max(causal, dtype):
+    # Keys from 300 on are 30x larger: their scores exceed the first tile's row max by far
+    # more than 64 (log2 units), so the fast pass marks those rows and the exact pass
+    # (per-tile max) must redo their query tiles; the result is checked like any other.
+    B, H, N, d = 1, 2, 700, 128
+    say(f"case jumping scores causal={causal} dtype={dtype}")
+    q, k, v = inputs.draw_qkv(12, B, H, N, d)
+    k = k.copy()
+    k[:, :, 300:] *= np.float32(30.0)
+    tq, tk, tv = (inputs.to_torch(x, dtype) for x in (q, k, v))
+    check((tq, tk, tv), tuple(t.cuda() for t in (tq, tk, tv)), dtype, causal)
+
+
 def test_outputs_fully_written_and_deterministic():
     cpu, gpu = make(10, 2, 2, 700, 128, "bf16")
     o1 = torch.full_like(gpu[0], float("nan"))
