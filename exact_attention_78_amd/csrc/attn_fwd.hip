@@ -44,12 +44,15 @@ constexpr int kVD = 2;         // P.V MFMAs by which a V fragment read runs ahea
 constexpr float kTau = 8.0f;   // lazy-rescale threshold for the running max, in log2 units
 // Two launches per call. The fast pass computes no per-tile row max: every tile uses the
 // max of the first tile, which softmax allows (the result does not depend on the
-// reference value) as long as the probabilities stay finite. A row whose probabilities
-// reach 2^64 relative to it (a partial row sum above kGuard, or not finite) marks its
-// wave's LSE with NaN; the exact pass then redoes, with a per-tile max, every query tile
-// that carries a mark and leaves the others untouched. Below 2^64, P, l and O stay far
-// inside the fp32 / bf16 / fp16 ranges.
-constexpr float kGuard = 18446744073709551616.0f;   // 2^64
+// reference value) as long as the probabilities stay representable. A row whose
+// probabilities relative to it reach the guard (a partial row sum above it, or not
+// finite) marks its wave's LSE with NaN; the exact pass then redoes, with a per-tile max,
+// every query tile that carries a mark and leaves the others untouched. The guard keeps
+// P within its 16-bit type (bf16: 2^64, far inside its range; fp16: 2^15 < 65504) and l
+// and O far inside fp32.
+template <typename Tag> struct Guard;
+template <> struct Guard<Bf16Tag> { static constexpr float value = 18446744073709551616.0f; };   // 2^64
+template <> struct Guard<F16Tag> { static constexpr float value = 32768.0f; };                  // 2^15
 constexpr int kFixupWorkgroups = 256;               // exact pass: one workgroup per CU
 
 // LDS swizzles: 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
         finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
         const float lt = lsum[0] + lsum[1];
         l_part += lt;
-        if constexpr (FAST) ovf |= !(lt <= kGuard);
+        if constexpr (FAST) ovf |= !(lt <= Guard<Tag>::value);
       }
       wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
       barrier_lds();

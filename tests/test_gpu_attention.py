@@ -169,15 +169,17 @@ def test_large_key_shift_is_stable(causal):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_scores_jumping_past_the_first_tile_max(causal, dtype):
-    # Keys from 300 on are 30x larger: their scores exceed the first tile's row max by far
-    # more than 64 (log2 units), so the fast pass marks those rows and the exact pass
-    # (per-tile max) must redo their query tiles; the result is checked like any other.
+@pytest.mark.parametrize("factor", [8.0, 30.0])
+def test_scores_jumping_past_the_first_tile_max(factor, causal, dtype):
+    # Keys from 300 on are scaled up: their scores exceed the first tile's row max by about
+    # 25 (x8) or far more than 64 (x30) in log2 units. Probabilities against the first
+    # tile's max would then overflow fp16 (x8) or any 16-bit type (x30); the fast pass
+    # must mark those rows and the exact pass (per-tile max) redo their query tiles.
     B, H, N, d = 1, 2, 700, 128
-    say(f"case jumping scores causal={causal} dtype={dtype}")
+    say(f"case jumping scores x{factor} causal={causal} dtype={dtype}")
     q, k, v = inputs.draw_qkv(12, B, H, N, d)
     k = k.copy()
-    k[:, :, 300:] *= np.float32(30.0)
+    k[:, :, 300:] *= np.float32(factor)
     tq, tk, tv = (inputs.to_torch(x, dtype) for x in (q, k, v))
     check((tq, tk, tv), tuple(t.cuda() for t in (tq, tk, tv)), dtype, causal)
 
