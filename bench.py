@@ -59,7 +59,7 @@ def read_counters():
     if kv.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["hbm_bytes_per_launch"].split()[0])
     except (KeyError, ValueError):
         return None
 
