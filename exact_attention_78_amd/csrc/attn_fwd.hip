@@ -29,6 +29,9 @@
 //   step's MFMAs, LDS reads and VALU work are written in the order they are issued.
 //   K and V tiles sit in two 4-slot LDS rings (128 KiB at d = 128), filled by direct
 //   global->LDS loads (global_load_lds_dwordx4) two or three steps ahead of their use.
+//   Each call is two launches of this kernel: a fast pass that keeps the first tile's
+//   row max as the softmax reference for every tile, and an exact pass that redoes, with
+//   a per-tile running max, the query tiles whose probabilities outgrew that reference.
 #include <type_traits>
 
 #include "device_common.h"
