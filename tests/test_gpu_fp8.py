@@ -152,3 +152,24 @@ def test_rotation_lowers_fp8_error_with_outliers():
         errs[rot] = np.sqrt(np.mean((O - Oexact) ** 2))
     say(f"  RMSE with rotation {errs[True]:.4e}, without {errs[False]:.4e}, ratio {errs[False] / errs[True]:.2f}")
     assert errs[True] < errs[False]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("factor", [1.5, 4.0, 30.0])
+def test_fp8_scores_jumping_past_the_first_tile_max(factor, causal):
+    # K activations from key 300 on are scaled up before quantisation, so their scores rise
+    # far above the first key tile's row max (x4, x30), or a little above it for some rows
+    # (x1.5). Probabilities taken against the first tile's max then leave the E4M3 range:
+    # the fast pass must mark those rows and the exact pass (per-tile max) redo them.
+    B, H, N, d = 1, 2, 700, 128
+    say(f"case fp8 jumping scores x{factor} causal={causal}")
+    q, k, v, signs = inputs.draw_fp8_workload(52, B, H, N, d)
+    k = k.copy()
+    k[:, :, 300:] *= np.float32(factor)
+    xs = [bf16_activations(t)[1] for t in (q, k, v)]
+    p = ofp8.prepare_fp8(*xs, signs)
+    deq = [ofp8.dequantize_blocks(p[c], p[s]) for c, s in (("q8", "sq"), ("k8", "sk"), ("v8", "sv"))]
+    scale = inputs.softmax_scale(d)
+    O, L = run_fp8(p, causal, scale)
+    Oref, Lref = attention_forward(*deq, causal, scale)
+    compare(O, L, Oref, Lref, f"fp8 jump x{factor} causal={causal}")
