@@ -4,7 +4,8 @@ This module only draws inputs; it holds none of the attention or quantisation
 arithmetic, and both the device library's tests/bench and the CPU oracle consume what
 it returns. Every draw comes from numpy's PCG64 generator seeded by
 ``SeedSequence([78, workload_id, tensor_id])`` with tensor ids 0, 1, 2 for Q, K, V,
-3 for the Hadamard sign vector and 4 for the outlier channels.
+3 for the Hadamard sign vector, 4 for the outlier channels and 6 for the output
+gradient dO of the backward pass.
 
 The named workloads mirror the shapes the pages benchmark (heads = 16, head dims 64
 and 128, sequence lengths 1k-16k, causal and non-causal; "Triton 07: Flash Attention
@@ -20,7 +21,7 @@ from dataclasses import dataclass
 import numpy as np
 
 SEED_ROOT = 78
-Q_ID, K_ID, V_ID, SIGN_ID, OUTLIER_ID = 0, 1, 2, 3, 4
+Q_ID, K_ID, V_ID, SIGN_ID, OUTLIER_ID, DO_ID = 0, 1, 2, 3, 4, 6
 
 
 @dataclass(frozen=True)
@@ -68,6 +69,11 @@ def draw_qkv(wid: int, B: int, H: int, N: int, d: int):
     """Q, K, V ~ N(0, 1) as fp32 arrays [B, H, N, d]."""
     shape = (B, H, N, d)
     return normal_f32(wid, Q_ID, shape), normal_f32(wid, K_ID, shape), normal_f32(wid, V_ID, shape)
+
+
+def draw_dout(wid: int, B: int, H: int, N: int, d: int):
+    """The output gradient dO ~ N(0, 1) as an fp32 array [B, H, N, d]."""
+    return normal_f32(wid, DO_ID, (B, H, N, d))
 
 
 def outlier_channels(wid: int, d: int, frac: float = 0.01) -> np.ndarray:

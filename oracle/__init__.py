@@ -1,4 +1,4 @@
-"""CPU oracle for the exact attention forward pass and its fp8 input preparation.
+"""CPU oracle for exact attention (forward and backward) and its fp8 input preparation.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link this
 package: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -19,7 +19,8 @@ where it takes that decision in fp32, the precision the device kernel works in.
 
 Modules
 -------
-attention : plain definition of softmax(scale * Q K^T [+ causal mask]) V and its LSE.
+attention : plain definition of softmax(scale * Q K^T [+ causal mask]) V and its LSE,
+            and its gradients dQ, dK, dV by the chain rule.
 fp8       : OCP E4M3 codec, Sylvester Hadamard / fast Walsh-Hadamard transform,
             per-128-row block quantiser, and the fp8 input preparation.
 

@@ -1,4 +1,4 @@
-"""Plain fp64 definition of the exact attention forward pass (oracle; test infrastructure only).
+"""Plain fp64 definition of exact attention, forward and backward (oracle; test infrastructure only).
 
 What is computed (FlashAttention-2 digest, "Method — framework overview" flowchart and
 glossary): for each batch b and head h independently,
@@ -80,8 +80,69 @@ def attention_forward(q, k, v, causal: bool, scale: float, rows=None, heads=None
     return O, LSE
 
 
+def attention_backward(q, k, v, dout, causal: bool, scale: float, heads=None, row_chunk: int = 512):
+    """Gradients of the exact attention forward in fp64 (oracle; test infrastructure only).
+
+    The FlashAttention-2 digest (key technical points and method summary) has the
+    backward pass recompute the attention from the stored log-sum-exp and produce dQ, dK
+    and dV with the same query-split partition; it prints no formulas. What such a pass
+    must reach is the gradient of O = softmax(scale * Q K^T [+ causal mask]) V, which
+    the chain rule fixes. Per (b, h), with P the softmax rows of the forward pass:
+
+        dV   = P^T dO
+        dP   = dO V^T
+        dS_ij = P_ij * (dP_ij - sum_k P_ik dP_ik)     (Jacobian of a softmax row)
+        dQ   = scale * dS K
+        dK   = scale * dS^T Q
+
+    The oracle materialises P from its definition (max-subtracted exponentials divided
+    by their row sum), never from a stored LSE, so a wrong LSE on the device side cannot
+    hide. Query rows are processed in chunks of complete rows (``row_chunk``) to bound
+    memory; dK and dV sum the chunks' contributions.
+
+    Returns dQ, dK, dV as fp64 arrays [B, H, N, d]; heads not requested are NaN.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    dout = _as_f64(dout)
+    if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, k, v, dout must share one [B, H, N, d] shape")
+    B, H, N, d = q.shape
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    scale = float(scale)
+
+    dQ = np.full(q.shape, np.nan)
+    dK = np.full(q.shape, np.nan)
+    dV = np.full(q.shape, np.nan)
+    key_index = np.arange(N)
+    for b, h in heads:
+        dK[b, h] = 0.0
+        dV[b, h] = 0.0
+        for c0 in range(0, N, row_chunk):
+            r = np.arange(c0, min(N, c0 + row_chunk))
+            S = scale * (q[b, h, r, :] @ k[b, h].T)          # [len(r), N]
+            if causal:
+                S[key_index[None, :] > r[:, None]] = -np.inf
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            P = E / E.sum(axis=1, keepdims=True)
+            g = dout[b, h, r, :]
+            dV[b, h] += P.T @ g
+            dP = g @ v[b, h].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dQ[b, h, r] = scale * (dS @ k[b, h])
+            dK[b, h] += scale * (dS.T @ q[b, h, r, :])
+    return dQ, dK, dV
+
+
 def counted_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
     """Forward FLOP count by the convention the pages' throughput figures use:
     4*B*H*N^2*d (two N x N x d contractions), halved when causal."""
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
+
+
+def counted_flops_backward(B: int, H: int, N: int, d: int, causal: bool) -> float:
+    """Backward FLOP count: the five N x N x d contractions of the gradient (S again,
+    dV, dP, dQ, dK), 2.5 times the forward count, halved when causal."""
+    return 2.5 * counted_flops(B, H, N, d, causal)
