@@ -1,4 +1,4 @@
-"""Exact attention forward for AMD Instinct MI355X (gfx950).
+"""Exact attention (forward, backward, fp8 path) for AMD Instinct MI355X (gfx950).
 
 The computation runs in hand-written HIP kernels behind a C ABI (``include/attn.h``,
 built as ``libattn.so``); this package is the thin Python binding over it plus the
@@ -9,11 +9,14 @@ from ._binding import (  # noqa: F401
     AttnError,
     LIB_PATH,
     SIGNATURES,
+    attn_bwd_bf16,
+    attn_bwd_f16,
     attn_fwd_bf16,
     attn_fwd_f16,
     attn_fwd_f32,
     attn_fwd_fp8,
     attn_quant_fp8,
+    bwd,
     fwd,
     library,
 )

@@ -29,6 +29,8 @@ SIGNATURES = {
     "attn_fwd_f32": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_fwd_fp8": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_quant_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
+    "attn_bwd_bf16": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
+    "attn_bwd_f16": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_status_string": [_INT],
     "attn_abi_version": [],
 }
@@ -116,6 +118,49 @@ def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
     fn = {torch.bfloat16: attn_fwd_bf16, torch.float16: attn_fwd_f16, torch.float32: attn_fwd_f32}.get(q.dtype)
     _require(fn is not None, f"unsupported dtype {q.dtype}")
     return fn(q, k, v, causal, scale, out, lse)
+
+
+def _bwd(fn: str, dtype, q, k, v, o, lse, dout, causal: bool, scale, dq=None, dk=None, dv=None, workspace=None):
+    _qkv_checks(q, k, v, dtype)
+    B, H, N, d = q.shape
+    for name, t in (("o", o), ("dout", dout)):
+        _require(isinstance(t, torch.Tensor) and t.dtype == dtype and t.shape == q.shape and t.is_contiguous()
+                 and t.device == q.device, f"{name} must be a contiguous {dtype} [B, H, N, d] tensor on q's device")
+    _require(isinstance(lse, torch.Tensor) and lse.dtype == torch.float32 and lse.shape == (B, H, N)
+             and lse.is_contiguous() and lse.device == q.device, "lse must be fp32 [B, H, N] on q's device")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    grads = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        t = torch.empty_like(q) if t is None else t
+        _require(t.shape == q.shape and t.dtype == dtype and t.is_contiguous() and t.device == q.device, f"bad {name}")
+        grads.append(t)
+    ws = torch.empty((2, B, H, N), dtype=torch.float32, device=q.device) if workspace is None else workspace
+    _require(ws.dtype == torch.float32 and ws.numel() >= 2 * B * H * N and ws.is_contiguous()
+             and ws.device == q.device, "workspace must be a contiguous fp32 tensor of 2*B*H*N elements")
+    with torch.cuda.device(q.device):
+        st = getattr(library(), fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                                    ws.data_ptr(), B, H, N, d, int(bool(causal)), float(scale), _stream(q))
+    _check(fn, st)
+    return tuple(grads)
+
+
+def attn_bwd_bf16(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass of attn_fwd_bf16 (o, lse from that call); returns (dq, dk, dv), bf16."""
+    return _bwd("attn_bwd_bf16", torch.bfloat16, q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace)
+
+
+def attn_bwd_f16(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass of attn_fwd_f16; returns (dq, dk, dv), fp16."""
+    return _bwd("attn_bwd_f16", torch.float16, q, k, v, o, lse, dout, causal, scale, dq, dk, dv, workspace)
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None):
+    """Dispatch on q.dtype to attn_bwd_{bf16,f16}."""
+    fn = {torch.bfloat16: attn_bwd_bf16, torch.float16: attn_bwd_f16}.get(q.dtype)
+    _require(fn is not None, f"unsupported dtype {q.dtype}")
+    return fn(q, k, v, o, lse, dout, causal, scale)
 
 
 def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=None, out=None, lse=None):

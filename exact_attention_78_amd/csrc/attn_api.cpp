@@ -56,6 +56,34 @@ attn_status_t check_fwd(const void* q, const void* k, const void* v, const void*
   return ATTN_OK;
 }
 
+// Validation of the 16-bit backward entry points.
+attn_status_t check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, const void* dq, const void* dk, const void* dv, const float* ws,
+                        int64_t B, int64_t H, int64_t N, int64_t d, float scale) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !ws) return ATTN_ERR_INVALID_ARG;
+  int64_t elems, rows;
+  attn_status_t st = check_shape(B, H, N, d, &elems, &rows);
+  if (st != ATTN_OK) return st;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  const void* ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (attn::max_workgroups_bwd(B * H, N) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  const uintptr_t tb = (uintptr_t)elems * 2;
+  auto span = [](const void* p, uintptr_t n) { return Range{(uintptr_t)p, (uintptr_t)p + n}; };
+  const Range ins[6] = {span(q, tb), span(k, tb), span(v, tb), span(o, tb),
+                        span(lse, (uintptr_t)rows * sizeof(float)), span(dout, tb)};
+  const Range outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(ws, (uintptr_t)rows * 2 * sizeof(float))};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return ATTN_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return ATTN_ERR_INVALID_ARG;
+  }
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -128,6 +156,24 @@ attn_status_t attn_quant_fp8(const void* x, uint8_t* x8, float* scales, const fl
   if (overlaps(r8, rx) || overlaps(r8, rs) || overlaps(rs, rx)) return ATTN_ERR_INVALID_ARG;
   if (signs && (overlaps(rg, r8) || overlaps(rg, rs))) return ATTN_ERR_INVALID_ARG;
   return from_hip(attn::launch_quant_fp8(x, x8, scales, signs, B * H, N, d, (hipStream_t)stream));
+}
+
+attn_status_t attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv, float* workspace, int64_t B, int64_t H,
+                            int64_t N, int64_t d, int causal, float scale, void* stream) {
+  attn_status_t st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B * H, N, d, causal != 0, scale,
+                                        (hipStream_t)stream));
+}
+
+attn_status_t attn_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, float* workspace, int64_t B, int64_t H,
+                           int64_t N, int64_t d, int causal, float scale, void* stream) {
+  attn_status_t st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale);
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B * H, N, d, causal != 0, scale,
+                                       (hipStream_t)stream));
 }
 
 const char* attn_status_string(attn_status_t s) {

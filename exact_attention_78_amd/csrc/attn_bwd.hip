@@ -1,0 +1,438 @@
+// Exact attention backward for bf16 / fp16 on gfx950 (MI355X).
+//
+// The FlashAttention-2 digest (key technical points and method summary) has the backward
+// pass recompute the attention from the one log-sum-exp per row that the forward pass
+// stored, splitting the work the same way; it prints no formulas. The gradients are those
+// of O = softmax(scale * Q K^T [+ causal mask]) V:
+//   P = exp(scale * Q K^T - LSE)        recomputed per tile from the stored LSE
+//   dV = P^T dO,   dP = dO V^T,   Delta_i = dO_i . O_i  (= sum_j P_ij dP_ij)
+//   dS = P * (dP - Delta),   dQ = scale * dS K,   dK = scale * dS^T Q
+// Three launches per call:
+//   prep  Delta_i and LSE_i * log2(e) of every row into the caller's workspace (reads O
+//         and dO once).
+//   dq    one workgroup per (batch*head, 256-row query tile), 8 waves x 32 rows; K and V
+//         tiles of 64 keys stream through LDS (double-buffered direct loads). Per 32-key
+//         block: S^T = K Q^T and dP^T = V dO^T (A = K / V rows read from LDS, B = Q^T and
+//         dO^T kept in VGPRs), then P and dS in fp32 with one query row per lane (its LSE
+//         and Delta are scalars), then dQ^T += K^T dS^T (A = K^T by LDS transpose reads,
+//         B = dS rounded to 16 bits).
+//   dkdv  one workgroup per (batch*head, 128-key tile), 4 waves x 32 keys; Q and dO tiles
+//         of 32 queries stream through LDS. Per tile: S = Q K^T and dP = dO V^T (A = Q /
+//         dO rows from LDS, B = K^T / V^T kept in VGPRs: one key per lane), P and dS in
+//         fp32 with the 16 per-query LSE and Delta values of each lane read from LDS, then
+//         dV^T += dO^T P and dK^T += Q^T dS (A = dO^T / Q^T by LDS transpose reads, B = P /
+//         dS rounded to 16 bits).
+// The two gradient kernels each recompute S and dP, so that every gradient stays in
+// registers until its one store: no fp32 partial sums or atomics in memory.
+// Causal: query tiles of dq stop at the diagonal and key tiles of dkdv start at it;
+// waves skip blocks that are wholly masked for them, and only blocks crossing the
+// diagonal or the end of the sequence apply a mask.
+#include "device_common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int kWq = 8;      // dq: waves per workgroup (32 query rows each)
+constexpr int kBN = 64;     // dq: keys per K/V tile
+constexpr int kWk = 4;      // dkdv: waves per workgroup (32 keys each)
+constexpr int kBQ = 32;     // dkdv: queries per Q/dO tile
+constexpr int kPrepThreads = 256;
+
+// Chunk swizzle of the LDS tiles: 16-byte chunk c of tile row r is stored at chunk
+// c ^ f(r). The tiles here are read both by rows (32 rows x one chunk per ds_read_b128)
+// and by transpose reads (4 rows x 2 chunks per 16 lanes), and f spreads both patterns
+// over distinct banks: 16 consecutive rows get 16 (d = 128) or, paired with the row
+// parity, 8 (d = 64) distinct values, and rows 4a..4a+3 move a chunk pair {2g, 2g+1}
+// to four disjoint places. f depends on row bits 0..3 only.
+template <int D> struct BSwz;
+template <> struct BSwz<128> {
+  static __device__ __forceinline__ int f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+};
+template <> struct BSwz<64> {
+  static __device__ __forceinline__ int f(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+};
+
+// Per-lane LDS byte offsets inside a tile of rows of D 16-bit elements.
+template <int D>
+struct TileAddr {
+  static constexpr int ROW = D * 2;
+  static constexpr int NSTEP = D / 16;
+  static constexpr int NDB = D / 32;
+  uint32_t row[NSTEP];       // row read: row l32, head-dim step s (16 elements)
+  uint32_t tr[2][NDB];       // transpose read: rows tr_row (+8), head-dim block db
+  __device__ __forceinline__ void init(int lane) {
+    const int half = lane / 32, l32 = lane % 32;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) row[s] = l32 * ROW + (((2 * s + half) ^ BSwz<D>::f(l32)) << 4);
+    const int g16 = lane / 16, i16 = lane % 16;
+    const int tr_row = (g16 / 2) * 4 + i16 / 4;
+    const int tr_col = 16 * (g16 % 2) + 4 * (i16 % 4);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int r = tr_row + 8 * j, col = db * 32 + tr_col;
+        tr[j][db] = r * ROW + (((col >> 3) ^ BSwz<D>::f(r)) << 4) + ((col & 7) << 1);
+      }
+  }
+};
+
+// A-operand fragment of rows [r0, r0 + 32) of a tile, head-dim step s (row reads).
+template <int D>
+__device__ __forceinline__ u32x4 row_frag(const uint8_t* tile, const TileAddr<D>& a, int r0, int s) {
+  return *(const u32x4*)(tile + r0 * TileAddr<D>::ROW + a.row[s]);
+}
+// A-operand fragment of the transpose of rows [r0, r0 + 16) (the contraction index),
+// head-dim block db: the 8 rows each half of the wave supplies follow the order of the
+// 32x32 accumulator rows (8 * (r / 4) + 4 * half + r % 4) that the B operand comes from.
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag(const uint8_t* tile, const TileAddr<D>& a, int r0, int db) {
+  const uint8_t* base = tile + r0 * TileAddr<D>::ROW;
+  const u32x2 v1 = lds_read_tr16((const uint16_t*)(base + a.tr[0][db]));
+  const u32x2 v2 = lds_read_tr16((const uint16_t*)(base + a.tr[1][db]));
+  return u32x4{v1[0], v1[1], v2[0], v2[1]};
+}
+
+// Direct global -> LDS load of a tile of R rows starting at row r0 (rows past N re-read
+// row N-1, whose results are masked). Wave w of W fills 1 KiB pieces w, w + W, ...
+template <int D, int R, int W>
+__device__ __forceinline__ void load_rows(const uint16_t* src, int r0, int N, uint8_t* dst, int wave, int lane) {
+  constexpr int ROW = D * 2, TB = R * ROW, LPW = TB / 1024 / W;
+  static_assert(LPW >= 1 && LPW * 1024 * W == TB, "tile must split into whole 1 KiB loads per wave");
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int slot = (wave * LPW + i) * 1024 + lane * 16;
+    const int r = slot / ROW, phys = (slot % ROW) / 16;
+    const int row = min(r0 + r, N - 1);
+    dma_load16((const uint8_t*)(src + (int64_t)row * D) + ((phys ^ BSwz<D>::f(r)) << 4),
+               lds_u32(dst) + (wave * LPW + i) * 1024);
+  }
+}
+
+// B operand of the next contraction: 16 fp32 accumulator values -> two groups of 8
+// 16-bit values (accumulator rows 0..7 and 8..15).
+template <typename Tag>
+__device__ __forceinline__ void pack16(const float (&x)[16], u32x4 (&p)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    p[h] = u32x4{pack2(Tag{}, x[h * 8 + 0], x[h * 8 + 1]), pack2(Tag{}, x[h * 8 + 2], x[h * 8 + 3]),
+                 pack2(Tag{}, x[h * 8 + 4], x[h * 8 + 5]), pack2(Tag{}, x[h * 8 + 6], x[h * 8 + 7])};
+}
+
+// Store 32 x D accumulators (lane: one row of the result; head dims 8 * (r / 4) + 4 * half
+// + r % 4 of each block) times `mul` as 16-bit values.
+template <typename Tag, int D>
+__device__ __forceinline__ void store_rows(uint16_t* dst_row, const f32x16 (&acc)[D / 32], int half, float mul) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + g * 8 + half * 4;
+      const f32x16 a = acc[db];
+      u32x2 w = {pack2(Tag{}, a[g * 4 + 0] * mul, a[g * 4 + 1] * mul),
+                 pack2(Tag{}, a[g * 4 + 2] * mul, a[g * 4 + 3] * mul)};
+      *(u32x2*)(dst_row + d) = w;
+    }
+}
+
+// B-operand fragments of one row (this lane's) of a [N, D] tensor: head-dim step s holds
+// elements s * 16 + half * 8 .. + 7; zero past the end of the sequence.
+template <int D>
+__device__ __forceinline__ void load_row_operand(const uint16_t* base, int row, int N, int half, u32x4 (&r)[D / 16]) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    r[s] = row < N ? *(const u32x4*)(base + (int64_t)row * D + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
+}
+
+__device__ __forceinline__ float to_f32(Bf16Tag, uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
+__device__ __forceinline__ float to_f32(F16Tag, uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// Delta_i = sum_d dO_id * O_id (fp32) and LSE_i * log2(e), D/16 lanes per row.
+template <typename Tag, int D>
+__global__ __launch_bounds__(kPrepThreads) void attn_bwd_prep_kernel(const uint16_t* __restrict__ O,
+                                                                     const uint16_t* __restrict__ dO,
+                                                                     const float* __restrict__ LSE,
+                                                                     float* __restrict__ ws, int64_t rows) {
+  constexpr int LPR = D / 16;
+  const int64_t row = (int64_t)blockIdx.x * (kPrepThreads / LPR) + threadIdx.x / LPR;
+  const int seg = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 o = *(const u32x4*)(O + row * D + seg * 16 + i * 8);
+      const u32x4 g = *(const u32x4*)(dO + row * D + seg * 16 + i * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = __builtin_fmaf(to_f32(Tag{}, o[e] & 0xFFFFu), to_f32(Tag{}, g[e] & 0xFFFFu), acc);
+        acc = __builtin_fmaf(to_f32(Tag{}, o[e] >> 16), to_f32(Tag{}, g[e] >> 16), acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off /= 2) acc += __shfl_xor(acc, off);
+  if (row < rows && seg == 0) {
+    ws[row] = acc;
+    ws[rows + row] = LSE[row] * kLog2e;
+  }
+}
+
+template <typename Tag, int D, bool CAUSAL>
+__global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dQ, int N, int n_mtiles,
+    int total_wg, int64_t rows, float c /* scale*log2 e */, float scale) {
+  constexpr int W = kWq, BM = W * 32, NSTEP = D / 16, NKB = kBN / 32, NDB = D / 32;
+  constexpr int TB = kBN * D * 2;                   // bytes per K (or V) tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TB];   // K slots 0, 1; V slots 0, 1
+
+  const int logical = xcd_logical_id(blockIdx.x, total_wg);
+  const int bh = logical / n_mtiles;
+  int mt = logical % n_mtiles;
+  if (CAUSAL) mt = n_mtiles - 1 - mt;               // longest query tiles first
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int half = lane / 32, l32 = lane % 32;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const uint16_t* Kh = K + head_off;
+  const uint16_t* Vh = V + head_off;
+
+  const int q0 = mt * BM + wave * 32;
+  const int qrow = q0 + l32;
+  u32x4 qreg[NSTEP], doreg[NSTEP];
+  load_row_operand<D>(Q + head_off, qrow, N, half, qreg);
+  load_row_operand<D>(dO + head_off, qrow, N, half, doreg);
+  const float delta = qrow < N ? ws[(int64_t)bh * N + qrow] : 0.f;
+  const float lse2 = qrow < N ? ws[rows + (int64_t)bh * N + qrow] : 0.f;
+
+  const int n_ktiles = (N + kBN - 1) / kBN;
+  const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * BM + kBN - 1) / kBN) : n_ktiles;
+  TileAddr<D> ta;
+  ta.init(lane);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  auto kbuf = [&](int slot) __attribute__((always_inline)) { return lds + slot * TB; };
+  auto vbuf = [&](int slot) __attribute__((always_inline)) { return lds + (2 + slot) * TB; };
+
+  load_rows<D, kBN, W>(Kh, 0, N, kbuf(0), wave, lane);
+  load_rows<D, kBN, W>(Vh, 0, N, vbuf(0), wave, lane);
+  wait_vmcnt<0>();
+  barrier_lds();
+  for (int t = 0; t < T; ++t) {
+    const int slot = t & 1;
+    if (t + 1 < T) {
+      load_rows<D, kBN, W>(Kh, (t + 1) * kBN, N, kbuf(slot ^ 1), wave, lane);
+      load_rows<D, kBN, W>(Vh, (t + 1) * kBN, N, vbuf(slot ^ 1), wave, lane);
+    }
+    if (!CAUSAL || t * kBN <= q0 + 31) {            // else: every key of the tile lies past this wave's rows
+      const uint8_t* kt = kbuf(slot);
+      const uint8_t* vt = vbuf(slot);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) s = mfma32(Tag{}, row_frag<D>(kt, ta, kb * 32, st), qreg[st], s);
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) dp = mfma32(Tag{}, row_frag<D>(vt, ta, kb * 32, st), doreg[st], dp);
+        const int key0 = t * kBN + kb * 32;
+        const bool edge = (CAUSAL && key0 + 31 > q0) || key0 + 32 > N;
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[r];
+          if (edge) {
+            const int key = key0 + (r / 4) * 8 + half * 4 + (r % 4);
+            if ((CAUSAL && key > qrow) || key >= N) x = -INFINITY;
+          }
+          const float p = fast_exp2(__builtin_fmaf(x, c, -lse2));
+          ds[r] = p * (dp[r] - delta);
+        }
+        u32x4 pb[2];
+        pack16<Tag>(ds, pb);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(Tag{}, tr_frag<D>(kt, ta, kb * 32 + h * 16, db), pb[h], acc[db]);
+      }
+    }
+    wait_vmcnt<0>();
+    barrier_lds();
+  }
+  if (qrow < N) store_rows<Tag, D>(dQ + head_off + (int64_t)qrow * D, acc, half, scale);
+}
+
+template <typename Tag, int D, bool CAUSAL>
+__global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int N, int n_ntiles, int total_wg, int64_t rows, float c, float scale) {
+  constexpr int W = kWk, BNK = W * 32, NSTEP = D / 16, NDB = D / 32;
+  constexpr int TB = kBQ * D * 2;                   // bytes per Q (or dO) tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TB];   // Q slots 0, 1; dO slots 0, 1
+  __shared__ __attribute__((aligned(16))) float lsd[2][2][kBQ];  // [slot][LSE*log2 e | Delta][query]
+
+  const int logical = xcd_logical_id(blockIdx.x, total_wg);
+  const int bh = logical / n_ntiles;
+  const int nt = logical % n_ntiles;                // causal: low key tiles carry the most queries, and go first
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int half = lane / 32, l32 = lane % 32;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const uint16_t* Qh = Q + head_off;
+  const uint16_t* dOh = dO + head_off;
+  const float* delta_h = ws + (int64_t)bh * N;
+  const float* lse2_h = ws + rows + (int64_t)bh * N;
+
+  const int k0 = nt * BNK + wave * 32;
+  const int krow = k0 + l32;
+  u32x4 kreg[NSTEP], vreg[NSTEP];
+  load_row_operand<D>(K + head_off, krow, N, half, kreg);
+  load_row_operand<D>(V + head_off, krow, N, half, vreg);
+
+  const int n_qtiles = (N + kBQ - 1) / kBQ;
+  const int u0 = CAUSAL ? (nt * BNK) / kBQ : 0;
+  TileAddr<D> ta;
+  ta.init(lane);
+
+  f32x16 acck[NDB], accv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    acck[db] = f32x16{};
+    accv[db] = f32x16{};
+  }
+  auto qbuf = [&](int slot) __attribute__((always_inline)) { return lds + slot * TB; };
+  auto gbuf = [&](int slot) __attribute__((always_inline)) { return lds + (2 + slot) * TB; };
+  // the first 64 threads fetch the LSE (log2 units) and Delta of a query tile
+  auto fetch_ld = [&](int u) __attribute__((always_inline)) -> float {
+    const int q = min(u * kBQ + (tid % 32), N - 1);
+    return tid < 32 ? lse2_h[q] : delta_h[q];
+  };
+
+  if (u0 < n_qtiles) {
+    load_rows<D, kBQ, W>(Qh, u0 * kBQ, N, qbuf(0), wave, lane);
+    load_rows<D, kBQ, W>(dOh, u0 * kBQ, N, gbuf(0), wave, lane);
+    if (tid < 64) lsd[0][tid / 32][tid % 32] = fetch_ld(u0);
+    wait_vmcnt<0>();
+    barrier_lds();
+  }
+  for (int u = u0; u < n_qtiles; ++u) {
+    const int slot = (u - u0) & 1;
+    float pf = 0.f;
+    if (u + 1 < n_qtiles) {
+      load_rows<D, kBQ, W>(Qh, (u + 1) * kBQ, N, qbuf(slot ^ 1), wave, lane);
+      load_rows<D, kBQ, W>(dOh, (u + 1) * kBQ, N, gbuf(slot ^ 1), wave, lane);
+      if (tid < 64) pf = fetch_ld(u + 1);
+    }
+    const int qbase = u * kBQ;
+    if (!CAUSAL || qbase + kBQ - 1 >= k0) {         // else: every query of the tile precedes this wave's keys
+      const uint8_t* qt = qbuf(slot);
+      const uint8_t* gt = gbuf(slot);
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) s = mfma32(Tag{}, row_frag<D>(qt, ta, 0, st), kreg[st], s);
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) dp = mfma32(Tag{}, row_frag<D>(gt, ta, 0, st), vreg[st], dp);
+      const bool edge = (CAUSAL && qbase < k0 + 31) || qbase + kBQ > N;
+      float p[16], ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = g * 8 + half * 4;            // this lane's queries qi .. qi + 3 of the tile
+        const f32x4 l4 = *(const f32x4*)&lsd[slot][0][qi];
+        const f32x4 d4 = *(const f32x4*)&lsd[slot][1][qi];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = g * 4 + e;
+          float x = s[r];
+          if (edge) {
+            const int q = qbase + qi + e;
+            if ((CAUSAL && q < krow) || q >= N) x = -INFINITY;
+          }
+          p[r] = fast_exp2(__builtin_fmaf(x, c, -l4[e]));
+          ds[r] = p[r] * (dp[r] - d4[e]);
+        }
+      }
+      u32x4 pb[2], sb[2];
+      pack16<Tag>(p, pb);
+      pack16<Tag>(ds, sb);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          accv[db] = mfma32(Tag{}, tr_frag<D>(gt, ta, h * 16, db), pb[h], accv[db]);
+          acck[db] = mfma32(Tag{}, tr_frag<D>(qt, ta, h * 16, db), sb[h], acck[db]);
+        }
+    }
+    if (u + 1 < n_qtiles && tid < 64) lsd[slot ^ 1][tid / 32][tid % 32] = pf;
+    wait_vmcnt<0>();
+    barrier_lds();
+  }
+  if (krow < N) {
+    store_rows<Tag, D>(dK + head_off + (int64_t)krow * D, acck, half, scale);
+    store_rows<Tag, D>(dV + head_off + (int64_t)krow * D, accv, half, 1.f);
+  }
+}
+
+template <typename Tag, int D, bool CAUSAL>
+hipError_t launch_one(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                      void* dq, void* dk, void* dv, float* ws, int64_t BH, int64_t N, float scale, hipStream_t stream) {
+  const int64_t rows = BH * N;
+  constexpr int rows_per_prep = kPrepThreads / (D / 16);
+  hipLaunchKernelGGL((attn_bwd_prep_kernel<Tag, D>), dim3((unsigned)((rows + rows_per_prep - 1) / rows_per_prep)),
+                     dim3(kPrepThreads), 0, stream, (const uint16_t*)o, (const uint16_t*)dout, lse, ws, rows);
+  const float c = scale * kLog2e;
+  const int n_mtiles = (int)((N + kWq * 32 - 1) / (kWq * 32));
+  const int64_t total_q = BH * n_mtiles;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag, D, CAUSAL>), dim3((unsigned)total_q), dim3(kWq * 64), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws,
+                     (uint16_t*)dq, (int)N, n_mtiles, (int)total_q, rows, c, scale);
+  const int n_ntiles = (int)((N + kWk * 32 - 1) / (kWk * 32));
+  const int64_t total_k = BH * n_ntiles;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)total_k), dim3(kWk * 64), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws,
+                     (uint16_t*)dk, (uint16_t*)dv, (int)N, n_ntiles, (int)total_k, rows, c, scale);
+  return hipGetLastError();
+}
+
+template <typename Tag>
+hipError_t launch_16bit(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, float* ws, int64_t BH, int64_t N, int64_t d,
+                        bool causal, float scale, hipStream_t stream) {
+  if (d == 128)
+    return causal ? launch_one<Tag, 128, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, BH, N, scale, stream)
+                  : launch_one<Tag, 128, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, BH, N, scale, stream);
+  return causal ? launch_one<Tag, 64, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, BH, N, scale, stream)
+                : launch_one<Tag, 64, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, BH, N, scale, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, float* ws, int64_t BH, int64_t N, int64_t d,
+                           bool causal, float scale, hipStream_t stream) {
+  return launch_16bit<Bf16Tag>(q, k, v, o, lse, dout, dq, dk, dv, ws, BH, N, d, causal, scale, stream);
+}
+
+hipError_t launch_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, float* ws, int64_t BH, int64_t N, int64_t d,
+                          bool causal, float scale, hipStream_t stream) {
+  return launch_16bit<F16Tag>(q, k, v, o, lse, dout, dq, dk, dv, ws, BH, N, d, causal, scale, stream);
+}
+
+int64_t max_workgroups_bwd(int64_t BH, int64_t N) {
+  const int64_t a = BH * ((N + kWq * 32 - 1) / (kWq * 32));
+  const int64_t b = BH * ((N + kWk * 32 - 1) / (kWk * 32));
+  const int64_t p = (BH * N + 15) / 16;              // prep: at least 16 rows per workgroup
+  return a > b ? (a > p ? a : p) : (b > p ? b : p);
+}
+
+}  // namespace attn

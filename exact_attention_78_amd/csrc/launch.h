@@ -19,10 +19,18 @@ hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v
 hipError_t launch_quant_fp8(const void* x, uint8_t* x8, float* scales, const float* signs, int64_t BH, int64_t N,
                             int64_t d, hipStream_t stream);
 
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, float* ws, int64_t BH, int64_t N, int64_t d,
+                           bool causal, float scale, hipStream_t stream);
+hipError_t launch_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, float* ws, int64_t BH, int64_t N, int64_t d,
+                          bool causal, float scale, hipStream_t stream);
+
 // Workgroup counts of the launches above (validated against the 32-bit grid limit).
 int64_t max_workgroups_fwd16(int64_t BH, int64_t N);
 int64_t max_workgroups_fwd32(int64_t BH, int64_t N);
 int64_t max_workgroups_fwd8(int64_t BH, int64_t N);
 int64_t max_workgroups_quant(int64_t BH, int64_t N);
+int64_t max_workgroups_bwd(int64_t BH, int64_t N);
 
 }  // namespace attn

@@ -1,5 +1,6 @@
 /*
- * attn.h — C ABI of the exact attention forward library for AMD Instinct MI355X (gfx950).
+ * attn.h — C ABI of the exact attention library (forward, backward, fp8 input preparation)
+ * for AMD Instinct MI355X (gfx950).
  *
  * Operation (all entry points). For every batch b and head h independently, with
  * Q, K, V the [N, d] slices of that head:
@@ -32,7 +33,7 @@
  *      ATTN_ERR_INVALID_ARG  a NULL pointer, B/H/N < 1, a scale that is not finite and
  *                            > 0, a pointer not 16-byte aligned, an element count that
  *                            overflows int64, or an output range overlapping an input
- *                            or the other output;
+ *                            or another output;
  *      ATTN_ERR_UNSUPPORTED  d not in {64, 128} (fp8 entry points: d = 128 only);
  *      ATTN_ERR_LAUNCH       the kernel launch itself failed (hipGetLastError).
  *  - Numbers: inputs with NaN or Inf give undefined outputs (not checked on the device).
@@ -105,6 +106,29 @@ attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* 
  * even. Writes x8 (uint8 [B, H, N, d]) and scales (fp32 [B, H, ceil(N/128)]). */
 attn_status_t attn_quant_fp8(const void* x, uint8_t* x8, float* scales, const float* signs,
                              int64_t B, int64_t H, int64_t N, int64_t d, void* stream);
+
+/* Backward pass of attn_fwd_bf16 (FlashAttention-2 digest, key technical points and
+ * method summary: the gradients are recomputed from the one stored log-sum-exp per row,
+ * with the same split of the work as the forward pass). Inputs: q, k, v, the forward
+ * outputs o and lse of the same call (same causal flag and scale), and dout = dL/dO, all
+ * bf16 [B, H, N, d] except lse (fp32 [B, H, N]). Outputs (bf16 [B, H, N, d], round to
+ * nearest even): dq, dk, dv, the gradients of sum(dout * O) with respect to q, k, v for
+ * O = softmax(scale * q k^T [+ causal mask]) v. workspace is caller-owned device memory
+ * of 2 * B * H * N floats; the call overwrites it (per row: dout . o, then lse * log2 e)
+ * and it holds nothing of use afterwards. The products use bf16 operands (P and dS
+ * rounded to bf16) with fp32 accumulation. The call enqueues three kernels on `stream`;
+ * dq, dk and dv are complete when the last has run. Outputs must not overlap each other,
+ * the inputs or the workspace. */
+attn_status_t attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv, float* workspace,
+                            int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                            void* stream);
+
+/* fp16 tensors in and out; as attn_bwd_bf16 with fp16 in place of bf16. */
+attn_status_t attn_bwd_f16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, float* workspace,
+                           int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                           void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* attn_status_string(attn_status_t s);

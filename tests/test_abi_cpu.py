@@ -25,7 +25,7 @@ OK, INVALID, UNSUPPORTED = 0, 1, 2
 # validation bug can never turn one into a real launch.
 no_gpu_only = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="fake-pointer validation runs on GPU-less hosts")
 # distinct, 16-byte aligned, far-apart fake device addresses (never dereferenced)
-A = [(i + 1) << 40 for i in range(8)]
+A = [(i + 1) << 40 for i in range(10)]
 
 
 def header_functions():
@@ -41,7 +41,7 @@ def lib():
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = header_functions()
     assert set(names) == {"attn_fwd_bf16", "attn_fwd_f16", "attn_fwd_f32", "attn_fwd_fp8", "attn_quant_fp8",
-                          "attn_status_string", "attn_abi_version"}
+                          "attn_bwd_bf16", "attn_bwd_f16", "attn_status_string", "attn_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in _binding.SIGNATURES, n
@@ -101,6 +101,24 @@ def test_quant_validation(lib, defect, expect):
     args = dict(x=A[0], x8=A[1], sc=A[2], signs=A[3], B=1, H=1, N=256, d=128)
     args.update(defect)
     assert lib.attn_quant_fp8(*args.values(), None) == expect
+
+
+@no_gpu_only
+@pytest.mark.parametrize("fn", ["attn_bwd_bf16", "attn_bwd_f16"])
+@pytest.mark.parametrize("defect,expect", [
+    (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(lse=None), INVALID), (dict(dout=None), INVALID),
+    (dict(dq=None), INVALID), (dict(dv=None), INVALID), (dict(ws=None), INVALID), (dict(N=0), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(scale=0.0), INVALID), (dict(scale=math.nan), INVALID),
+    (dict(dk=A[5] + 8), INVALID), (dict(ws=A[9] + 4), INVALID),
+    (dict(dq=A[0]), INVALID), (dict(dk=A[3] + 64), INVALID), (dict(dv=A[5] + 16), INVALID), (dict(ws=A[4]), INVALID),
+    (dict(ws=A[6] + 32), INVALID), (dict(dq=A[7]), INVALID),
+    (dict(B=1 << 31, H=1 << 31, N=1 << 20), INVALID),
+])
+def test_bwd_validation(lib, fn, defect, expect):
+    args = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], dout=A[5], dq=A[6], dk=A[7], dv=A[8], ws=A[9],
+                B=1, H=2, N=64, d=64, causal=1, scale=0.125)
+    args.update(defect)
+    assert getattr(lib, fn)(*args.values(), None) == expect
 
 
 def test_binding_rejects_host_tensors_before_calling():

@@ -1,0 +1,121 @@
+"""GPU parity of the bf16 / fp16 attention backward against the fp64 oracle.
+
+The device forward (attn_fwd_*) produces O and LSE, the device backward (attn_bwd_*)
+the gradients; both go through the C ABI. The oracle differentiates the plain
+definition in fp64 on exactly the rounded Q, K, V and dO the GPU sees, so the error
+covers the whole device path: the forward's rounded O and stored LSE, P and dS rounded
+to 16 bits, fp32 accumulation and the 16-bit gradients.
+
+Tolerance. No passage fixes one for the gradients. Each gradient is a sum of products
+whose factors the device rounds to 16 bits once (relative error 2^-9 for bf16, 2^-12
+for fp16) before fp32 accumulation, and the result is rounded once more; with the
+forward's O gate (2e-2 absolute on values of order one) as the model, the bound here is
+max|dX - dX_ref| <= 2e-2 * max(1, max|dX_ref|) per gradient tensor, the same budget
+scaled by the gradient's magnitude (which grows with the number of rows that attend to
+a key). The test prints the measured errors, which sit well inside it.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_78_amd import attn_bwd_bf16, attn_bwd_f16, attn_fwd_bf16, attn_fwd_f16, bwd, inputs
+from oracle.attention import attention_backward
+
+pytestmark = pytest.mark.gpu
+
+G_TOL = 2e-2
+
+FWD = {"bf16": attn_fwd_bf16, "f16": attn_fwd_f16}
+BWD = {"bf16": attn_bwd_bf16, "f16": attn_bwd_f16}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def make(wid, B, H, N, d, dtype, k_mult=1.0):
+    q, k, v = inputs.draw_qkv(wid, B, H, N, d)
+    if k_mult != 1.0:
+        k = k * np.float32(k_mult)
+    g = inputs.draw_dout(wid, B, H, N, d)
+    return tuple(inputs.to_torch(x, dtype) for x in (q, k, v, g))
+
+
+def run_device(cpu, dtype, causal):
+    tq, tk, tv, tg = (t.cuda() for t in cpu)
+    scale = inputs.softmax_scale(tq.shape[-1])
+    o, lse = FWD[dtype](tq, tk, tv, causal=causal, scale=scale)
+    dq, dk, dv = BWD[dtype](tq, tk, tv, o, lse, tg, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return [x.double().cpu().numpy() for x in (dq, dk, dv)]
+
+
+def compare(got, ref, label, heads=None):
+    errs = []
+    for name, x, r in zip(("dQ", "dK", "dV"), got, ref):
+        if heads is not None:
+            idx = tuple(np.array(heads).T)
+            x, r = x[idx], r[idx]
+        assert np.isfinite(x).all(), name
+        e = np.abs(x - r).max()
+        bound = G_TOL * max(1.0, np.abs(r).max())
+        errs.append(f"{name} {e:.2e} (bound {bound:.2e})")
+        assert e <= bound, (name, e, bound)
+    say(f"  {label}: " + ", ".join(errs))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 1000, 128), (2, 3, 333, 64), (1, 1, 1, 64), (1, 2, 17, 128),
+                                   (1, 1, 129, 64), (1, 1, 257, 128), (2, 2, 640, 128), (1, 1, 300, 64)])
+def test_small_ragged_shapes(shape, causal, dtype):
+    B, H, N, d = shape
+    say(f"case bwd {dtype} shape={shape} causal={causal}")
+    cpu = make(60 + N % 17, B, H, N, d, dtype)
+    got = run_device(cpu, dtype, causal)
+    ref = attention_backward(*cpu, causal, inputs.softmax_scale(d))
+    compare(got, ref, f"{dtype} {shape} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_scores(causal):
+    # keys scaled x8: peaked softmax rows, large LSE values and large dS entries
+    B, H, N, d = 1, 2, 700, 128
+    say(f"case bwd large scores causal={causal}")
+    cpu = make(71, B, H, N, d, "bf16", k_mult=8.0)
+    got = run_device(cpu, "bf16", causal)
+    ref = attention_backward(*cpu, causal, inputs.softmax_scale(d))
+    compare(got, ref, f"x8 keys causal={causal}")
+
+
+@pytest.mark.parametrize("name", ["C3", "H"])
+def test_full_size_sampled_heads(name):
+    # full-size launch (every head computed on the device); the oracle differentiates
+    # two heads completely
+    w = inputs.WORKLOADS[name]
+    say(f"case bwd full size {name} B{w.B} H{w.H} N{w.N} d{w.d} causal")
+    cpu = make(w.wid, w.B, w.H, w.N, w.d, "bf16")
+    got = run_device(cpu, "bf16", True)
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    ref = attention_backward(*cpu, True, w.scale, heads=heads, row_chunk=1024)
+    compare(got, ref, f"{name} sampled heads", heads=heads)
+    for x in got:
+        assert np.isfinite(x).all()
+
+
+def test_dispatch_stream_and_determinism():
+    cpu = make(72, 1, 2, 300, 64, "f16")
+    tq, tk, tv, tg = (t.cuda() for t in cpu)
+    o, lse = attn_fwd_f16(tq, tk, tv, causal=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = bwd(tq, tk, tv, o, lse, tg, causal=True)
+    s.synchronize()
+    b = attn_bwd_f16(tq, tk, tv, o, lse, tg, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
