@@ -16,14 +16,19 @@
 //         dO^T kept in VGPRs), then P and dS in fp32 with one query row per lane (its LSE
 //         and Delta are scalars), then dQ^T += K^T dS^T (A = K^T by LDS transpose reads,
 //         B = dS rounded to 16 bits).
-//   dkdv  one workgroup per (batch*head, 128-key tile), 4 waves x 32 keys; Q and dO tiles
-//         of 32 queries stream through LDS. Per tile: S = Q K^T and dP = dO V^T (A = Q /
-//         dO rows from LDS, B = K^T / V^T kept in VGPRs: one key per lane), P and dS in
-//         fp32 with the 16 per-query LSE and Delta values of each lane read from LDS, then
-//         dV^T += dO^T P and dK^T += Q^T dS (A = dO^T / Q^T by LDS transpose reads, B = P /
-//         dS rounded to 16 bits).
+//   dkdv  one workgroup per (batch*head, 128-key tile), 4 waves x 32 keys; the tile's K
+//         and V stay in LDS, Q and dO tiles of 64 queries stream through it. Per 32-query
+//         block: S = Q K^T and dP = dO V^T (A = Q / dO rows, B = K^T / V^T as rows of K / V:
+//         one key per lane), P and dS in fp32 with the 16 per-query LSE and Delta values
+//         of each lane read from LDS, then dV^T += dO^T P and dK^T += Q^T dS (A = dO^T /
+//         Q^T by LDS transpose reads, B = P / dS rounded to 16 bits). K and V are read
+//         from LDS rather than kept in VGPRs so that the kernel fits 256 VGPRs: beyond
+//         that the compiler moves every MFMA result through AGPRs.
 // The two gradient kernels each recompute S and dP, so that every gradient stays in
 // registers until its one store: no fp32 partial sums or atomics in memory.
+// At d = 128 the dkdv kernel needs more than 256 registers (one wave per SIMD); this file
+// is compiled with MFMA results in VGPRs (-amdgpu-mfma-vgpr-form), so that only what does
+// not fit spills to AGPRs instead of every S / dP block being copied out of them.
 // Causal: query tiles of dq stop at the diagonal and key tiles of dkdv start at it;
 // waves skip blocks that are wholly masked for them, and only blocks crossing the
 // diagonal or the end of the sequence apply a mask.
@@ -36,7 +41,7 @@ namespace {
 constexpr int kWq = 8;      // dq: waves per workgroup (32 query rows each)
 constexpr int kBN = 64;     // dq: keys per K/V tile
 constexpr int kWk = 4;      // dkdv: waves per workgroup (32 keys each)
-constexpr int kBQ = 32;     // dkdv: queries per Q/dO tile
+constexpr int kBQ = 64;     // dkdv: queries per Q/dO tile (two 32-query blocks)
 constexpr int kPrepThreads = 256;
 
 // Chunk swizzle of the LDS tiles: 16-byte chunk c of tile row r is stored at chunk
@@ -270,13 +275,14 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
 }
 
 template <typename Tag, int D, bool CAUSAL>
-__global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kWk * 64, D == 64 ? 2 : 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int N, int n_ntiles, int total_wg, int64_t rows, float c, float scale) {
-  constexpr int W = kWk, BNK = W * 32, NSTEP = D / 16, NDB = D / 32;
+  constexpr int W = kWk, BNK = W * 32, NSTEP = D / 16, NDB = D / 32, NQB = kBQ / 32;
   constexpr int TB = kBQ * D * 2;                   // bytes per Q (or dO) tile
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TB];   // Q slots 0, 1; dO slots 0, 1
+  constexpr int TKV = BNK * D * 2;                  // bytes of the workgroup's K (or V)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TB + 2 * TKV];   // Q slots 0, 1; dO slots 0, 1; K; V
   __shared__ __attribute__((aligned(16))) float lsd[2][2][kBQ];  // [slot][LSE*log2 e | Delta][query]
 
   const int logical = xcd_logical_id(blockIdx.x, total_wg);
@@ -295,9 +301,6 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
 
   const int k0 = nt * BNK + wave * 32;
   const int krow = k0 + l32;
-  u32x4 kreg[NSTEP], vreg[NSTEP];
-  load_row_operand<D>(K + head_off, krow, N, half, kreg);
-  load_row_operand<D>(V + head_off, krow, N, half, vreg);
 
   const int n_qtiles = (N + kBQ - 1) / kBQ;
   const int u0 = CAUSAL ? (nt * BNK) / kBQ : 0;
@@ -312,67 +315,83 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
   }
   auto qbuf = [&](int slot) __attribute__((always_inline)) { return lds + slot * TB; };
   auto gbuf = [&](int slot) __attribute__((always_inline)) { return lds + (2 + slot) * TB; };
-  // the first 64 threads fetch the LSE (log2 units) and Delta of a query tile
+  uint8_t* const kt = lds + 4 * TB;                 // rows: the workgroup's keys (past N: row N-1, never stored)
+  uint8_t* const vt = kt + TKV;
+  // the first 2 * kBQ threads fetch the LSE (log2 units) and Delta of a query tile
   auto fetch_ld = [&](int u) __attribute__((always_inline)) -> float {
-    const int q = min(u * kBQ + (tid % 32), N - 1);
-    return tid < 32 ? lse2_h[q] : delta_h[q];
+    const int q = min(u * kBQ + (tid % kBQ), N - 1);
+    return tid < kBQ ? lse2_h[q] : delta_h[q];
   };
+  static_assert(2 * kBQ <= W * 64, "one thread per fetched value");
 
-  if (u0 < n_qtiles) {
-    load_rows<D, kBQ, W>(Qh, u0 * kBQ, N, qbuf(0), wave, lane);
-    load_rows<D, kBQ, W>(dOh, u0 * kBQ, N, gbuf(0), wave, lane);
-    if (tid < 64) lsd[0][tid / 32][tid % 32] = fetch_ld(u0);
-    wait_vmcnt<0>();
-    barrier_lds();
-  }
+  load_rows<D, BNK, W>(K + head_off, nt * BNK, N, kt, wave, lane);
+  load_rows<D, BNK, W>(V + head_off, nt * BNK, N, vt, wave, lane);
+  load_rows<D, kBQ, W>(Qh, u0 * kBQ, N, qbuf(0), wave, lane);      // u0 < n_qtiles: the tile's first key is < N
+  load_rows<D, kBQ, W>(dOh, u0 * kBQ, N, gbuf(0), wave, lane);
+  if (tid < 2 * kBQ) lsd[0][tid / kBQ][tid % kBQ] = fetch_ld(u0);
+  wait_vmcnt<0>();
+  barrier_lds();
   for (int u = u0; u < n_qtiles; ++u) {
     const int slot = (u - u0) & 1;
     float pf = 0.f;
     if (u + 1 < n_qtiles) {
       load_rows<D, kBQ, W>(Qh, (u + 1) * kBQ, N, qbuf(slot ^ 1), wave, lane);
       load_rows<D, kBQ, W>(dOh, (u + 1) * kBQ, N, gbuf(slot ^ 1), wave, lane);
-      if (tid < 64) pf = fetch_ld(u + 1);
+      if (tid < 2 * kBQ) pf = fetch_ld(u + 1);
     }
     const int qbase = u * kBQ;
     if (!CAUSAL || qbase + kBQ - 1 >= k0) {         // else: every query of the tile precedes this wave's keys
       const uint8_t* qt = qbuf(slot);
       const uint8_t* gt = gbuf(slot);
-      f32x16 s = f32x16{}, dp = f32x16{};
+      f32x16 s[NQB], dp[NQB];
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st) s = mfma32(Tag{}, row_frag<D>(qt, ta, 0, st), kreg[st], s);
+      for (int qb = 0; qb < NQB; ++qb) {
+        s[qb] = f32x16{};
+        dp[qb] = f32x16{};
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st) dp = mfma32(Tag{}, row_frag<D>(gt, ta, 0, st), vreg[st], dp);
-      const bool edge = (CAUSAL && qbase < k0 + 31) || qbase + kBQ > N;
-      float p[16], ds[16];
+        for (int st = 0; st < NSTEP; ++st)
+          s[qb] = mfma32(Tag{}, row_frag<D>(qt, ta, qb * 32, st), row_frag<D>(kt, ta, wave * 32, st), s[qb]);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qi = g * 8 + half * 4;            // this lane's queries qi .. qi + 3 of the tile
-        const f32x4 l4 = *(const f32x4*)&lsd[slot][0][qi];
-        const f32x4 d4 = *(const f32x4*)&lsd[slot][1][qi];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = g * 4 + e;
-          float x = s[r];
-          if (edge) {
-            const int q = qbase + qi + e;
-            if ((CAUSAL && q < krow) || q >= N) x = -INFINITY;
-          }
-          p[r] = fast_exp2(__builtin_fmaf(x, c, -l4[e]));
-          ds[r] = p[r] * (dp[r] - d4[e]);
-        }
+        for (int st = 0; st < NSTEP; ++st)
+          dp[qb] = mfma32(Tag{}, row_frag<D>(gt, ta, qb * 32, st), row_frag<D>(vt, ta, wave * 32, st), dp[qb]);
       }
-      u32x4 pb[2], sb[2];
-      pack16<Tag>(p, pb);
-      pack16<Tag>(ds, sb);
+      u32x4 pb[NQB][2], sb[NQB][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int qb0 = qbase + qb * 32;
+        const bool edge = (CAUSAL && qb0 < k0 + 31) || qb0 + 32 > N;
+        float p[16], ds[16];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          accv[db] = mfma32(Tag{}, tr_frag<D>(gt, ta, h * 16, db), pb[h], accv[db]);
-          acck[db] = mfma32(Tag{}, tr_frag<D>(qt, ta, h * 16, db), sb[h], acck[db]);
+        for (int g = 0; g < 4; ++g) {
+          const int qi = qb * 32 + g * 8 + half * 4;   // this lane's queries qi .. qi + 3 of the tile
+          const f32x4 l4 = *(const f32x4*)&lsd[slot][0][qi];
+          const f32x4 d4 = *(const f32x4*)&lsd[slot][1][qi];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = g * 4 + e;
+            float x = s[qb][r];
+            if (edge) {
+              const int q = qbase + qi + e;
+              if ((CAUSAL && q < krow) || q >= N) x = -INFINITY;
+            }
+            p[r] = fast_exp2(__builtin_fmaf(x, c, -l4[e]));
+            ds[r] = p[r] * (dp[qb][r] - d4[e]);
+          }
         }
+        pack16<Tag>(p, pb[qb]);
+        pack16<Tag>(ds, sb[qb]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            accv[db] = mfma32(Tag{}, tr_frag<D>(gt, ta, qb * 32 + h * 16, db), pb[qb][h], accv[db]);
+            acck[db] = mfma32(Tag{}, tr_frag<D>(qt, ta, qb * 32 + h * 16, db), sb[qb][h], acck[db]);
+          }
     }
-    if (u + 1 < n_qtiles && tid < 64) lsd[slot ^ 1][tid / 32][tid % 32] = pf;
+    if (u + 1 < n_qtiles && tid < 2 * kBQ) lsd[slot ^ 1][tid / kBQ][tid % kBQ] = pf;
     wait_vmcnt<0>();
     barrier_lds();
   }
