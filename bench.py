@@ -7,9 +7,10 @@ the dense bf16 MFMA peak. One step is one forward pass of the whole path (workgr
 order, Q/K/V loads, both MFMA contractions, masking, online softmax, epilogue) over
 one batch of seeded synthetic inputs that are already resident in HBM.
 
-Prints ONE JSON line. Also reported, outside ``value``: the fp8 path on the fp8
-workload (B = 2, H = 16, N = 8192, d = 128, causal: quantiser and attention timed
-separately), and the CPU oracle timed on a bounded sample of the same bf16 workload.
+Prints ONE JSON line. Also reported, outside ``value``: the backward pass of the same
+bf16 workload (dQ, dK, dV from a seeded dO; 2.5 times the forward FLOPs), the fp8 path
+on the fp8 workload (B = 2, H = 16, N = 8192, d = 128, causal: quantiser and attention
+timed separately), and the CPU oracle timed on a bounded sample of the bf16 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -108,6 +109,23 @@ def cpu_baseline(q, k, v, causal, scale, budget_s):
                       f"workload, fp64 NumPy, {dt:.1f} s"}
 
 
+def backward_leg(torch, ea, inputs, w, tensors, o, lse, steps, warmup):
+    """The backward pass of the forward call just timed (same inputs, its O and LSE)."""
+    gq, gk, gv = tensors
+    g = inputs.to_torch(inputs.draw_dout(w.wid, w.B, w.H, w.N, w.d), "bf16").cuda()
+    ea.attn_fwd_bf16(gq, gk, gv, causal=True, scale=w.scale, out=o, lse=lse)
+    dq, dk, dv = (torch.empty_like(gq) for _ in range(3))
+    ws = torch.empty((2, w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ms = timed(lambda: ea.attn_bwd_bf16(gq, gk, gv, o, lse, g, causal=True, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                                        workspace=ws), steps, warmup, torch)
+    flops = 2.5 * counted_flops(w.B, w.H, w.N, w.d, True)
+    assert all(bool(torch.isfinite(t.float()).all()) for t in (dq, dk, dv))
+    return {"workload": "bf16 causal attention backward (dQ, dK, dV), B=2 H=16 N=8192 d=128",
+            "us": ms * 1e3, "tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "flop_convention": "2.5 x forward (five N x N x d contractions), halved for causal"}
+
+
 def fp8_leg(torch, ea, inputs, steps, warmup):
     import numpy as np
 
@@ -149,7 +167,7 @@ def main():
     # 100 untimed steps (~60 ms here) get there before the timed region starts.
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--no-extra", action="store_true", help="skip the fp8 leg")
+    ap.add_argument("--no-extra", action="store_true", help="skip the backward and fp8 legs")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB x 4 (HBM counter calibration) and exit")
@@ -210,6 +228,7 @@ def main():
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": read_counters()},
     }
     if not args.no_extra:
+        out["backward"] = backward_leg(torch, ea, inputs, w, (gq, gk, gv), o, lse, max(3, args.steps // 2), 3)
         out["fp8"] = fp8_leg(torch, ea, inputs, max(3, args.steps // 2), 1)
     if not args.no_cpu_baseline:
         qf, kf, vf = (t.float().numpy() for t in cpu)     # the bf16 values, upcast exactly

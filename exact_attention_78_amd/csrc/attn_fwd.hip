@@ -56,7 +56,6 @@ constexpr float kTau = 8.0f;   // lazy-rescale threshold for the running max, in
 template <typename Tag> struct Guard;
 template <> struct Guard<Bf16Tag> { static constexpr float value = 18446744073709551616.0f; };   // 2^64
 template <> struct Guard<F16Tag> { static constexpr float value = 32768.0f; };                  // 2^15
-constexpr int kFixupWorkgroups = 256;               // exact pass: one workgroup per CU
 
 // LDS swizzles: 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
 // K is read 32 rows x one chunk per instruction; V is read as 8 rows x 4 chunks
@@ -89,14 +88,11 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   // per head-dim step.
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];
   __shared__ int marked;                            // exact pass: this tile carries a mark
+  __shared__ int stop[2];                           // fast pass: some wave is marked (by step parity)
 
-  // One query tile (batch*head, m-tile) of the grid. The fast pass runs one tile per
-  // workgroup; the exact pass is a persistent grid that walks all tiles and redoes the
-  // marked ones.
-  auto tile = [&](const int logical) __attribute__((always_inline)) {
-    const int bh = logical / n_mtiles;
-    int mt = logical % n_mtiles;
-    if (CAUSAL) mt = n_mtiles - 1 - mt;               // longest query tiles first
+  // One query tile (batch*head, m-tile) per workgroup, in both passes; in the exact pass
+  // the workgroups of unmarked tiles leave at once.
+  auto tile = [&](const int bh, const int mt) __attribute__((always_inline)) {
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -110,16 +106,19 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     const int q0 = mt * BM + wave * 32;               // this wave's 32 rows; one per lane (and lane^32)
     const int qrow = q0 + l32;
     if constexpr (!FAST) {
-      // Exact pass: only query tiles that the fast pass marked (a NaN LSE) are redone. The
-      // first barrier also keeps the next tile's loads from overwriting LDS that a slower
-      // wave still reads for the previous one.
-      __syncthreads();
+      // Exact pass: only query tiles that the fast pass marked (a NaN LSE) are redone.
       if (tid == 0) marked = 0;
       __syncthreads();
       const bool mine = half == 0 && qrow < N && __builtin_isnan(LSE[(int64_t)bh * N + qrow]);
       if (__builtin_amdgcn_ballot_w64(mine) != 0 && lane == 0) marked = 1;
       __syncthreads();
       if (marked == 0) return;
+    }
+    if constexpr (FAST) {
+      if (tid == 0) {                                   // read only after the prologue's barriers
+        stop[0] = 0;
+        stop[1] = 0;
+      }
     }
     u32x4 qreg[NSTEP];                                // Q^T as the B operand, resident
 #pragma unroll
@@ -331,6 +330,10 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
         l_part += lt;
         if constexpr (FAST) ovf |= !(lt <= Guard<Tag>::value);
       }
+      if constexpr (FAST) {
+        // a marked wave dooms the whole query tile to the exact pass: say so to the others
+        if (__builtin_amdgcn_ballot_w64(ovf) != 0 && lane == 0) stop[t & 1] = 1;
+      }
       wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
       barrier_lds();
     };
@@ -361,11 +364,19 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     qk(IC<1>{}, Sb);
     barrier_lds();                 // K slots 0 and 1 are refilled from step 0 on
 
-    for (int t = 0; t < T; t += 4) {
+    int t_end = T;
+    for (int t = 0; t < t_end; t += 4) {
       step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{});
       if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{});
       if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{});
       if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{});
+      // Fast pass: once some wave is marked, the tile is left to the exact pass. stop[1]
+      // was last written in step t+3 (or t+1) before its barrier and is next written in
+      // step t+5, after the barrier of step t+4, so every wave reads the same value here
+      // and all leave the loop together.
+      if constexpr (FAST) {
+        if (stop[1] != 0) t_end = t + 4;
+      }
     }
     wait_vmcnt<0>();               // no load may still target this workgroup's LDS when it exits
     if (pend) rescale_o();
@@ -390,11 +401,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     }
     if (half == 0) LSE[(int64_t)bh * N + qrow] = lse;
   };
-  if constexpr (FAST) {
-    tile(xcd_logical_id(blockIdx.x, total_wg));
-  } else {
-    for (int lg = blockIdx.x; lg < total_wg; lg += gridDim.x) tile(lg);
-  }
+  const int logical = xcd_logical_id(blockIdx.x, total_wg);
+  const int m = logical % n_mtiles;
+  tile(logical / n_mtiles, CAUSAL ? n_mtiles - 1 - m : m);   // longest query tiles first
 }
 
 template <typename Tag, int D, bool CAUSAL>
@@ -406,8 +415,7 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
   hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, kWaves, true>), dim3((unsigned)total), dim3(kWaves * 64), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
                      n_mtiles, (int)total, scale * kLog2e);
-  const int64_t fixup_wg = total < kFixupWorkgroups ? total : kFixupWorkgroups;
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, kWaves, false>), dim3((unsigned)fixup_wg), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, kWaves, false>), dim3((unsigned)total), dim3(kWaves * 64), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
                      n_mtiles, (int)total, scale * kLog2e);
   return hipGetLastError();

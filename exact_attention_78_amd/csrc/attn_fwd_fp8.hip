@@ -36,16 +36,8 @@ constexpr int kBN = 64;
 constexpr int kWaves = 8;
 constexpr int kBM = kWaves * 32;
 constexpr int kScaleRows = 128;
-constexpr float kPShift = 6.0f;   // exact pass: P' = 2^6 * P
-constexpr float kTau = 2.0f;      // exact pass: lazy-rescale threshold (log2 units): P' <= 2^(6+2) = 256
-// Two launches per call. The fast pass keeps the first tile's row max M0 as the softmax
-// reference for every tile (no per-tile max, no running-max rescale) and uses
-// P' = 2^2 * 2^(s - M0), so that scores up to ~6.8 (log2 units) above M0 still fit E4M3.
-// It checks per tile that the sum of a lane's P' (an upper bound of each of them) stays
-// within the E4M3 range (448); a wave where that fails marks its rows' LSE with NaN, and
-// the exact pass (lazy per-tile max, P' = 2^6 * P) redoes every marked query tile.
-constexpr float kPShiftFast = 2.0f;
-constexpr int kFixupWorkgroups = 256;
+constexpr float kPShift = 6.0f;   // P' = 2^6 * P
+constexpr float kTau = 2.0f;      // lazy-rescale threshold (log2 units): P' <= 2^(6+2) = 256
 static_assert(kScaleRows % kBN == 0 && kBM % kScaleRows == 0, "tiles nest inside scale blocks");
 
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
@@ -65,7 +57,7 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
 // tiles use the same swizzle. It depends on row bits 1..3 only.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-template <bool CAUSAL, bool FAST>
+template <bool CAUSAL>
 __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
@@ -79,343 +71,304 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   static_assert(LPW == 1, "one direct load per wave per tile");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];   // K ring, then V ring
 
-  __shared__ int marked;                            // exact pass: this tile carries a mark
+  const int logical = xcd_logical_id(blockIdx.x, total_wg);
+  const int bh = logical / n_mtiles;
+  int mt = logical % n_mtiles;
+  if (CAUSAL) mt = n_mtiles - 1 - mt;                // longest query tiles first
 
-  // One query tile (batch*head, m-tile) of the grid. The fast pass runs one tile per
-  // workgroup; the exact pass is a persistent grid that walks all tiles and redoes the
-  // marked ones.
-  auto tile = [&](const int logical) __attribute__((always_inline)) {
-    const int bh = logical / n_mtiles;
-    int mt = logical % n_mtiles;
-    if (CAUSAL) mt = n_mtiles - 1 - mt;                // longest query tiles first
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64;
+  const int half = lane / 32, l32 = lane % 32;
+  const int64_t head_off = (int64_t)bh * N * kD;
+  const uint8_t* Qh = Q + head_off;
+  const uint8_t* Kh = K + head_off;
+  const uint8_t* Vh = V + head_off;
+  const float* sk = SK + (int64_t)bh * nblk;
+  const float* sv = SV + (int64_t)bh * nblk;
 
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int lane = tid % 64;
-    const int half = lane / 32, l32 = lane % 32;
-    const int64_t head_off = (int64_t)bh * N * kD;
-    const uint8_t* Qh = Q + head_off;
-    const uint8_t* Kh = K + head_off;
-    const uint8_t* Vh = V + head_off;
-    const float* sk = SK + (int64_t)bh * nblk;
-    const float* sv = SV + (int64_t)bh * nblk;
+  const int q0 = mt * kBM + wave * 32;               // this wave's 32 rows (inside one Q scale block)
+  const int qrow = q0 + l32;
+  const float cq = c_base * SQ[(int64_t)bh * nblk + min(q0 / kScaleRows, nblk - 1)];
 
-    const int q0 = mt * kBM + wave * 32;               // this wave's 32 rows (inside one Q scale block)
-    const int qrow = q0 + l32;
-    if constexpr (!FAST) {
-      // Exact pass: only query tiles that the fast pass marked (a NaN LSE) are redone. The
-      // first barrier also keeps the next tile's loads from overwriting LDS that a slower
-      // wave still reads for the previous one.
-      __syncthreads();
-      if (tid == 0) marked = 0;
-      __syncthreads();
-      const bool mine = half == 0 && qrow < N && __builtin_isnan(LSE[(int64_t)bh * N + qrow]);
-      if (__builtin_amdgcn_ballot_w64(mine) != 0 && lane == 0) marked = 1;
-      __syncthreads();
-      if (marked == 0) return;
+  // Q^T as the B operand: for MFMA m (head-dim half), bytes [m*64 + half*32, +32) of the row.
+  i32x8 qreg[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    if (qrow < N) {
+      const i32x4 a = *(const i32x4*)(Qh + (int64_t)qrow * kD + m * 64 + half * 32);
+      const i32x4 b = *(const i32x4*)(Qh + (int64_t)qrow * kD + m * 64 + half * 32 + 16);
+      qreg[m] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    } else {
+      qreg[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    const float cq = c_base * SQ[(int64_t)bh * nblk + min(q0 / kScaleRows, nblk - 1)];
+  }
 
-    // Q^T as the B operand: for MFMA m (head-dim half), bytes [m*64 + half*32, +32) of the row.
-    i32x8 qreg[2];
-  #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (qrow < N) {
-        const i32x4 a = *(const i32x4*)(Qh + (int64_t)qrow * kD + m * 64 + half * 32);
-        const i32x4 b = *(const i32x4*)(Qh + (int64_t)qrow * kD + m * 64 + half * 32 + 16);
-        qreg[m] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  const int n_ktiles = (N + kBN - 1) / kBN;
+  const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * kBM + kBN - 1) / kBN) : n_ktiles;
+
+  // K fragment (kb, m): row kb*32 + l32, chunks m*4 + half*2 and +1 (32 bytes).
+  uint32_t kaddr[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) kaddr[m] = l32 * ROW + (((m * 4 + half * 2) ^ swz(l32)) << 4);
+  // V^T fragment (db): four 8-byte transpose reads; read m covers the keys
+  // (m/2)*32 + ((m%2)*2 + j/4)*8 + tr_h*4 + j%4, the order of this lane's P bytes. The
+  // row offsets of m (multiples of 16) leave the swizzle unchanged.
+  const int g16 = lane / 16, i16 = lane % 16;
+  const int tr_h = g16 / 2, tr_j = i16 >> 1;
+  const int tr_row = (tr_j / 4) * 8 + tr_h * 4 + (tr_j % 4);
+  const int tr_col = 16 * (g16 % 2) + 8 * (i16 & 1);
+  uint32_t vaddr[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int col = db * 32 + tr_col;
+    vaddr[db] = tr_row * ROW + (((col >> 4) ^ swz(tr_row)) << 4) + (col & 15);
+  }
+
+  // Direct global -> LDS loads: wave w fills bytes [w*1024, +1024) of a tile, 16 per lane.
+  const int ld_slot = wave * 1024 + lane * 16;
+  const int ld_row = ld_slot / ROW;
+  const int ld_ch = ((ld_slot % ROW) / 16) ^ swz(ld_row);
+  const int ld_off = ld_row * ROW + ld_ch * 16;
+  auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* { return lds + decltype(SLOT)::value * TB; };
+  auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* {
+    return lds + (NS + decltype(SLOT)::value) * TB;
+  };
+  auto load_tile = [&](const uint8_t* src, int kt, uint8_t* dst) __attribute__((always_inline)) {
+    if (kt * kBN + kBN <= N) {
+      dma_load16(src + (int64_t)kt * TB + ld_off, lds_u32(dst) + wave * 1024);
+    } else {   // rows past the end re-read the last row (masked scores, P = 0)
+      const int key = min(kt * kBN + ld_row, N - 1);
+      dma_load16(src + (int64_t)key * ROW + ld_ch * 16, lds_u32(dst) + wave * 1024);
+    }
+  };
+  auto kfrag = [&](const uint8_t* kb_base, int kb, int m) __attribute__((always_inline)) -> i32x8 {
+    const uint8_t* p = kb_base + kb * 32 * ROW + kaddr[m];
+    const i32x4 a0 = *(const i32x4*)p;
+    const i32x4 a1 = *(const i32x4*)(kb_base + kb * 32 * ROW + (kaddr[m] ^ 16));
+    return i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  };
+  auto qk = [&](auto SLOT, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      S[kb] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) S[kb] = mfma_fp8(kfrag(kbuf(SLOT), kb, m), qreg[m], S[kb]);
+    }
+  };
+
+  f32x16 oacc[NDB], lacc = f32x16{};   // P'.V (in units of the current V scale) and sum of rounded P'
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  // Running max M (log2 units), this lane's partial row sum of the unrounded
+  // probabilities (for the LSE), and a pending rescale factor of the accumulators.
+  float M = -INFINITY, l_part = 0.f, alpha_pend = 1.f;
+  float sv_units = 1.f;      // the V block scale the P.V accumulator is expressed in
+
+  // Per-tile constants of tile u: score factor and V block scale.
+  auto tile_c = [&](int u) __attribute__((always_inline)) { return cq * sk[min(u * kBN / kScaleRows, nblk - 1)]; };
+  auto tile_sv = [&](int u) __attribute__((always_inline)) { return sv[min(u * kBN / kScaleRows, nblk - 1)]; };
+
+  auto mask_tile = [&](int u, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
+    const int key0 = u * kBN;
+    if ((CAUSAL && key0 + kBN - 1 > q0) || key0 + kBN > N) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
+          if ((CAUSAL && key > qrow) || key >= N) S[kb][r] = -INFINITY;
+        }
+    }
+  };
+  auto max_pairs = [&](float (&m4)[4], const f32x16 (&S)[NKB], int e_begin, int e_end) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = e_begin; e < e_end; e += 2)
+      m4[(e / 2) % 4] = max3f(m4[(e / 2) % 4], S[e / 16][e % 16], S[e / 16][e % 16 + 1]);
+  };
+  // Raise M when some row of the wave grew by more than kTau (branch-free); l is
+  // rescaled at once, O at the start of the next step. Returns whether M moved.
+  auto max_final = [&](const float (&m4)[4], float ct) __attribute__((always_inline)) -> bool {
+    const float mx = max_halves(max3f(m4[0], m4[1], __builtin_elementwise_maximum(m4[2], m4[3]))) * ct;
+    const bool grow = __builtin_amdgcn_ballot_w64(mx > M + kTau) != 0;
+    const float M_new = grow ? __builtin_elementwise_maximum(M, mx) : M;
+    const float alpha = grow ? fast_exp2(M - M_new) : 1.f;
+    M = M_new;
+    l_part *= alpha;
+    alpha_pend *= alpha;
+    return grow;
+  };
+  // P' of scores [e0, e1), in three passes issued apart so that no VALU op waits on the
+  // one before it: the exp2 arguments (args), the exponentials, written over the scores
+  // (exps), then the row sums (two chains) and the rounding to E4M3, four per word (finish).
+  auto args = [&](f32x16 (&S)[NKB], float ct, float bias, int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = __builtin_fmaf(S[e / 16][e % 16], ct, -bias);
+  };
+  auto exps = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = fast_exp2(S[e / 16][e % 16]);
+  };
+  auto finish = [&](const f32x16 (&S)[NKB], int (&P)[8], float (&lsum)[2], int e0, int e1)
+                    __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) {
+      const float pe = S[e / 16][e % 16];
+      lsum[e % 2] += pe;
+      if (e % 4 == 1) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(S[e / 16][e % 16 - 1], pe, 0, false);
+      if (e % 4 == 3) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(S[e / 16][e % 16 - 1], pe, P[e / 4], true);
+    }
+  };
+  // Owed running-max rescale, and (at the first tile of a V scale block) the change of
+  // V units sv_old / sv_new of the P.V accumulator.
+  auto rescale = [&](float sv_ratio) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha_pend * sv_ratio;
+    lacc *= alpha_pend;
+    alpha_pend = 1.f;
+  };
+
+  f32x16 Sa[NKB], Sb[NKB];
+  int Pa[8], Pb[8];
+  bool pend = false;     // wave-uniform: an O rescale is owed
+
+  // Step t: S(t+1) in S_soft, S(t+2) -> S_new, P(t) in P_use, P(t+1) -> P_new;
+  // K(t+2) in K slot (t+2)%4, V(t) in V slot t%4; loads K(t+4) -> K slot t%4 and
+  // V(t+3) -> V slot (t+3)%4 (clamped past the last tile, never read; the scores of tile
+  // T, if computed, are fully masked).
+  auto step = [&](int t, f32x16 (&S_soft)[NKB], f32x16 (&S_new)[NKB], const int (&P_use)[8], int (&P_new)[8],
+                  auto KRD, auto VRD, auto KLD, auto VLD) __attribute__((always_inline)) {
+    load_tile(Kh, min(t + 4, T - 1), kbuf(KLD));
+    load_tile(Vh, min(t + 3, T - 1), vbuf(VLD));
+    static_assert(kScaleRows == 2 * kBN, "a V scale block spans two tiles");
+    // Causal: once the tile's first key lies past this wave's last row, this and every
+    // later tile are fully masked for the wave; it only keeps up its loads and barriers.
+    if (!CAUSAL || t * kBN <= q0 + 31) {
+      if constexpr (decltype(VRD)::value % 2 == 0) {   // t even: tile t opens a V scale block
+        const float sv_new = tile_sv(t);
+        rescale(t > 0 ? sv_units * __builtin_amdgcn_rcpf(sv_new) : 1.f);
+        sv_units = sv_new;
       } else {
-        qreg[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (pend) rescale(1.f);
       }
-    }
-
-    const int n_ktiles = (N + kBN - 1) / kBN;
-    const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * kBM + kBN - 1) / kBN) : n_ktiles;
-
-    // K fragment (kb, m): row kb*32 + l32, chunks m*4 + half*2 and +1 (32 bytes).
-    uint32_t kaddr[2];
-  #pragma unroll
-    for (int m = 0; m < 2; ++m) kaddr[m] = l32 * ROW + (((m * 4 + half * 2) ^ swz(l32)) << 4);
-    // V^T fragment (db): four 8-byte transpose reads; read m covers the keys
-    // (m/2)*32 + ((m%2)*2 + j/4)*8 + tr_h*4 + j%4, the order of this lane's P bytes. The
-    // row offsets of m (multiples of 16) leave the swizzle unchanged.
-    const int g16 = lane / 16, i16 = lane % 16;
-    const int tr_h = g16 / 2, tr_j = i16 >> 1;
-    const int tr_row = (tr_j / 4) * 8 + tr_h * 4 + (tr_j % 4);
-    const int tr_col = 16 * (g16 % 2) + 8 * (i16 & 1);
-    uint32_t vaddr[NDB];
-  #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int col = db * 32 + tr_col;
-      vaddr[db] = tr_row * ROW + (((col >> 4) ^ swz(tr_row)) << 4) + (col & 15);
-    }
-
-    // Direct global -> LDS loads: wave w fills bytes [w*1024, +1024) of a tile, 16 per lane.
-    const int ld_slot = wave * 1024 + lane * 16;
-    const int ld_row = ld_slot / ROW;
-    const int ld_ch = ((ld_slot % ROW) / 16) ^ swz(ld_row);
-    const int ld_off = ld_row * ROW + ld_ch * 16;
-    auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* { return lds + decltype(SLOT)::value * TB; };
-    auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* {
-      return lds + (NS + decltype(SLOT)::value) * TB;
-    };
-    auto load_tile = [&](const uint8_t* src, int kt, uint8_t* dst) __attribute__((always_inline)) {
-      if (kt * kBN + kBN <= N) {
-        dma_load16(src + (int64_t)kt * TB + ld_off, lds_u32(dst) + wave * 1024);
-      } else {   // rows past the end re-read the last row (masked scores, P = 0)
-        const int key = min(kt * kBN + ld_row, N - 1);
-        dma_load16(src + (int64_t)key * ROW + ld_ch * 16, lds_u32(dst) + wave * 1024);
-      }
-    };
-    auto kfrag = [&](const uint8_t* kb_base, int kb, int m) __attribute__((always_inline)) -> i32x8 {
-      const uint8_t* p = kb_base + kb * 32 * ROW + kaddr[m];
-      const i32x4 a0 = *(const i32x4*)p;
-      const i32x4 a1 = *(const i32x4*)(kb_base + kb * 32 * ROW + (kaddr[m] ^ 16));
-      return i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    };
-    auto qk = [&](auto SLOT, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
-  #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        S[kb] = f32x16{};
-  #pragma unroll
-        for (int m = 0; m < 2; ++m) S[kb] = mfma_fp8(kfrag(kbuf(SLOT), kb, m), qreg[m], S[kb]);
-      }
-    };
-
-    f32x16 oacc[NDB], lacc = f32x16{};   // P'.V (in units of the current V scale) and sum of rounded P'
-  #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-    // Running max M (log2 units), this lane's partial row sum of the unrounded
-    // probabilities (for the LSE), and a pending rescale factor of the accumulators.
-    float M = -INFINITY, l_part = 0.f, alpha_pend = 1.f;
-    float sv_units = 1.f;      // the V block scale the P.V accumulator is expressed in
-    bool ovf = false;          // fast pass: some tile's row sum of P' passed the E4M3 range guard
-
-    // Per-tile constants of tile u: score factor and V block scale.
-    auto tile_c = [&](int u) __attribute__((always_inline)) { return cq * sk[min(u * kBN / kScaleRows, nblk - 1)]; };
-    auto tile_sv = [&](int u) __attribute__((always_inline)) { return sv[min(u * kBN / kScaleRows, nblk - 1)]; };
-
-    auto mask_tile = [&](int u, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
-      const int key0 = u * kBN;
-      if ((CAUSAL && key0 + kBN - 1 > q0) || key0 + kBN > N) {
-  #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kb * 32 + (r / 4) * 8 + half * 4 + (r % 4);
-            if ((CAUSAL && key > qrow) || key >= N) S[kb][r] = -INFINITY;
-          }
-      }
-    };
-    auto max_pairs = [&](float (&m4)[4], const f32x16 (&S)[NKB], int e_begin, int e_end) __attribute__((always_inline)) {
-  #pragma unroll
-      for (int e = e_begin; e < e_end; e += 2)
-        m4[(e / 2) % 4] = max3f(m4[(e / 2) % 4], S[e / 16][e % 16], S[e / 16][e % 16 + 1]);
-    };
-    // Raise M when some row of the wave grew by more than kTau (branch-free); l is
-    // rescaled at once, O at the start of the next step. Returns whether M moved.
-    auto max_final = [&](const float (&m4)[4], float ct) __attribute__((always_inline)) -> bool {
-      const float mx = max_halves(max3f(m4[0], m4[1], __builtin_elementwise_maximum(m4[2], m4[3]))) * ct;
-      const bool grow = __builtin_amdgcn_ballot_w64(mx > M + kTau) != 0;
-      const float M_new = grow ? __builtin_elementwise_maximum(M, mx) : M;
-      const float alpha = grow ? fast_exp2(M - M_new) : 1.f;
-      M = M_new;
-      l_part *= alpha;
-      alpha_pend *= alpha;
-      return grow;
-    };
-    // P' of scores [e0, e1), in three passes issued apart so that no VALU op waits on the
-    // one before it: the exp2 arguments (args), the exponentials, written over the scores
-    // (exps), then the row sums (two chains) and the rounding to E4M3, four per word (finish).
-    auto args = [&](f32x16 (&S)[NKB], float ct, float bias, int e0, int e1) __attribute__((always_inline)) {
-  #pragma unroll
-      for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = __builtin_fmaf(S[e / 16][e % 16], ct, -bias);
-    };
-    auto exps = [&](f32x16 (&S)[NKB], int e0, int e1) __attribute__((always_inline)) {
-  #pragma unroll
-      for (int e = e0; e < e1; ++e) S[e / 16][e % 16] = fast_exp2(S[e / 16][e % 16]);
-    };
-    auto finish = [&](const f32x16 (&S)[NKB], int (&P)[8], float (&lsum)[2], int e0, int e1)
-                      __attribute__((always_inline)) {
-  #pragma unroll
-      for (int e = e0; e < e1; ++e) {
-        const float pe = S[e / 16][e % 16];
-        lsum[e % 2] += pe;
-        if (e % 4 == 1) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(S[e / 16][e % 16 - 1], pe, 0, false);
-        if (e % 4 == 3) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(S[e / 16][e % 16 - 1], pe, P[e / 4], true);
-      }
-    };
-    // Owed running-max rescale, and (at the first tile of a V scale block) the change of
-    // V units sv_old / sv_new of the P.V accumulator.
-    auto rescale = [&](float sv_ratio) __attribute__((always_inline)) {
-  #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha_pend * sv_ratio;
-      lacc *= alpha_pend;
-      alpha_pend = 1.f;
-    };
-
-    f32x16 Sa[NKB], Sb[NKB];
-    int Pa[8], Pb[8];
-    bool pend = false;     // wave-uniform: an O rescale is owed
-
-    // Step t: S(t+1) in S_soft, S(t+2) -> S_new, P(t) in P_use, P(t+1) -> P_new;
-    // K(t+2) in K slot (t+2)%4, V(t) in V slot t%4; loads K(t+4) -> K slot t%4 and
-    // V(t+3) -> V slot (t+3)%4 (clamped past the last tile, never read; the scores of tile
-    // T, if computed, are fully masked).
-    auto step = [&](int t, f32x16 (&S_soft)[NKB], f32x16 (&S_new)[NKB], const int (&P_use)[8], int (&P_new)[8],
-                    auto KRD, auto VRD, auto KLD, auto VLD) __attribute__((always_inline)) {
-      load_tile(Kh, min(t + 4, T - 1), kbuf(KLD));
-      load_tile(Vh, min(t + 3, T - 1), vbuf(VLD));
-      static_assert(kScaleRows == 2 * kBN, "a V scale block spans two tiles");
-      // Causal: once the tile's first key lies past this wave's last row, this and every
-      // later tile are fully masked for the wave; it only keeps up its loads and barriers.
-      if (!CAUSAL || t * kBN <= q0 + 31) {
-        if constexpr (decltype(VRD)::value % 2 == 0) {   // t even: tile t opens a V scale block
-          const float sv_new = tile_sv(t);
-          rescale(t > 0 ? sv_units * __builtin_amdgcn_rcpf(sv_new) : 1.f);
-          sv_units = sv_new;
-        } else if constexpr (!FAST) {
-          if (pend) rescale(1.f);
+      mask_tile(t + 1, S_soft);
+      const float ct = tile_c(t + 1);
+      // Main block in issue order: 4 S^T MFMAs (K fragments one MFMA ahead) and 4 P.V
+      // MFMAs (V^T fragments one MFMA ahead); the row max runs beside the first two S^T
+      // MFMAs, the exponentials beside the other six.
+      i32x8 kf[4], vf[NDB];
+      auto kread = [&](int i) __attribute__((always_inline)) { kf[i] = kfrag(kbuf(KRD), i % NKB, i / NKB); };
+      auto vread = [&](int db) __attribute__((always_inline)) {
+        int av[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const i32x2 x = lds_read_tr8(vbuf(VRD) + ((m / 2) * 32 + (m % 2) * 16) * ROW + vaddr[db]);
+          av[2 * m] = x[0];
+          av[2 * m + 1] = x[1];
         }
-        mask_tile(t + 1, S_soft);
-        const float ct = tile_c(t + 1);
-        // Main block in issue order: 4 S^T MFMAs (K fragments one MFMA ahead) and 4 P.V
-        // MFMAs (V^T fragments one MFMA ahead); (exact pass) the row max runs beside the
-        // first two S^T MFMAs, the exponentials beside the other six; (fast pass) the
-        // exponentials beside the last seven.
-        i32x8 kf[4], vf[NDB];
-        auto kread = [&](int i) __attribute__((always_inline)) { kf[i] = kfrag(kbuf(KRD), i % NKB, i / NKB); };
-        auto vread = [&](int db) __attribute__((always_inline)) {
-          int av[8];
-  #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const i32x2 x = lds_read_tr8(vbuf(VRD) + ((m / 2) * 32 + (m % 2) * 16) * ROW + vaddr[db]);
-            av[2 * m] = x[0];
-            av[2 * m + 1] = x[1];
-          }
-          vf[db] = i32x8{av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
-        };
-        float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
-        float lsum[2] = {0.f, 0.f}, bias = FAST ? M - kPShiftFast : 0.f;
-        // the slots (exact pass: S^T MFMAs 2, 3 and the four P.V MFMAs; fast pass: also S^T
-        // MFMA 1) share the 32 scores; slot k issues the arguments of slot k+1, the
-        // exponentials of slot k and the sums of slot k-1
-        constexpr int NSLOT = FAST ? 7 : 6;
-        auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
-        auto exps_slot = [&](int slot) __attribute__((always_inline)) {
-          if (slot + 1 < NSLOT) args(S_soft, ct, bias, lo(slot + 1), lo(slot + 2));
-          exps(S_soft, lo(slot), lo(slot + 1));
-          if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
-        };
-        kread(0);
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) {               // i = m * NKB + kb
-          if (i + 1 < 4) kread(i + 1);
-          else vread(0);
-          const int kb = i % NKB, m = i / NKB;
-          S_new[kb] = mfma_fp8(kf[i], qreg[m], m == 0 ? f32x16{} : S_new[kb]);
-          if constexpr (FAST) {
-            if (i == 0) args(S_soft, ct, bias, lo(0), lo(1));
-            else exps_slot(i - 1);
-          } else {
-            if (i == 0) {
-              max_pairs(m4, S_soft, 4, 18);
-            } else if (i == 1) {
-              max_pairs(m4, S_soft, 18, NKB * 16);
-              pend = max_final(m4, ct);
-              bias = M - kPShift;
-              args(S_soft, ct, bias, lo(0), lo(1));
-            } else {
-              exps_slot(i - 2);
-            }
-          }
+        vf[db] = i32x8{av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
+      };
+      float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
+      float lsum[2] = {0.f, 0.f}, bias = 0.f;
+      // six slots (S^T MFMAs 2, 3 and the four P.V MFMAs) share the 32 scores; slot k issues
+      // the arguments of slot k+1, the exponentials of slot k and the sums of slot k-1
+      constexpr int NSLOT = 6;
+      auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
+      auto exps_slot = [&](int slot) __attribute__((always_inline)) {
+        if (slot + 1 < NSLOT) args(S_soft, ct, bias, lo(slot + 1), lo(slot + 2));
+        exps(S_soft, lo(slot), lo(slot + 1));
+        if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
+      };
+      kread(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {               // i = m * NKB + kb
+        if (i + 1 < 4) kread(i + 1);
+        else vread(0);
+        const int kb = i % NKB, m = i / NKB;
+        S_new[kb] = mfma_fp8(kf[i], qreg[m], m == 0 ? f32x16{} : S_new[kb]);
+        if (i == 0) {
+          max_pairs(m4, S_soft, 4, 18);
+        } else if (i == 1) {
+          max_pairs(m4, S_soft, 18, NKB * 16);
+          pend = max_final(m4, ct);
+          bias = M - kPShift;
+          args(S_soft, ct, bias, lo(0), lo(1));
+        } else {
+          exps_slot(i - 2);
         }
-  #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          if (db + 1 < NDB) vread(db + 1);
-          const i32x8 pb = {P_use[0], P_use[1], P_use[2], P_use[3], P_use[4], P_use[5], P_use[6], P_use[7]};
-          oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
-          if (db == NDB - 1) {
-            // all-ones A operand (E4M3 1.0), built here from a value tied to t so that it is
-            // not kept live across the loop (t < 2^30, so the shift adds 0)
-            const int one4 = 0x38383838 + (t >> 30);
-            lacc = mfma_fp8(i32x8{one4, one4, one4, one4, one4, one4, one4, one4}, pb, lacc);
-          }
-          exps_slot(NSLOT - NDB + db);
-        }
-        finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
-        const float ls = lsum[0] + lsum[1];
-        l_part += ls;
-        // every P' of this lane's 32 scores is at most their sum: a sum within the E4M3
-        // range keeps each code finite
-        if constexpr (FAST) ovf |= !(ls <= 448.f);
       }
-      wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
-      barrier_lds();
-    };
-
-    // Prologue: K tiles 0..3 and V tiles 0..2; S(0), softmax of tile 0, S(1).
-    load_tile(Kh, 0, kbuf(IC<0>{}));
-    load_tile(Kh, min(1, T - 1), kbuf(IC<1>{}));
-    load_tile(Kh, min(2, T - 1), kbuf(IC<2>{}));
-    load_tile(Kh, min(3, T - 1), kbuf(IC<3>{}));
-    load_tile(Vh, 0, vbuf(IC<0>{}));
-    load_tile(Vh, min(1, T - 1), vbuf(IC<1>{}));
-    load_tile(Vh, min(2, T - 1), vbuf(IC<2>{}));
-    wait_vmcnt<0>();
-    barrier_lds();
-    qk(IC<0>{}, Sa);
-    {
-      mask_tile(0, Sa);
-      const float ct = tile_c(0);
-      float m4[4] = {Sa[0][0], Sa[0][1], Sa[0][2], Sa[0][3]};
-      max_pairs(m4, Sa, 4, NKB * 16);
-      max_final(m4, ct);
-      alpha_pend = 1.f;            // O is still zero: no rescale owed
-      const float bias = M - (FAST ? kPShiftFast : kPShift);
-      float lsum[2] = {0.f, 0.f};
-      args(Sa, ct, bias, 0, NKB * 16);
-      exps(Sa, 0, NKB * 16);
-      finish(Sa, Pa, lsum, 0, NKB * 16);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        if (db + 1 < NDB) vread(db + 1);
+        const i32x8 pb = {P_use[0], P_use[1], P_use[2], P_use[3], P_use[4], P_use[5], P_use[6], P_use[7]};
+        oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
+        if (db == NDB - 1) {
+          // all-ones A operand (E4M3 1.0), built here from a value tied to t so that it is
+          // not kept live across the loop (t < 2^30, so the shift adds 0)
+          const int one4 = 0x38383838 + (t >> 30);
+          lacc = mfma_fp8(i32x8{one4, one4, one4, one4, one4, one4, one4, one4}, pb, lacc);
+        }
+        exps_slot(2 + db);
+      }
+      finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
       l_part += lsum[0] + lsum[1];
     }
-    qk(IC<1>{}, Sb);
-    barrier_lds();                 // K slots 0 and 1 are refilled from step 0 on
-
-    for (int t = 0; t < T; t += 4) {
-      step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{});
-      if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{});
-      if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{});
-      if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{});
-    }
-    wait_vmcnt<0>();               // no load may still target this workgroup's LDS when it exits
-    if (pend) rescale(1.f);
-
-    const float l_tot = add_halves(l_part) * (1.f / (1 << (int)(FAST ? kPShiftFast : kPShift)));   // sum of probabilities
-    if (qrow >= N) return;
-    const float inv = sv_units / lacc[0];
-    uint16_t* Orow = O + head_off + (int64_t)qrow * kD;
-  #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-  #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + g * 8 + half * 4;
-        const f32x16 a = oacc[db];
-        u32x2 w = {pack2(Bf16Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv),
-                   pack2(Bf16Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
-        *(u32x2*)(Orow + d) = w;
-      }
-    float lse = (M + __builtin_log2f(l_tot)) * kLn2;
-    if constexpr (FAST) {
-      if (__builtin_amdgcn_ballot_w64(ovf) != 0) lse = __builtin_nanf("");   // mark: redo in the exact pass
-    }
-    if (half == 0) LSE[(int64_t)bh * N + qrow] = lse;
+    wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
+    barrier_lds();
   };
-  if constexpr (FAST) {
-    tile(xcd_logical_id(blockIdx.x, total_wg));
-  } else {
-    for (int lg = blockIdx.x; lg < total_wg; lg += gridDim.x) tile(lg);
+
+  // Prologue: K tiles 0..3 and V tiles 0..2; S(0), softmax of tile 0, S(1).
+  load_tile(Kh, 0, kbuf(IC<0>{}));
+  load_tile(Kh, min(1, T - 1), kbuf(IC<1>{}));
+  load_tile(Kh, min(2, T - 1), kbuf(IC<2>{}));
+  load_tile(Kh, min(3, T - 1), kbuf(IC<3>{}));
+  load_tile(Vh, 0, vbuf(IC<0>{}));
+  load_tile(Vh, min(1, T - 1), vbuf(IC<1>{}));
+  load_tile(Vh, min(2, T - 1), vbuf(IC<2>{}));
+  wait_vmcnt<0>();
+  barrier_lds();
+  qk(IC<0>{}, Sa);
+  {
+    mask_tile(0, Sa);
+    const float ct = tile_c(0);
+    float m4[4] = {Sa[0][0], Sa[0][1], Sa[0][2], Sa[0][3]};
+    max_pairs(m4, Sa, 4, NKB * 16);
+    max_final(m4, ct);
+    alpha_pend = 1.f;            // O is still zero: no rescale owed
+    const float bias = M - kPShift;
+    float lsum[2] = {0.f, 0.f};
+    args(Sa, ct, bias, 0, NKB * 16);
+    exps(Sa, 0, NKB * 16);
+    finish(Sa, Pa, lsum, 0, NKB * 16);
+    l_part += lsum[0] + lsum[1];
   }
+  qk(IC<1>{}, Sb);
+  barrier_lds();                 // K slots 0 and 1 are refilled from step 0 on
+
+  for (int t = 0; t < T; t += 4) {
+    step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{});
+    if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{});
+    if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{});
+    if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{});
+  }
+  wait_vmcnt<0>();               // no load may still target this workgroup's LDS when it exits
+  if (pend) rescale(1.f);
+
+  const float l_tot = add_halves(l_part) * (1.f / (1 << (int)kPShift));   // sum of probabilities
+  if (qrow >= N) return;
+  const float inv = sv_units / lacc[0];
+  uint16_t* Orow = O + head_off + (int64_t)qrow * kD;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + g * 8 + half * 4;
+      const f32x16 a = oacc[db];
+      u32x2 w = {pack2(Bf16Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv),
+                 pack2(Bf16Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
+      *(u32x2*)(Orow + d) = w;
+    }
+  if (half == 0) LSE[(int64_t)bh * N + qrow] = (M + __builtin_log2f(l_tot)) * kLn2;
 }
 
 template <bool CAUSAL>
@@ -424,11 +377,8 @@ hipError_t launch(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const
   const int n_mtiles = (int)((N + kBM - 1) / kBM);
   const int nblk = (int)((N + kScaleRows - 1) / kScaleRows);
   const int64_t total = BH * n_mtiles;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, true>), dim3((unsigned)total), dim3(kWaves * 64), 0, stream, q8, k8,
-                     v8, sq, sk, sv, (uint16_t*)o, lse, (int)N, n_mtiles, nblk, (int)total, scale * kLog2e);
-  const int64_t fixup_wg = total < kFixupWorkgroups ? total : kFixupWorkgroups;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, false>), dim3((unsigned)fixup_wg), dim3(kWaves * 64), 0, stream, q8,
-                     k8, v8, sq, sk, sv, (uint16_t*)o, lse, (int)N, n_mtiles, nblk, (int)total, scale * kLog2e);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL>), dim3((unsigned)total), dim3(kWaves * 64), 0, stream, q8, k8, v8,
+                     sq, sk, sv, (uint16_t*)o, lse, (int)N, n_mtiles, nblk, (int)total, scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -83,13 +83,10 @@ attn_status_t attn_fwd_f32(const float* q, const float* k, const float* v, float
  * fp32 scales of each 128-row block, so the value of a code x in block t is
  * decode(x) * scale[b, h, t]. O is bf16 [B, H, N, d], LSE fp32 [B, H, N]. Scores
  * accumulate e4m3 x e4m3 products in fp32 and are scaled by q_scale * k_scale * scale;
- * the probabilities enter the P.V contraction (fp32 accumulation) as E4M3 codes, and O
- * is divided by the sum of those rounded codes while the LSE uses the unrounded fp32 sum.
- * The call enqueues two kernels on `stream`: the first codes 2^2 * 2^(s - M0) against the
- * first key tile's row max M0 and marks every query tile where a code could pass the
- * E4M3 range (448); the second redoes the marked tiles with codes of 2^6 * P relative to
- * a running max that trails the true one by at most 2 (log2 units), so codes stay <= 256.
- * O and LSE are complete when both have run. All scales must be finite and > 0. */
+ * the probabilities enter the P.V contraction (fp32 accumulation) as E4M3 codes of
+ * 2^6 * P relative to a running max that trails the true one by at most 2 (log2 units),
+ * so codes stay <= 256; O is divided by the sum of those rounded codes and the LSE uses
+ * the unrounded fp32 sum. All scales must be finite and > 0. */
 attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                            const float* q_scale, const float* k_scale, const float* v_scale,
                            void* o, float* lse,
