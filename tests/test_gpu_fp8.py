@@ -159,8 +159,8 @@ def test_rotation_lowers_fp8_error_with_outliers():
 def test_fp8_scores_jumping_past_the_first_tile_max(factor, causal):
     # K activations from key 300 on are scaled up before quantisation, so their scores rise
     # far above the first key tile's row max (x4, x30), or a little above it for some rows
-    # (x1.5). Probabilities taken against the first tile's max then leave the E4M3 range:
-    # the fast pass must mark those rows and the exact pass (per-tile max) redo them.
+    # (x1.5). The running max must then move, with the accumulators rescaled, so that the
+    # E4M3 codes of the probabilities stay in range.
     B, H, N, d = 1, 2, 700, 128
     say(f"case fp8 jumping scores x{factor} causal={causal}")
     q, k, v, signs = inputs.draw_fp8_workload(52, B, H, N, d)
