@@ -36,7 +36,6 @@ COMMON = [
 FILE_FLAGS = {
     "attn_fwd.hip": ["-mllvm", "-enable-misched=0", "-mllvm", "-enable-post-misched=0"],
     "attn_fwd_fp8.hip": ["-mllvm", "-enable-misched=0", "-mllvm", "-enable-post-misched=0"],
-    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

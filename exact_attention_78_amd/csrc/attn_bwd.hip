@@ -16,19 +16,17 @@
 //         dO^T kept in VGPRs), then P and dS in fp32 with one query row per lane (its LSE
 //         and Delta are scalars), then dQ^T += K^T dS^T (A = K^T by LDS transpose reads,
 //         B = dS rounded to 16 bits).
-//   dkdv  one workgroup per (batch*head, 128-key tile), 4 waves x 32 keys; the tile's K
-//         and V stay in LDS, Q and dO tiles of 64 queries stream through it. Per 32-query
-//         block: S = Q K^T and dP = dO V^T (A = Q / dO rows, B = K^T / V^T as rows of K / V:
-//         one key per lane), P and dS in fp32 with the 16 per-query LSE and Delta values
-//         of each lane read from LDS, then dV^T += dO^T P and dK^T += Q^T dS (A = dO^T /
-//         Q^T by LDS transpose reads, B = P / dS rounded to 16 bits). K and V are read
-//         from LDS rather than kept in VGPRs so that the kernel fits 256 VGPRs: beyond
-//         that the compiler moves every MFMA result through AGPRs.
+//   dkdv  one workgroup per (batch*head, 128-key tile), 8 waves: 4 key groups of 32 keys
+//         x 2 halves of each 64-query tile. The tile's K and V stay in LDS, Q and dO tiles
+//         stream through it. Per wave and tile: S = Q K^T and dP = dO V^T on its 32
+//         queries (A = Q / dO rows, B = K^T / V^T as rows of K / V: one key per lane), P
+//         and dS in fp32 with the 16 per-query LSE and Delta values of each lane read from
+//         LDS, then dV^T += dO^T P and dK^T += Q^T dS (A = dO^T / Q^T by LDS transpose
+//         reads, B = P / dS rounded to 16 bits). The two halves of a key group add their
+//         partial dK / dV once, through LDS, at the end. Two waves per SIMD keep each
+//         wave within 256 VGPRs, so MFMA results stay in VGPRs (no AGPR copies).
 // The two gradient kernels each recompute S and dP, so that every gradient stays in
 // registers until its one store: no fp32 partial sums or atomics in memory.
-// At d = 128 the dkdv kernel needs more than 256 registers (one wave per SIMD); this file
-// is compiled with MFMA results in VGPRs (-amdgpu-mfma-vgpr-form), so that only what does
-// not fit spills to AGPRs instead of every S / dP block being copied out of them.
 // Causal: query tiles of dq stop at the diagonal and key tiles of dkdv start at it;
 // waves skip blocks that are wholly masked for them, and only blocks crossing the
 // diagonal or the end of the sequence apply a mask.
@@ -40,7 +38,8 @@ namespace {
 
 constexpr int kWq = 8;      // dq: waves per workgroup (32 query rows each)
 constexpr int kBN = 64;     // dq: keys per K/V tile
-constexpr int kWk = 4;      // dkdv: waves per workgroup (32 keys each)
+constexpr int kKG = 4;      // dkdv: key groups of 32 keys per workgroup
+constexpr int kWk = 8;      // dkdv: waves per workgroup (a key group x a query half of each tile)
 constexpr int kBQ = 64;     // dkdv: queries per Q/dO tile (two 32-query blocks)
 constexpr int kPrepThreads = 256;
 
@@ -275,15 +274,18 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
 }
 
 template <typename Tag, int D, bool CAUSAL>
-__global__ __launch_bounds__(kWk * 64, D == 64 ? 2 : 1) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int N, int n_ntiles, int total_wg, int64_t rows, float c, float scale) {
-  constexpr int W = kWk, BNK = W * 32, NSTEP = D / 16, NDB = D / 32, NQB = kBQ / 32;
+  constexpr int W = kWk, BNK = kKG * 32, NSTEP = D / 16, NDB = D / 32;
   constexpr int TB = kBQ * D * 2;                   // bytes per Q (or dO) tile
   constexpr int TKV = BNK * D * 2;                  // bytes of the workgroup's K (or V)
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TB + 2 * TKV];   // Q slots 0, 1; dO slots 0, 1; K; V
-  __shared__ __attribute__((aligned(16))) float lsd[2][2][kBQ];  // [slot][LSE*log2 e | Delta][query]
+  constexpr int LDS_BYTES = 4 * TB + 2 * TKV;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];   // Q slots 0, 1; dO slots 0, 1; K; V
+  __shared__ __attribute__((aligned(16))) float lsd[2][2][kBQ];    // [slot][LSE*log2 e | Delta][query]
+  static_assert(W == 2 * kKG && kBQ == 64, "two waves (query halves) per key group");
+  static_assert(2 * kKG * NDB * 16 * 64 * 4 <= LDS_BYTES, "the final exchange fits the tiles' LDS");
 
   const int logical = xcd_logical_id(blockIdx.x, total_wg);
   const int bh = logical / n_ntiles;
@@ -293,13 +295,14 @@ __global__ __launch_bounds__(kWk * 64, D == 64 ? 2 : 1) void attn_bwd_dkdv_kerne
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64;
   const int half = lane / 32, l32 = lane % 32;
+  const int kg = wave % kKG, qh = wave / kKG;       // key group; query half of each tile
   const int64_t head_off = (int64_t)bh * N * D;
   const uint16_t* Qh = Q + head_off;
   const uint16_t* dOh = dO + head_off;
   const float* delta_h = ws + (int64_t)bh * N;
   const float* lse2_h = ws + rows + (int64_t)bh * N;
 
-  const int k0 = nt * BNK + wave * 32;
+  const int k0 = nt * BNK + kg * 32;
   const int krow = k0 + l32;
 
   const int n_qtiles = (N + kBQ - 1) / kBQ;
@@ -339,65 +342,85 @@ __global__ __launch_bounds__(kWk * 64, D == 64 ? 2 : 1) void attn_bwd_dkdv_kerne
       load_rows<D, kBQ, W>(dOh, (u + 1) * kBQ, N, gbuf(slot ^ 1), wave, lane);
       if (tid < 2 * kBQ) pf = fetch_ld(u + 1);
     }
-    const int qbase = u * kBQ;
-    if (!CAUSAL || qbase + kBQ - 1 >= k0) {         // else: every query of the tile precedes this wave's keys
+    const int qr = qh * 32;                         // this wave's 32 queries start at row qr of the tile
+    const int qb0 = u * kBQ + qr;
+    if (!CAUSAL || qb0 + 31 >= k0) {                // else: every query of the block precedes this wave's keys
       const uint8_t* qt = qbuf(slot);
       const uint8_t* gt = gbuf(slot);
-      f32x16 s[NQB], dp[NQB];
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
+      for (int st = 0; st < NSTEP; ++st)
+        s = mfma32(Tag{}, row_frag<D>(qt, ta, qr, st), row_frag<D>(kt, ta, kg * 32, st), s);
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st)
-          s[qb] = mfma32(Tag{}, row_frag<D>(qt, ta, qb * 32, st), row_frag<D>(kt, ta, wave * 32, st), s[qb]);
+      for (int st = 0; st < NSTEP; ++st)
+        dp = mfma32(Tag{}, row_frag<D>(gt, ta, qr, st), row_frag<D>(vt, ta, kg * 32, st), dp);
+      const bool edge = (CAUSAL && qb0 < k0 + 31) || qb0 + 32 > N;
+      float p[16], ds[16];
 #pragma unroll
-        for (int st = 0; st < NSTEP; ++st)
-          dp[qb] = mfma32(Tag{}, row_frag<D>(gt, ta, qb * 32, st), row_frag<D>(vt, ta, wave * 32, st), dp[qb]);
-      }
-      u32x4 pb[NQB][2], sb[NQB][2];
+      for (int g = 0; g < 4; ++g) {
+        const int qi = qr + g * 8 + half * 4;       // this lane's queries qi .. qi + 3 of the tile
+        const f32x4 l4 = *(const f32x4*)&lsd[slot][0][qi];
+        const f32x4 d4 = *(const f32x4*)&lsd[slot][1][qi];
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int qb0 = qbase + qb * 32;
-        const bool edge = (CAUSAL && qb0 < k0 + 31) || qb0 + 32 > N;
-        float p[16], ds[16];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int qi = qb * 32 + g * 8 + half * 4;   // this lane's queries qi .. qi + 3 of the tile
-          const f32x4 l4 = *(const f32x4*)&lsd[slot][0][qi];
-          const f32x4 d4 = *(const f32x4*)&lsd[slot][1][qi];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = g * 4 + e;
-            float x = s[qb][r];
-            if (edge) {
-              const int q = qbase + qi + e;
-              if ((CAUSAL && q < krow) || q >= N) x = -INFINITY;
-            }
-            p[r] = fast_exp2(__builtin_fmaf(x, c, -l4[e]));
-            ds[r] = p[r] * (dp[qb][r] - d4[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = g * 4 + e;
+          float x = s[r];
+          if (edge) {
+            const int q = u * kBQ + qi + e;
+            if ((CAUSAL && q < krow) || q >= N) x = -INFINITY;
           }
+          p[r] = fast_exp2(__builtin_fmaf(x, c, -l4[e]));
+          ds[r] = p[r] * (dp[r] - d4[e]);
         }
-        pack16<Tag>(p, pb[qb]);
-        pack16<Tag>(ds, sb[qb]);
       }
+      u32x4 pb[2], sb[2];
+      pack16<Tag>(p, pb);
+      pack16<Tag>(ds, sb);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            accv[db] = mfma32(Tag{}, tr_frag<D>(gt, ta, qb * 32 + h * 16, db), pb[qb][h], accv[db]);
-            acck[db] = mfma32(Tag{}, tr_frag<D>(qt, ta, qb * 32 + h * 16, db), sb[qb][h], acck[db]);
-          }
+        for (int db = 0; db < NDB; ++db) {
+          accv[db] = mfma32(Tag{}, tr_frag<D>(gt, ta, qr + h * 16, db), pb[h], accv[db]);
+          acck[db] = mfma32(Tag{}, tr_frag<D>(qt, ta, qr + h * 16, db), sb[h], acck[db]);
+        }
     }
     if (u + 1 < n_qtiles && tid < 2 * kBQ) lsd[slot ^ 1][tid / kBQ][tid % kBQ] = pf;
     wait_vmcnt<0>();
     barrier_lds();
   }
+  // The two query halves of a key group hold partial sums of the same dK and dV rows.
+  // Half 1 hands over its dK part and half 0 its dV part through LDS (the tiles are no
+  // longer read: the loop ended on a barrier); then half 0 stores dK and half 1 dV.
+  // Layout: [tensor][key group][16-byte piece i of the lane's accumulators][lane].
+  f32x4* xch = (f32x4*)lds;
+  auto piece = [&](int which, int g, int i) __attribute__((always_inline)) -> f32x4* {
+    return xch + ((which * kKG + g) * (NDB * 4) + i) * 64 + lane;
+  };
+  auto give = [&](const f32x16 (&a)[NDB], int which) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *piece(which, kg, db * 4 + q4) = f32x4{a[db][q4 * 4], a[db][q4 * 4 + 1], a[db][q4 * 4 + 2], a[db][q4 * 4 + 3]};
+  };
+  auto take = [&](f32x16 (&a)[NDB], int which) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 b = *piece(which, kg, db * 4 + q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[db][q4 * 4 + e] += b[e];
+      }
+  };
+  if (qh == 1) give(acck, 0);
+  else give(accv, 1);
+  barrier_lds();
+  if (qh == 0) take(acck, 0);
+  else take(accv, 1);
   if (krow < N) {
-    store_rows<Tag, D>(dK + head_off + (int64_t)krow * D, acck, half, scale);
-    store_rows<Tag, D>(dV + head_off + (int64_t)krow * D, accv, half, 1.f);
+    if (qh == 0) store_rows<Tag, D>(dK + head_off + (int64_t)krow * D, acck, half, scale);
+    else store_rows<Tag, D>(dV + head_off + (int64_t)krow * D, accv, half, 1.f);
   }
 }
 
@@ -414,7 +437,7 @@ hipError_t launch_one(const void* q, const void* k, const void* v, const void* o
   hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag, D, CAUSAL>), dim3((unsigned)total_q), dim3(kWq * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws,
                      (uint16_t*)dq, (int)N, n_mtiles, (int)total_q, rows, c, scale);
-  const int n_ntiles = (int)((N + kWk * 32 - 1) / (kWk * 32));
+  const int n_ntiles = (int)((N + kKG * 32 - 1) / (kKG * 32));
   const int64_t total_k = BH * n_ntiles;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)total_k), dim3(kWk * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws,
@@ -449,7 +472,7 @@ hipError_t launch_bwd_f16(const void* q, const void* k, const void* v, const voi
 
 int64_t max_workgroups_bwd(int64_t BH, int64_t N) {
   const int64_t a = BH * ((N + kWq * 32 - 1) / (kWq * 32));
-  const int64_t b = BH * ((N + kWk * 32 - 1) / (kWk * 32));
+  const int64_t b = BH * ((N + kKG * 32 - 1) / (kKG * 32));
   const int64_t p = (BH * N + 15) / 16;              // prep: at least 16 rows per workgroup
   return a > b ? (a > p ? a : p) : (b > p ? b : p);
 }
