@@ -1,5 +1,9 @@
 """Plain fp64 definition of exact attention, forward and backward (oracle; test infrastructure only).
 
+The forward also takes fewer query rows than keys without a mask (one decoding step
+against a key/value cache: the digest's discussion points ask whether such steps
+need a kernel of their own); it is the same definition with Nq rows.
+
 What is computed (FlashAttention-2 digest, "Method — framework overview" flowchart and
 glossary): for each batch b and head h independently,
 
@@ -38,8 +42,11 @@ def attention_forward(q, k, v, causal: bool, scale: float, rows=None, heads=None
 
     Parameters
     ----------
-    q, k, v : arrays of shape [B, H, N, d] (numpy or CPU torch, any float dtype).
-    causal  : mask keys j > i (query i may see keys 0..i).
+    q, k, v : arrays of shape [B, H, N, d] (numpy or CPU torch, any float dtype). When
+              causal is False, q may have its own row count: q [B, H, Nq, d] against
+              k, v [B, H, Nk, d] (every query row sees all Nk keys, as one decoding
+              step does against a key/value cache).
+    causal  : mask keys j > i (query i may see keys 0..i); needs Nq == Nk.
     scale   : the softmax scale, used as given (callers pass the same fp32 value the
               device uses, upcast exactly).
     rows    : optional 1-D array of query-row indices to evaluate (default: all rows).
@@ -54,12 +61,15 @@ def attention_forward(q, k, v, causal: bool, scale: float, rows=None, heads=None
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
-    if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    B, H, N, d = q.shape
-    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
-    if rows.ndim != 1 or (rows.size and (rows.min() < 0 or rows.max() >= N)):
-        raise ValueError("rows must be a 1-D array of indices in [0, N)")
+    if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q [B, H, Nq, d], k and v [B, H, Nk, d] with matching B, H, d")
+    if causal and q.shape != k.shape:
+        raise ValueError("the causal mask needs as many query rows as keys")
+    B, H, Nq, d = q.shape
+    N = k.shape[2]
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    if rows.ndim != 1 or (rows.size and (rows.min() < 0 or rows.max() >= Nq)):
+        raise ValueError("rows must be a 1-D array of indices in [0, Nq)")
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     scale = float(scale)
 

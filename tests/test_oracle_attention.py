@@ -25,12 +25,13 @@ rng = np.random.default_rng(1234)
 def brute_force(q, k, v, causal, scale):
     """Scalar loops with math.exp / math.fsum; no numpy arithmetic."""
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     O = np.zeros((B, H, N, d))
     L = np.zeros((B, H, N))
     for b in range(B):
         for h in range(H):
             for i in range(N):
-                js = range(i + 1) if causal else range(N)
+                js = range(i + 1) if causal else range(Nk)
                 s = [scale * math.fsum(float(q[b, h, i, t]) * float(k[b, h, j, t]) for t in range(d)) for j in js]
                 m = max(s)
                 e = [math.exp(x - m) for x in s]
@@ -50,6 +51,30 @@ def test_brute_force_tiny(shape, causal):
     Ob, Lb = brute_force(q, k, v, causal, scale)
     np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
     np.testing.assert_allclose(L, Lb, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("nq,nk", [(1, 9), (3, 16), (5, 2)])
+def test_brute_force_fewer_queries_than_keys(nq, nk):
+    # decoding shape: q [B, H, Nq, d] against a key/value cache [B, H, Nk, d], no mask
+    q = rng.standard_normal((2, 2, nq, 4))
+    k, v = rng.standard_normal((2, 2, nk, 4)), rng.standard_normal((2, 2, nk, 4))
+    O, L = attention_forward(q, k, v, False, 0.6)
+    Ob, Lb = brute_force(q, k, v, False, 0.6)
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, Lb, rtol=0, atol=1e-12)
+
+
+def test_decode_shape_against_torch_sdpa_and_causal_rejected():
+    q = rng.standard_normal((2, 3, 4, 32))
+    k, v = rng.standard_normal((2, 3, 300, 32)), rng.standard_normal((2, 3, 300, 32))
+    O, L = attention_forward(q, k, v, False, 0.17)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    To = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.17)
+    TL = torch.logsumexp(0.17 * torch.matmul(tq, tk.transpose(-1, -2).contiguous()), dim=-1)
+    np.testing.assert_allclose(O, To.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, TL.numpy(), rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        attention_forward(q, k, v, True, 0.17)
 
 
 @pytest.mark.parametrize("causal", [False, True])
