@@ -11,6 +11,8 @@ from ._binding import (  # noqa: F401
     SIGNATURES,
     attn_bwd_bf16,
     attn_bwd_f16,
+    attn_decode_bf16,
+    attn_decode_f16,
     attn_fwd_bf16,
     attn_fwd_f16,
     attn_fwd_f32,

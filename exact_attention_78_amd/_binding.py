@@ -31,6 +31,9 @@ SIGNATURES = {
     "attn_quant_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "attn_bwd_bf16": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_bwd_f16": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
+    "attn_decode_bf16": [_P] * 6 + [_I64, _I64, _I64, _I64, _I64, _F32, _P],
+    "attn_decode_f16": [_P] * 6 + [_I64, _I64, _I64, _I64, _I64, _F32, _P],
+    "attn_decode_workspace_floats": [_I64, _I64, _I64, _I64, _I64],
     "attn_status_string": [_INT],
     "attn_abi_version": [],
 }
@@ -52,7 +55,8 @@ def library():
         for name, args in SIGNATURES.items():
             fn = getattr(lib, name)
             fn.argtypes = args
-            fn.restype = ctypes.c_char_p if name == "attn_status_string" else ctypes.c_int
+            fn.restype = {"attn_status_string": ctypes.c_char_p,
+                          "attn_decode_workspace_floats": ctypes.c_int64}.get(name, ctypes.c_int)
         _lib = lib
     return _lib
 
@@ -161,6 +165,43 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None):
     fn = {torch.bfloat16: attn_bwd_bf16, torch.float16: attn_bwd_f16}.get(q.dtype)
     _require(fn is not None, f"unsupported dtype {q.dtype}")
     return fn(q, k, v, o, lse, dout, causal, scale)
+
+
+def _decode(fn: str, dtype, q, k, v, scale, out=None, lse=None, workspace=None):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and t.dim() == 4
+                 and t.is_contiguous() and t.device == q.device, f"{name} must be a contiguous {dtype} GPU tensor")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _require(k.shape == (B, H, Nk, d) and v.shape == k.shape, "k and v must be [B, H, Nk, d] with q's B, H, d")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    n_ws = library().attn_decode_workspace_floats(B, H, Nq, Nk, d)
+    _require(n_ws > 0, "unsupported decode sizes (1 <= Nq <= 32)")
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    ws = torch.empty(n_ws, dtype=torch.float32, device=q.device) if workspace is None else workspace
+    _require(o.shape == q.shape and o.dtype == dtype and o.is_contiguous() and o.device == q.device, "bad out")
+    _require(L.shape == (B, H, Nq) and L.dtype == torch.float32 and L.is_contiguous() and L.device == q.device,
+             "bad lse")
+    _require(ws.dtype == torch.float32 and ws.is_contiguous() and ws.numel() >= n_ws and ws.device == q.device,
+             f"workspace must be a contiguous fp32 tensor of at least {n_ws} elements")
+    with torch.cuda.device(q.device):
+        st = getattr(library(), fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(),
+                                    ws.data_ptr(), B, H, Nq, Nk, d, float(scale), _stream(q))
+    _check(fn, st)
+    return o, L
+
+
+def attn_decode_bf16(q, k, v, scale=None, out=None, lse=None, workspace=None):
+    """Split-KV decoding step: bf16 q [B,H,Nq<=32,d] against k, v [B,H,Nk,d], no mask.
+    Returns (O bf16 [B,H,Nq,d], LSE fp32 [B,H,Nq])."""
+    return _decode("attn_decode_bf16", torch.bfloat16, q, k, v, scale, out, lse, workspace)
+
+
+def attn_decode_f16(q, k, v, scale=None, out=None, lse=None, workspace=None):
+    """fp16 variant of attn_decode_bf16."""
+    return _decode("attn_decode_f16", torch.float16, q, k, v, scale, out, lse, workspace)
 
 
 def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=None, out=None, lse=None):

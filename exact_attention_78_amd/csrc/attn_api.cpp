@@ -84,6 +84,43 @@ attn_status_t check_bwd(const void* q, const void* k, const void* v, const void*
   return ATTN_OK;
 }
 
+// Shapes of the decode entry points: q [B,H,Nq,d], k/v [B,H,Nk,d]; writes element counts.
+attn_status_t check_decode_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t* q_elems,
+                                 int64_t* kv_elems, int64_t* rows) {
+  if (Nq < 1 || Nq > 32) return ATTN_ERR_INVALID_ARG;
+  attn_status_t st = check_shape(B, H, Nk, d, kv_elems, rows);
+  if (st != ATTN_OK) return st;
+  if (__builtin_mul_overflow(B * H, Nq, rows) || __builtin_mul_overflow(*rows, d, q_elems) || *q_elems > INT64_MAX / 8)
+    return ATTN_ERR_INVALID_ARG;                   // (B * H cannot overflow: check_shape bounded B * H * Nk * d)
+  return ATTN_OK;
+}
+
+attn_status_t check_decode(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const float* ws, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale) {
+  if (!q || !k || !v || !o || !lse || !ws) return ATTN_ERR_INVALID_ARG;
+  int64_t qe, kve, rows;
+  attn_status_t st = check_decode_shape(B, H, Nq, Nk, d, &qe, &kve, &rows);
+  if (st != ATTN_OK) return st;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  const void* ptrs[6] = {q, k, v, o, lse, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (attn::max_workgroups_decode(B * H, Nq, Nk) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  auto span = [](const void* p, uintptr_t n) { return Range{(uintptr_t)p, (uintptr_t)p + n}; };
+  const int64_t wsf = attn::decode_workspace_floats(B * H, Nq, Nk, d);
+  const Range ins[3] = {span(q, (uintptr_t)qe * 2), span(k, (uintptr_t)kve * 2), span(v, (uintptr_t)kve * 2)};
+  const Range outs[3] = {span(o, (uintptr_t)qe * 2), span(lse, (uintptr_t)rows * sizeof(float)),
+                         span(ws, (uintptr_t)wsf * sizeof(float))};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return ATTN_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j])) return ATTN_ERR_INVALID_ARG;
+  }
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,6 +211,26 @@ attn_status_t attn_bwd_f16(const void* q, const void* k, const void* v, const vo
   if (st != ATTN_OK) return st;
   return from_hip(attn::launch_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, workspace, B * H, N, d, causal != 0, scale,
                                        (hipStream_t)stream));
+}
+
+int64_t attn_decode_workspace_floats(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+  int64_t qe, kve, rows;
+  if (check_decode_shape(B, H, Nq, Nk, d, &qe, &kve, &rows) != ATTN_OK) return -1;
+  return attn::decode_workspace_floats(B * H, Nq, Nk, d);
+}
+
+attn_status_t attn_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
+                               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, void* stream) {
+  attn_status_t st = check_decode(q, k, v, o, lse, workspace, B, H, Nq, Nk, d, scale);
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_decode_bf16(q, k, v, o, lse, workspace, B * H, Nq, Nk, d, scale, (hipStream_t)stream));
+}
+
+attn_status_t attn_decode_f16(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, void* stream) {
+  attn_status_t st = check_decode(q, k, v, o, lse, workspace, B, H, Nq, Nk, d, scale);
+  if (st != ATTN_OK) return st;
+  return from_hip(attn::launch_decode_f16(q, k, v, o, lse, workspace, B * H, Nq, Nk, d, scale, (hipStream_t)stream));
 }
 
 const char* attn_status_string(attn_status_t s) {

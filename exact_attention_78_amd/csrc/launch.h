@@ -26,11 +26,19 @@ hipError_t launch_bwd_f16(const void* q, const void* k, const void* v, const voi
                           const void* dout, void* dq, void* dk, void* dv, float* ws, int64_t BH, int64_t N, int64_t d,
                           bool causal, float scale, hipStream_t stream);
 
+hipError_t launch_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* ws,
+                              int64_t BH, int64_t Nq, int64_t Nk, int64_t d, float scale, hipStream_t stream);
+hipError_t launch_decode_f16(const void* q, const void* k, const void* v, void* o, float* lse, float* ws,
+                             int64_t BH, int64_t Nq, int64_t Nk, int64_t d, float scale, hipStream_t stream);
+// Floats of workspace the decode launches use.
+int64_t decode_workspace_floats(int64_t BH, int64_t Nq, int64_t Nk, int64_t d);
+
 // Workgroup counts of the launches above (validated against the 32-bit grid limit).
 int64_t max_workgroups_fwd16(int64_t BH, int64_t N);
 int64_t max_workgroups_fwd32(int64_t BH, int64_t N);
 int64_t max_workgroups_fwd8(int64_t BH, int64_t N);
 int64_t max_workgroups_quant(int64_t BH, int64_t N);
 int64_t max_workgroups_bwd(int64_t BH, int64_t N);
+int64_t max_workgroups_decode(int64_t BH, int64_t Nq, int64_t Nk);
 
 }  // namespace attn

@@ -20,8 +20,9 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Layout: Q, K, V and O are contiguous row-major [B, H, N, d] (row stride d elements);
- *    LSE is contiguous fp32 [B, H, N]. Per-block fp8 scales are fp32 [B, H, ceil(N/128)].
+ *  - Layout: Q, K, V and O are contiguous row-major [B, H, N, d] (row stride d elements;
+ *    decode: Nq query rows against Nk keys); LSE is contiguous fp32 [B, H, N]. Per-block
+ *    fp8 scales are fp32 [B, H, ceil(N/128)].
  *  - Ownership: every pointer is caller-owned device memory on the current HIP device.
  *    The library allocates nothing, frees nothing and keeps no state between calls; calls
  *    are reentrant. Tensor pointers must be 16-byte aligned.
@@ -126,6 +127,28 @@ attn_status_t attn_bwd_f16(const void* q, const void* k, const void* v, const vo
                            const void* dout, void* dq, void* dk, void* dv, float* workspace,
                            int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                            void* stream);
+
+/* Decoding step against a key/value cache (split-KV): q [B, H, Nq, d] with 1 <= Nq <= 32
+ * query rows, k and v [B, H, Nk, d], no mask (every query row sees all Nk keys), in bf16;
+ * writes O bf16 [B, H, Nq, d] and LSE fp32 [B, H, Nq] with the same definitions as
+ * attn_fwd_bf16. The FlashAttention-2 digest (discussion points) asks whether decoding
+ * needs its own kernel; here the keys are split into chunks, each chunk's partial O and
+ * LSE go to `workspace` (caller-owned device memory of attn_decode_workspace_floats(...)
+ * fp32 values, overwritten, nothing of use afterwards), and a second kernel merges them
+ * through the LSEs. Two kernels are enqueued on `stream`. Nq outside [1, 32] is
+ * ATTN_ERR_INVALID_ARG; d as for the other entry points. */
+attn_status_t attn_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
+                               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                               void* stream);
+
+/* fp16 tensors in and out; as attn_decode_bf16 with fp16 in place of bf16. */
+attn_status_t attn_decode_f16(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                              void* stream);
+
+/* Workspace size (fp32 values) that attn_decode_* needs for these sizes; -1 if the sizes
+ * are invalid. Host-only, no HIP call. */
+int64_t attn_decode_workspace_floats(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d);
 
 /* Static description of a status code; never NULL. */
 const char* attn_status_string(attn_status_t s);

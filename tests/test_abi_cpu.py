@@ -30,7 +30,7 @@ A = [(i + 1) << 40 for i in range(10)]
 
 def header_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:attn_status_t|const char\*|int)\s+(attn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:attn_status_t|const char\*|int|int64_t)\s+(attn_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +41,8 @@ def lib():
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = header_functions()
     assert set(names) == {"attn_fwd_bf16", "attn_fwd_f16", "attn_fwd_f32", "attn_fwd_fp8", "attn_quant_fp8",
-                          "attn_bwd_bf16", "attn_bwd_f16", "attn_status_string", "attn_abi_version"}
+                          "attn_bwd_bf16", "attn_bwd_f16", "attn_decode_bf16", "attn_decode_f16",
+                          "attn_decode_workspace_floats", "attn_status_string", "attn_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in _binding.SIGNATURES, n
@@ -119,6 +120,28 @@ def test_bwd_validation(lib, fn, defect, expect):
                 B=1, H=2, N=64, d=64, causal=1, scale=0.125)
     args.update(defect)
     assert getattr(lib, fn)(*args.values(), None) == expect
+
+
+@no_gpu_only
+@pytest.mark.parametrize("fn", ["attn_decode_bf16", "attn_decode_f16"])
+@pytest.mark.parametrize("defect,expect", [
+    (dict(q=None), INVALID), (dict(v=None), INVALID), (dict(ws=None), INVALID), (dict(Nq=0), INVALID),
+    (dict(Nq=33), INVALID), (dict(Nk=0), INVALID), (dict(d=96), UNSUPPORTED), (dict(scale=0.0), INVALID),
+    (dict(o=A[0]), INVALID), (dict(lse=A[1] + 64), INVALID), (dict(ws=A[3]), INVALID), (dict(ws=A[4] + 8), INVALID),
+    (dict(B=1 << 40, H=1 << 40), INVALID),
+])
+def test_decode_validation(lib, fn, defect, expect):
+    args = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], ws=A[5], B=2, H=2, Nq=1, Nk=1000, d=128, scale=0.0884)
+    args.update(defect)
+    assert getattr(lib, fn)(*args.values(), None) == expect
+
+
+def test_decode_workspace_size(lib):
+    # B*H*n_split*Nq*(d+1): one partial O row and LSE per (head, key chunk, query row)
+    n = lib.attn_decode_workspace_floats(2, 16, 1, 8192, 128)
+    assert n > 0 and n % (2 * 16 * 1 * 129) == 0
+    assert lib.attn_decode_workspace_floats(2, 16, 0, 8192, 128) == -1
+    assert lib.attn_decode_workspace_floats(2, 16, 33, 8192, 128) == -1
 
 
 def test_binding_rejects_host_tensors_before_calling():
