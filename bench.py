@@ -10,7 +10,9 @@ one batch of seeded synthetic inputs that are already resident in HBM.
 Prints ONE JSON line. Also reported, outside ``value``: the backward pass of the same
 bf16 workload (dQ, dK, dV from a seeded dO; 2.5 times the forward FLOPs), the fp8 path
 on the fp8 workload (B = 2, H = 16, N = 8192, d = 128, causal: quantiser and attention
-timed separately), and the CPU oracle timed on a bounded sample of the bf16 workload.
+timed separately), one split-KV decoding step (B = 16, H = 16, 1 query row against
+8192 keys; HBM-bound, reported in GB/s), and the CPU oracle timed on a bounded sample
+of the bf16 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -126,6 +128,23 @@ def backward_leg(torch, ea, inputs, w, tensors, o, lse, steps, warmup):
             "flop_convention": "2.5 x forward (five N x N x d contractions), halved for causal"}
 
 
+def decode_leg(torch, ea, inputs, steps, warmup):
+    """One decoding step (split-KV): 1 query row per head against an 8192-key bf16 cache."""
+    B, H, Nq, Nk, d = 16, 16, 1, 8192, 128
+    q = inputs.to_torch(inputs.normal_f32(7, inputs.Q_ID, (B, H, Nq, d)), "bf16").cuda()
+    k = inputs.to_torch(inputs.normal_f32(7, inputs.K_ID, (B, H, Nk, d)), "bf16").cuda()
+    v = inputs.to_torch(inputs.normal_f32(7, inputs.V_ID, (B, H, Nk, d)), "bf16").cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ea.library().attn_decode_workspace_floats(B, H, Nq, Nk, d), dtype=torch.float32, device="cuda")
+    ms = timed(lambda: ea.attn_decode_bf16(q, k, v, out=o, lse=lse, workspace=ws), steps, warmup, torch)
+    nbytes = 2 * B * H * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4   # K, V, Q read; O, LSE written
+    assert bool(torch.isfinite(o.float()).all())
+    return {"workload": "bf16 decoding step, B=16 H=16 Nq=1 Nk=8192 d=128, no mask (split-KV)",
+            "us": ms * 1e3, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def fp8_leg(torch, ea, inputs, steps, warmup):
     import numpy as np
 
@@ -167,7 +186,7 @@ def main():
     # 100 untimed steps (~60 ms here) get there before the timed region starts.
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--no-extra", action="store_true", help="skip the backward and fp8 legs")
+    ap.add_argument("--no-extra", action="store_true", help="skip the backward, fp8 and decode legs")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB x 4 (HBM counter calibration) and exit")
@@ -230,6 +249,7 @@ def main():
     if not args.no_extra:
         out["backward"] = backward_leg(torch, ea, inputs, w, (gq, gk, gv), o, lse, max(3, args.steps // 2), 3)
         out["fp8"] = fp8_leg(torch, ea, inputs, max(3, args.steps // 2), 1)
+        out["decode"] = decode_leg(torch, ea, inputs, max(3, args.steps), 5)
     if not args.no_cpu_baseline:
         qf, kf, vf = (t.float().numpy() for t in cpu)     # the bf16 values, upcast exactly
         out["cpu_baseline"] = cpu_baseline(qf, kf, vf, True, scale, args.cpu_budget)
