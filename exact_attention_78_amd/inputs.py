@@ -104,6 +104,18 @@ def draw_fp8_workload(wid: int, B: int, H: int, N: int, d: int, frac: float = 0.
     return q, k, v, signs
 
 
+def draw_fp8_entry_outliers(wid: int, B: int, H: int, N: int, d: int, frac: float = 0.01, mult: float = 20.0):
+    """Like ``draw_fp8_workload`` but the outliers are scattered entries instead of whole
+    channels: a seeded ``frac`` of the entries of Q and of K (independent positions,
+    tensor ids 8 and 9) is multiplied by ``mult``; V is plain."""
+    q, k, v = draw_qkv(wid, B, H, N, d)
+    for x, tid in ((q, 8), (k, 9)):
+        mask = generator(wid, tid).random(size=x.shape) < frac
+        x[mask] *= np.float32(mult)
+    signs = np.where(generator(wid, SIGN_ID).integers(0, 2, size=d) == 1, 1.0, -1.0).astype(np.float32)
+    return q, k, v, signs
+
+
 def to_torch(x: np.ndarray, dtype: str):
     """Round an fp32 array to the named dtype on the CPU (round-to-nearest-even) as a
     contiguous CPU torch tensor. fp8 workloads carry bf16 activations."""
