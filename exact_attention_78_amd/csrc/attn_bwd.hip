@@ -88,10 +88,8 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
   constexpr int TB = kBN * D * 2;                   // bytes per K (or V) tile
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TB];   // K slots 0, 1; V slots 0, 1
 
-  const int logical = xcd_logical_id(blockIdx.x, total_wg);
-  const int bh = logical / n_mtiles;
-  int mt = logical % n_mtiles;
-  if (CAUSAL) mt = n_mtiles - 1 - mt;               // longest query tiles first
+  int bh, mt;
+  xcd_query_tile(blockIdx.x, total_wg, n_mtiles, CAUSAL, bh, mt);   // causal: longest query tiles first
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -182,9 +180,11 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
   static_assert(W == 2 * kKG && kBQ == 64, "two waves (query halves) per key group");
   static_assert(2 * kKG * NDB * 16 * 64 * 4 <= LDS_BYTES, "the final exchange fits the tiles' LDS");
 
-  const int logical = xcd_logical_id(blockIdx.x, total_wg);
-  const int bh = logical / n_ntiles;
-  const int nt = logical % n_ntiles;                // causal: low key tiles carry the most queries, and go first
+  // causal: low key tiles see the most queries; the query-tile order, reversed, runs
+  // them first
+  int bh, rt;
+  xcd_query_tile(blockIdx.x, total_wg, n_ntiles, CAUSAL, bh, rt);
+  const int nt = CAUSAL ? n_ntiles - 1 - rt : rt;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);

@@ -401,9 +401,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     }
     if (half == 0) LSE[(int64_t)bh * N + qrow] = lse;
   };
-  const int logical = xcd_logical_id(blockIdx.x, total_wg);
-  const int m = logical % n_mtiles;
-  tile(logical / n_mtiles, CAUSAL ? n_mtiles - 1 - m : m);   // longest query tiles first
+  int bh, mt;
+  xcd_query_tile(blockIdx.x, total_wg, n_mtiles, CAUSAL, bh, mt);
+  tile(bh, mt);
 }
 
 template <typename Tag, int D, bool CAUSAL>

@@ -33,10 +33,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(const float* 
   __shared__ float Ks[kBN * LD];
   __shared__ float Vs[kBN * LD];
 
-  const int logical = xcd_logical_id(blockIdx.x, total_wg);
-  const int bh = logical / n_mtiles;
-  int mt = logical % n_mtiles;
-  if (CAUSAL) mt = n_mtiles - 1 - mt;
+  int bh, mt;
+  xcd_query_tile(blockIdx.x, total_wg, n_mtiles, CAUSAL, bh, mt);
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int half = lane / 32, l32 = lane % 32;

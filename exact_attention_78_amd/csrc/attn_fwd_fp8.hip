@@ -71,10 +71,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   static_assert(LPW == 1, "one direct load per wave per tile");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];   // K ring, then V ring
 
-  const int logical = xcd_logical_id(blockIdx.x, total_wg);
-  const int bh = logical / n_mtiles;
-  int mt = logical % n_mtiles;
-  if (CAUSAL) mt = n_mtiles - 1 - mt;                // longest query tiles first
+  int bh, mt;
+  xcd_query_tile(blockIdx.x, total_wg, n_mtiles, CAUSAL, bh, mt);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);

@@ -95,6 +95,26 @@ __device__ __forceinline__ int xcd_logical_id(int w, int total) {
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
 }
 
+// Query tile (bh, mt) of workgroup w in a grid of total = BH * n_mtiles workgroups.
+// Each XCD gets a contiguous set of heads, so their K/V stay in its L2. Causal grids go
+// longest query tile first, per group of two heads when BH is a multiple of 16 (the XCD
+// starts both heads' longest tiles before any shorter one: the tail of short tiles
+// shrinks, while only two heads' K/V compete for the L2), else per head.
+__device__ __forceinline__ void xcd_query_tile(int w, int total, int n_mtiles, bool causal, int& bh, int& mt) {
+  const int n_bh = total / n_mtiles;
+  if (causal && n_bh % 8 == 0) {
+    const int nh = n_bh / 8, g = nh % 2 == 0 ? 2 : 1, loc = w / 8;
+    const int grp = loc / (g * n_mtiles), r = loc % (g * n_mtiles);
+    bh = (w % 8) * nh + grp * g + r % g;
+    mt = n_mtiles - 1 - r / g;
+  } else {
+    const int logical = xcd_logical_id(w, total);
+    const int m = logical % n_mtiles;
+    bh = logical / n_mtiles;
+    mt = causal ? n_mtiles - 1 - m : m;
+  }
+}
+
 // Wait until at most N vector-memory loads of this wave are outstanding.
 // (s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at
 // their maxima; the builtin keeps the compiler's own counter tracking informed.)
