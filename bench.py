@@ -49,9 +49,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def read_counters():
-    """HBM bytes per launch of the bf16 kernel from the committed rocprofv3 counter summary,
-    or None when the summary is missing or was taken on different kernel sources."""
+def read_counters(key="hbm_bytes_per_launch"):
+    """A figure of the committed rocprofv3 counter summary of the bf16 kernel (HBM bytes per
+    launch by default), or None when the summary is missing or was taken on different
+    kernel sources."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     kv = {}
@@ -62,7 +63,7 @@ def read_counters():
     if kv.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"].split()[0])
+        return float(kv[key].split()[0])
     except (KeyError, ValueError):
         return None
 
@@ -224,6 +225,7 @@ def main():
         ea.attn_fwd_bf16(gq, gk, gv, causal=True, scale=scale, out=o, lse=lse)
 
     ms = timed(step, args.steps, args.warmup, torch)
+    sclk = read_counters("sclk_ghz_estimate")
     flops = counted_flops(w.B, w.H, w.N, w.d, True)
     tflops = flops / (ms * 1e-3) / 1e12
 
@@ -243,6 +245,9 @@ def main():
         "config": {"workload": "bf16 causal attention forward, B=2 H=16 N=8192 d=128", "B": w.B, "H": w.H,
                    "N": w.N, "d": w.d, "causal": True, "flop_per_step": flops},
         "pct_of_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        # the engine clock under this load (counter run) and the peak scaled to it
+        "sclk_ghz": sclk,
+        "pct_of_peak_at_measured_clock": None if sclk is None else 100.0 * tflops / (PEAK_BF16_TFLOPS * sclk / 2.4),
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": read_counters()},
     }
