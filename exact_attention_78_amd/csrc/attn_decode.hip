@@ -21,7 +21,8 @@
 //            LDS transpose reads, P rounded to 16 bits); writes O_s / l_s (fp32) and LSE_s
 //            to the caller's workspace.
 //   combine  one workgroup per (batch*head, query row): the weights exp(LSE_s - LSE) and
-//            the weighted sum of the O_s, rounded once to 16 bits.
+//            the weighted sum of the O_s (chunks spread over 8 (d=128) or 16 (d=64)
+//            groups of threads, added through LDS), rounded once to 16 bits.
 #include "device_common.h"
 #include "launch.h"
 #include "tile_lds.h"
@@ -32,7 +33,7 @@ namespace {
 constexpr int kDW = 4;            // waves (key chunks) per workgroup
 constexpr int kKT = 32;           // keys per tile
 constexpr int kTargetWaves = 2048;
-constexpr int kCombineThreads = 64;
+constexpr int kCombineThreads = 256;
 
 // Key chunking: chunk = a multiple of kKT, so that every chunk holds at least one key.
 struct Split {
@@ -153,28 +154,47 @@ __global__ __launch_bounds__(kCombineThreads) void attn_decode_combine_kernel(co
                                                                               uint16_t* __restrict__ O,
                                                                               float* __restrict__ LSE, int Nq,
                                                                               int n_split) {
-  constexpr int EPT = D / kCombineThreads;          // output elements per thread (2 or 1)
+  // kGroups groups of D/4 threads; group g sums the chunks sp = g, g + kGroups, ... for
+  // 4 head dims per thread, then the groups' sums are added through LDS.
+  constexpr int TPG = D / 4, kGroups = kCombineThreads / TPG;
+  __shared__ float red_m[kCombineThreads / 64];
+  __shared__ __attribute__((aligned(16))) f32x4 part_o[kGroups][TPG];
+  __shared__ float part_w[kGroups];
   const int row = blockIdx.x;                       // bh * Nq + q
   const int bh = row / Nq, q = row % Nq;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, g = tid / TPG, t = tid % TPG;
   auto part = [&](int sp) -> int64_t { return ((int64_t)bh * n_split + sp) * Nq + q; };
   float m = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, ws_l[part(sp)]);
-  float wsum = 0.f, acc[EPT] = {};
-  for (int sp = 0; sp < n_split; ++sp) {
+  for (int sp = tid; sp < n_split; sp += kCombineThreads) m = fmaxf(m, ws_l[part(sp)]);
+#pragma unroll
+  for (int off = 32; off >= 1; off /= 2) m = fmaxf(m, __shfl_xor(m, off));
+  if (tid % 64 == 0) red_m[tid / 64] = m;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kCombineThreads / 64; ++i) m = fmaxf(m, red_m[i]);
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = g; sp < n_split; sp += kGroups) {
     const float w = __expf(ws_l[part(sp)] - m);
     wsum += w;
+    const f32x4 x = *(const f32x4*)(ws_o + part(sp) * D + t * 4);
+    acc = f32x4{__builtin_fmaf(w, x[0], acc[0]), __builtin_fmaf(w, x[1], acc[1]), __builtin_fmaf(w, x[2], acc[2]),
+                __builtin_fmaf(w, x[3], acc[3])};
+  }
+  part_o[g][t] = acc;
+  if (t == 0) part_w[g] = wsum;
+  __syncthreads();
+  if (g != 0) return;
+  float wt = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) acc[e] = __builtin_fmaf(w, ws_o[part(sp) * D + tid * EPT + e], acc[e]);
+  for (int i = 0; i < kGroups; ++i) {
+    wt += part_w[i];
+    o += part_o[i][t];
   }
-  const float inv = 1.f / wsum;
-  if constexpr (EPT == 2) {
-    *(uint32_t*)(O + (int64_t)row * D + tid * 2) = pack2(Tag{}, acc[0] * inv, acc[1] * inv);
-  } else {
-    const uint32_t w2 = pack2(Tag{}, acc[0] * inv, 0.f);
-    O[(int64_t)row * D + tid] = (uint16_t)(w2 & 0xFFFFu);
-  }
-  if (tid == 0) LSE[row] = m + __logf(wsum);
+  const float inv = 1.f / wt;
+  *(u32x2*)(O + (int64_t)row * D + t * 4) = u32x2{pack2(Tag{}, o[0] * inv, o[1] * inv), pack2(Tag{}, o[2] * inv, o[3] * inv)};
+  if (t == 0) LSE[row] = m + __logf(wt);
 }
 
 template <typename Tag, int D>
