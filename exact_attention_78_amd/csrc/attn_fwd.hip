@@ -29,9 +29,10 @@
 //   step's MFMAs, LDS reads and VALU work are written in the order they are issued.
 //   K and V tiles sit in two 4-slot LDS rings (128 KiB at d = 128), filled by direct
 //   global->LDS loads (global_load_lds_dwordx4) two or three steps ahead of their use.
-//   Each call is two launches of this kernel: a fast pass that keeps the first tile's
-//   row max as the softmax reference for every tile, and an exact pass that redoes, with
-//   a per-tile running max, the query tiles whose probabilities outgrew that reference.
+//   A call of at least ~1e11 FLOPs is two launches of this kernel: a fast pass that keeps
+//   the first tile's row max as the softmax reference for every tile, and an exact pass
+//   that redoes, with a per-tile running max, the query tiles whose probabilities
+//   outgrew that reference. Smaller calls launch the exact pass alone, on every tile.
 #include <type_traits>
 
 #include "device_common.h"
@@ -53,6 +54,7 @@ constexpr float kTau = 8.0f;   // lazy-rescale threshold for the running max, in
 // every query tile that carries a mark and leaves the others untouched. The guard keeps
 // P within its 16-bit type (bf16: 2^64, far inside its range; fp16: 2^15 < 65504) and l
 // and O far inside fp32.
+constexpr double kTwoPassFlops = 1e11;               // smaller calls: exact pass only
 template <typename Tag> struct Guard;
 template <> struct Guard<Bf16Tag> { static constexpr float value = 18446744073709551616.0f; };   // 2^64
 template <> struct Guard<F16Tag> { static constexpr float value = 32768.0f; };                  // 2^15
@@ -73,7 +75,8 @@ template <> struct Swz<64> {
 template <typename Tag, int D, bool CAUSAL, int W, bool FAST>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int total_wg, float c /* scale*log2 e */) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int total_wg, float c /* scale*log2 e */,
+    int check_marks /* exact pass: redo marked tiles only (1) or every tile (0) */) {
   constexpr int BM = W * 32;                        // query rows per workgroup
   constexpr int NSTEP = D / 16;                     // MFMA k-steps over the head dim
   constexpr int NKB = kBN / 32;                     // 32-key blocks per tile
@@ -105,8 +108,8 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
 
     const int q0 = mt * BM + wave * 32;               // this wave's 32 rows; one per lane (and lane^32)
     const int qrow = q0 + l32;
-    if constexpr (!FAST) {
-      // Exact pass: only query tiles that the fast pass marked (a NaN LSE) are redone.
+    if (!FAST && check_marks) {
+      // Exact pass after a fast pass: only query tiles that it marked (a NaN LSE) are redone.
       if (tid == 0) marked = 0;
       __syncthreads();
       const bool mine = half == 0 && qrow < N && __builtin_isnan(LSE[(int64_t)bh * N + qrow]);
@@ -406,18 +409,23 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   tile(bh, mt);
 }
 
-template <typename Tag, int D, bool CAUSAL>
+template <typename Tag, int D, bool CAUSAL, int W>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
                       float scale, hipStream_t stream) {
-  constexpr int BM = kWaves * 32;
+  constexpr int BM = W * 32;
   const int n_mtiles = (int)((N + BM - 1) / BM);
   const int64_t total = BH * n_mtiles;
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, kWaves, true>), dim3((unsigned)total), dim3(kWaves * 64), 0,
+  // Below ~1e11 counted FLOPs (~0.1 ms of work) the fast pass saves less than the exact
+  // pass's launch costs, so such calls run the exact pass alone, on every tile.
+  const double flops = 4.0 * (double)BH * (double)N * (double)N * D / (CAUSAL ? 2 : 1);
+  const bool two_pass = flops >= kTwoPassFlops;
+  if (two_pass)
+    hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, true>), dim3((unsigned)total), dim3(W * 64), 0,
+                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
+                       n_mtiles, (int)total, scale * kLog2e, 1);
+  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, false>), dim3((unsigned)total), dim3(W * 64), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
-                     n_mtiles, (int)total, scale * kLog2e);
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, kWaves, false>), dim3((unsigned)total), dim3(kWaves * 64), 0,
-                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
-                     n_mtiles, (int)total, scale * kLog2e);
+                     n_mtiles, (int)total, scale * kLog2e, two_pass ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -425,10 +433,10 @@ template <typename Tag>
 hipError_t launch_16bit(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
                         int64_t d, bool causal, float scale, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_one<Tag, 128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch_one<Tag, 128, false>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch_one<Tag, 64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_one<Tag, 64, false>(q, k, v, o, lse, BH, N, scale, stream);
+    return causal ? launch_one<Tag, 128, true, kWaves>(q, k, v, o, lse, BH, N, scale, stream)
+                  : launch_one<Tag, 128, false, kWaves>(q, k, v, o, lse, BH, N, scale, stream);
+  return causal ? launch_one<Tag, 64, true, kWaves>(q, k, v, o, lse, BH, N, scale, stream)
+                : launch_one<Tag, 64, false, kWaves>(q, k, v, o, lse, BH, N, scale, stream);
 }
 
 }  // namespace

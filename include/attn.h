@@ -61,10 +61,12 @@ typedef enum {
 #define ATTN_ABI_VERSION 1
 
 /* bf16 Q/K/V in, bf16 O out (round to nearest even), fp32 LSE out. P is rounded to
- * bf16 before the P.V contraction; both contractions accumulate in fp32. The call
- * enqueues two kernels on `stream` (a pass that uses the first key tile's row max as the
- * softmax reference, then a pass that redoes with a per-tile max any query tile whose
- * probabilities outgrew it); O and LSE are complete when both have run. */
+ * bf16 before the P.V contraction; both contractions accumulate in fp32. A call of at
+ * least 1e11 counted FLOPs (4*B*H*N^2*d, halved for causal) enqueues two kernels on
+ * `stream` (a pass that uses the first key tile's row max as the softmax reference, then
+ * a pass that redoes with a per-tile max any query tile whose probabilities outgrew it);
+ * a smaller call enqueues the second kernel alone, on every tile. O and LSE are complete
+ * when the call's kernels have run. */
 attn_status_t attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                             void* stream);

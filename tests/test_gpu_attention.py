@@ -92,6 +92,16 @@ def test_c2_full(dtype):
     check(cpu, gpu, dtype, True)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_d64_larger_grid_sampled_heads(causal, dtype):
+    # d = 64 on a grid of 512 workgroups (128 heads x 4 query tiles), three heads checked
+    B, H, N, d = 4, 32, 1024, 64
+    say(f"case d64 8-wave grid causal={causal} dtype={dtype}")
+    cpu, gpu = make(2, B, H, N, d, dtype)
+    check(cpu, gpu, dtype, causal, heads=[(0, 0), (3, 31), (2, 17)])
+
+
 def sample_rows(N, n_random=96, seed=0):
     r = np.random.default_rng(seed)
     edges = [0, 1, 2, 63, 64, 127, 128, 129, N // 2, N - 129, N - 128, N - 65, N - 64, N - 2, N - 1]
@@ -173,15 +183,22 @@ def test_large_key_shift_is_stable(causal):
 def test_scores_jumping_past_the_first_tile_max(factor, causal, dtype):
     # Keys from 300 on are scaled up: their scores exceed the first tile's row max by about
     # 25 (x8) or far more than 64 (x30) in log2 units. Probabilities against the first
-    # tile's max would then overflow fp16 (x8) or any 16-bit type (x30); the fast pass
-    # must mark those rows and the exact pass (per-tile max) redo their query tiles.
-    B, H, N, d = 1, 2, 700, 128
+    # tile's max would then overflow fp16 (x8) or any 16-bit type (x30). At N = 700 the
+    # call runs the exact pass alone (per-tile max); at B2 H16 N4096 (above the two-pass
+    # threshold of 1e11 FLOPs) the fast pass must mark those rows and the exact pass redo
+    # their query tiles, checked on sampled rows of two heads.
     say(f"case jumping scores x{factor} causal={causal} dtype={dtype}")
-    q, k, v = inputs.draw_qkv(12, B, H, N, d)
-    k = k.copy()
-    k[:, :, 300:] *= np.float32(factor)
-    tq, tk, tv = (inputs.to_torch(x, dtype) for x in (q, k, v))
-    check((tq, tk, tv), tuple(t.cuda() for t in (tq, tk, tv)), dtype, causal)
+    for B, H, N, d in ((1, 2, 700, 128), (2, 16, 4096, 128)):
+        q, k, v = inputs.draw_qkv(12, B, H, N, d)
+        k = k.copy()
+        k[:, :, 300:] *= np.float32(factor)
+        tq, tk, tv = (inputs.to_torch(x, dtype) for x in (q, k, v))
+        if N <= 1000:
+            check((tq, tk, tv), tuple(t.cuda() for t in (tq, tk, tv)), dtype, causal)
+        else:
+            rows = np.unique(np.concatenate([np.arange(0, 320, 7), [N - 1], np.random.default_rng(3).integers(0, N, 64)]))
+            check((tq, tk, tv), tuple(t.cuda() for t in (tq, tk, tv)), dtype, causal, rows=rows,
+                  heads=[(0, 0), (1, 15)])
 
 
 def test_outputs_fully_written_and_deterministic():
