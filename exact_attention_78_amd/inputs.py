@@ -116,6 +116,18 @@ def draw_fp8_entry_outliers(wid: int, B: int, H: int, N: int, d: int, frac: floa
     return q, k, v, signs
 
 
+def normal_on_device(wid: int, tensor_id: int, shape, dtype, device="cuda"):
+    """Seeded N(0,1) tensor drawn directly on the device in the given torch dtype (torch's
+    Philox generator, seeded from SeedSequence([78, workload_id, tensor_id])), for
+    workloads too large to draw on the host. The oracle reads back the values drawn."""
+    import torch
+
+    seed = int(np.random.SeedSequence([SEED_ROOT, wid, tensor_id]).generate_state(1, dtype=np.uint64)[0] >> 1)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=dtype, device=device)
+
+
 def to_torch(x: np.ndarray, dtype: str):
     """Round an fp32 array to the named dtype on the CPU (round-to-nearest-even) as a
     contiguous CPU torch tensor. fp8 workloads carry bf16 activations."""

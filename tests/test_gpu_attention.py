@@ -130,6 +130,33 @@ def test_long_sequence_sampled(causal):
     check(cpu, gpu, "bf16", causal, rows=rows, heads=[(0, 0)])
 
 
+def test_tensors_over_2_31_elements():
+    # B1 H4100 N4096 d128 bf16, causal: each of Q, K, V, O holds 2.15e9 elements (> 2^31,
+    # 4.3 GB), so the heads past 4096 sit beyond 32-bit element offsets. Inputs are drawn on
+    # the device; three heads (first, middle, last) are read back and checked on sampled rows.
+    B, H, N, d = 1, 4100, 4096, 128
+    assert B * H * N * d > 2**31
+    say(f"case >2^31 elements: B{B} H{H} N{N} d{d} bf16 causal")
+    gq, gk, gv = (inputs.normal_on_device(40, t, (B, H, N, d), torch.bfloat16) for t in range(3))
+    scale = inputs.softmax_scale(d)
+    o, lse = attn_fwd_bf16(gq, gk, gv, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    hs = [0, H // 2, H - 1]
+    cpu = tuple(t[:, hs].cpu() for t in (gq, gk, gv))
+    O = o[:, hs].float().cpu().numpy().astype(np.float64)
+    L = lse[:, hs].cpu().numpy().astype(np.float64)
+    del gq, gk, gv, o, lse
+    torch.cuda.empty_cache()
+    rows = sample_rows(N, n_random=48, seed=5)
+    Oref, Lref = attention_forward(*cpu, True, scale, rows=rows)
+    O, L = O[:, :, rows], L[:, :, rows]
+    assert np.isfinite(O).all() and np.isfinite(L).all()
+    eo, el = np.max(np.abs(O - Oref)), lse_err(L, Lref)
+    say(f"  heads {hs}: max|dO|={eo:.3e} max rel dLSE={el:.3e}")
+    assert eo <= O_TOL_16, eo
+    assert el <= LSE_REL, el
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_q_zero_closed_form(causal, dtype):
