@@ -13,16 +13,21 @@
 //   S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 on the raw codes (two per 32 keys);
 //   the block scales and scale*log2(e) form one factor c_t = scale*log2e*sq*sk applied
 //   inside the exp2 argument (the running max M is kept in these log2 units).
-//   P enters the P.V MFMA as E4M3 codes of P' = 2^kPShift * 2^(s - M): the running max
-//   is raised lazily (by more than kTau only), so P' <= 2^(kPShift+kTau) = 256 stays below
-//   the E4M3 maximum (448) while probabilities down to 2^-15 of the max stay
-//   representable. The accumulator is kept in units of the current V block scale: when
-//   the tiles move to the next 128-key block (every second tile) it is multiplied by
-//   sv_old / sv_new, together with any owed running-max rescale.
-//   O is normalised by the sum of the *rounded* P' codes, accumulated by one more MFMA
-//   per tile whose A operand is all ones (E4M3 1.0): numerator and denominator then use
-//   the same weights, so a row dominated by one key returns that key's V row however
-//   P' rounds. The LSE uses the sum of the unrounded fp32 probabilities.
+//   P enters the P.V MFMA as E4M3 codes of P'' = P' / w with P' = 2^kPShift * 2^(s - M)
+//   and w = U / sv[block]: the P.V accumulator is kept in a unit U (a V block scale) and
+//   the ratio of the tile's V block scale to U rides in the exp2 argument (a per-tile
+//   bias), so the accumulator is not rescaled when the tiles enter the next V block. U
+//   moves, lazily like the running max, only when that ratio leaves [1, 3/2] (U then
+//   follows the smallest V block scale seen, and moves only a few times along a row of
+//   blocks whose scales vary little); the accumulator is then rescaled once. With w <= 1,
+//   P'' is never below P' = 2^kPShift * 2^(s - M), so probabilities down to 2^-15 of the
+//   max stay representable, and as the running max is raised by more than kTau only,
+//   P'' <= 1.5 * 2^(kPShift+kTau) = 384 stays below the E4M3 maximum (448).
+//   O is normalised by the sum of the *rounded* P'' codes times w: one more MFMA per tile,
+//   whose A operand is all ones (E4M3 1.0), sums the tile's codes exactly in fp32, and
+//   that sum times the tile's w is added to the denominator. Numerator and denominator
+//   then use the same weights, so a row dominated by one key returns that key's V row
+//   however P'' rounds. The LSE uses the sum of the unrounded fp32 probabilities.
 //   V^T is gathered with ds_read_b64_tr_b8 (8-bit LDS transpose reads) in the key order
 //   the S^T accumulators give P.
 #include "device_common.h"
@@ -155,17 +160,33 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     }
   };
 
-  f32x16 oacc[NDB], lacc = f32x16{};   // P'.V (in units of the current V scale) and sum of rounded P'
+  f32x16 oacc[NDB], lacc = f32x16{};   // P''.V (in units of U) and the last tile's sum of rounded P''
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   // Running max M (log2 units), this lane's partial row sum of the unrounded
   // probabilities (for the LSE), and a pending rescale factor of the accumulators.
   float M = -INFINITY, l_part = 0.f, alpha_pend = 1.f;
-  float sv_units = 1.f;      // the V block scale the P.V accumulator is expressed in
+  // Unit U of the P.V accumulator (a V block scale), an owed change of unit, and the
+  // denominator: the sum over tiles of (sum of the tile's rounded P'' codes) * w.
+  float U = 1.f, unit_pend = 1.f, l_rnd = 0.f;
 
   // Per-tile constants of tile u: score factor and V block scale.
-  auto tile_c = [&](int u) __attribute__((always_inline)) { return cq * sk[min(u * kBN / kScaleRows, nblk - 1)]; };
+  auto tile_sk = [&](int u) __attribute__((always_inline)) { return sk[min(u * kBN / kScaleRows, nblk - 1)]; };
+  auto tile_c = [&](int u) __attribute__((always_inline)) { return cq * tile_sk(u); };
   auto tile_sv = [&](int u) __attribute__((always_inline)) { return sv[min(u * kBN / kScaleRows, nblk - 1)]; };
+  // w = U / svb of a tile with V block scale svb; when svb / U leaves [1, 3/2] the unit
+  // moves to svb (w = 1) and the accumulator owes the factor old U / new U. Returns
+  // whether the unit moved (wave-uniform: both scales are).
+  auto weight = [&](float svb, float& w) __attribute__((always_inline)) -> bool {
+    if (svb >= U && svb <= 1.5f * U) {
+      w = U * __builtin_amdgcn_rcpf(svb);
+      return false;
+    }
+    unit_pend *= U * __builtin_amdgcn_rcpf(svb);
+    U = svb;
+    w = 1.f;
+    return true;
+  };
 
   auto mask_tile = [&](int u, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
     const int key0 = u * kBN;
@@ -185,11 +206,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
       m4[(e / 2) % 4] = max3f(m4[(e / 2) % 4], S[e / 16][e % 16], S[e / 16][e % 16 + 1]);
   };
   // Raise M when some row of the wave grew by more than kTau (branch-free); l is
-  // rescaled at once, O at the start of the next step. Returns whether M moved.
-  auto max_final = [&](const float (&m4)[4], float ct) __attribute__((always_inline)) -> bool {
+  // rescaled at once, O at the start of the next step. Returns whether M moved. A row
+  // whose M moves to this tile's max takes M = max - log2 w (lw), so that its largest
+  // probability is coded as P'' = 2^kPShift exactly, as with w = 1.
+  auto max_final = [&](const float (&m4)[4], float ct, float lw) __attribute__((always_inline)) -> bool {
     const float mx = max_halves(max3f(m4[0], m4[1], __builtin_elementwise_maximum(m4[2], m4[3]))) * ct;
     const bool grow = __builtin_amdgcn_ballot_w64(mx > M + kTau) != 0;
-    const float M_new = grow ? __builtin_elementwise_maximum(M, mx) : M;
+    const float M_new = grow ? __builtin_elementwise_maximum(M, mx - lw) : M;
     const float alpha = grow ? fast_exp2(M - M_new) : 1.f;
     M = M_new;
     l_part *= alpha;
@@ -217,18 +240,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
       if (e % 4 == 3) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(S[e / 16][e % 16 - 1], pe, P[e / 4], true);
     }
   };
-  // Owed running-max rescale, and (at the first tile of a V scale block) the change of
-  // V units sv_old / sv_new of the P.V accumulator.
-  auto rescale = [&](float sv_ratio) __attribute__((always_inline)) {
+  // Owed running-max rescale (accumulator and rounded-code denominator) and change of
+  // unit (accumulator only: the denominator is in units of P').
+  auto rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha_pend * sv_ratio;
-    lacc *= alpha_pend;
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha_pend * unit_pend;
+    l_rnd *= alpha_pend;
     alpha_pend = 1.f;
+    unit_pend = 1.f;
   };
 
   f32x16 Sa[NKB], Sb[NKB];
   int Pa[8], Pb[8];
   bool pend = false;     // wave-uniform: an O rescale is owed
+  // w of the tile whose code sum lacc holds, and of the tile whose softmax ran last; the
+  // K and V block scales of the tile whose softmax runs next, loaded one step early so
+  // that their scalar loads complete under the step's barrier.
+  float w_lacc = 0.f, w_soft = 0.f, sk_next = 0.f, sv_next = 1.f;
 
   // Step t: S(t+1) in S_soft, S(t+2) -> S_new, P(t) in P_use, P(t+1) -> P_new;
   // K(t+2) in K slot (t+2)%4, V(t) in V slot t%4; loads K(t+4) -> K slot t%4 and
@@ -242,15 +270,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     // Causal: once the tile's first key lies past this wave's last row, this and every
     // later tile are fully masked for the wave; it only keeps up its loads and barriers.
     if (!CAUSAL || t * kBN <= q0 + 31) {
-      if constexpr (decltype(VRD)::value % 2 == 0) {   // t even: tile t opens a V scale block
-        const float sv_new = tile_sv(t);
-        rescale(t > 0 ? sv_units * __builtin_amdgcn_rcpf(sv_new) : 1.f);
-        sv_units = sv_new;
-      } else {
-        if (pend) rescale(1.f);
-      }
+      l_rnd = __builtin_fmaf(lacc[0], w_lacc, l_rnd);    // tile t-1's rounded codes
+      w_lacc = w_soft;                                    // tile t, whose codes lacc sums next
+      if (pend) rescale();
       mask_tile(t + 1, S_soft);
-      const float ct = tile_c(t + 1);
+      const float ct = cq * sk_next;
+      const bool uchg = weight(sv_next, w_soft);
+      const float lw = __builtin_amdgcn_logf(w_soft);     // log2 w
       // Main block in issue order: 4 S^T MFMAs (K fragments one MFMA ahead) and 4 P.V
       // MFMAs (V^T fragments one MFMA ahead); the row max runs beside the first two S^T
       // MFMAs, the exponentials beside the other six.
@@ -288,8 +314,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
           max_pairs(m4, S_soft, 4, 18);
         } else if (i == 1) {
           max_pairs(m4, S_soft, 18, NKB * 16);
-          pend = max_final(m4, ct);
-          bias = M - kPShift;
+          pend = max_final(m4, ct, lw) | uchg;
+          bias = M - kPShift + lw;
           args(S_soft, ct, bias, lo(0), lo(1));
         } else {
           exps_slot(i - 2);
@@ -304,12 +330,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
           // all-ones A operand (E4M3 1.0), built here from a value tied to t so that it is
           // not kept live across the loop (t < 2^30, so the shift adds 0)
           const int one4 = 0x38383838 + (t >> 30);
-          lacc = mfma_fp8(i32x8{one4, one4, one4, one4, one4, one4, one4, one4}, pb, lacc);
+          lacc = mfma_fp8(i32x8{one4, one4, one4, one4, one4, one4, one4, one4}, pb, f32x16{});
         }
         exps_slot(2 + db);
       }
       finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
-      l_part += lsum[0] + lsum[1];
+      l_part = __builtin_fmaf(lsum[0] + lsum[1], w_soft, l_part);
+      sk_next = tile_sk(t + 2);
+      sv_next = tile_sv(t + 2);
     }
     wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
     barrier_lds();
@@ -331,14 +359,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     const float ct = tile_c(0);
     float m4[4] = {Sa[0][0], Sa[0][1], Sa[0][2], Sa[0][3]};
     max_pairs(m4, Sa, 4, NKB * 16);
-    max_final(m4, ct);
+    max_final(m4, ct, 0.f);       // tile 0 has w = 1
     alpha_pend = 1.f;            // O is still zero: no rescale owed
+    U = tile_sv(0);              // the first tile sets the unit: w = 1
+    w_soft = 1.f;
     const float bias = M - kPShift;
     float lsum[2] = {0.f, 0.f};
     args(Sa, ct, bias, 0, NKB * 16);
     exps(Sa, 0, NKB * 16);
     finish(Sa, Pa, lsum, 0, NKB * 16);
-    l_part += lsum[0] + lsum[1];
+    l_part = __builtin_fmaf(lsum[0] + lsum[1], w_soft, l_part);
+    sk_next = tile_sk(1);
+    sv_next = tile_sv(1);
   }
   qk(IC<1>{}, Sb);
   barrier_lds();                 // K slots 0 and 1 are refilled from step 0 on
@@ -350,11 +382,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{});
   }
   wait_vmcnt<0>();               // no load may still target this workgroup's LDS when it exits
-  if (pend) rescale(1.f);
+  l_rnd = __builtin_fmaf(lacc[0], w_lacc, l_rnd);       // the last tile's rounded codes
+  if (pend) rescale();
 
   const float l_tot = add_halves(l_part) * (1.f / (1 << (int)kPShift));   // sum of probabilities
   if (qrow >= N) return;
-  const float inv = sv_units / lacc[0];
+  const float inv = U / l_rnd;
   uint16_t* Orow = O + head_off + (int64_t)qrow * kD;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)

@@ -87,9 +87,11 @@ attn_status_t attn_fwd_f32(const float* q, const float* k, const float* v, float
  * decode(x) * scale[b, h, t]. O is bf16 [B, H, N, d], LSE fp32 [B, H, N]. Scores
  * accumulate e4m3 x e4m3 products in fp32 and are scaled by q_scale * k_scale * scale;
  * the probabilities enter the P.V contraction (fp32 accumulation) as E4M3 codes of
- * 2^6 * P relative to a running max that trails the true one by at most 2 (log2 units),
- * so codes stay <= 256; O is divided by the sum of those rounded codes and the LSE uses
- * the unrounded fp32 sum. All scales must be finite and > 0. */
+ * 2^6 * P / w relative to a running max that trails the true one by at most 2 (log2
+ * units), where w = U / v_scale[key block] in [2/3, 1] carries the key's V block scale
+ * against the accumulator's unit U (a V block scale, moved only when w would leave that
+ * range), so codes stay <= 384; O is divided by the sum of those rounded codes times w
+ * and the LSE uses the unrounded fp32 sum. All scales must be finite and > 0. */
 attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                            const float* q_scale, const float* k_scale, const float* v_scale,
                            void* o, float* lse,

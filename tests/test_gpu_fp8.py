@@ -175,6 +175,30 @@ def test_fp8_scores_jumping_past_the_first_tile_max(factor, causal):
     compare(O, L, Oref, Lref, f"fp8 jump x{factor} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_v_block_scales_far_apart(causal):
+    # V's 128-row blocks are scaled by factors between 1/64 and 5/4 before quantisation, so
+    # neighbouring V block scales differ by up to 64x: where the ratio of a block's scale to
+    # the accumulator's unit leaves [1/4, 3/2] the accumulator changes unit, elsewhere the
+    # ratio rides in the exp2 argument. Both must give the weights the oracle uses.
+    B, H, N, d = 1, 2, 1300, 128
+    say(f"case fp8 V block scales far apart causal={causal}")
+    q, k, v, signs = inputs.draw_fp8_workload(53, B, H, N, d)
+    v = v.copy()
+    f = np.array([1, 1 / 16, 1, 0.5, 1 / 64, 0.75, 1, 1 / 8, 1.25, 1 / 32, 1, 0.3], dtype=np.float32)
+    for b in range((N + 127) // 128):
+        v[:, :, b * 128:(b + 1) * 128] *= f[b % len(f)]
+    xs = [bf16_activations(t)[1] for t in (q, k, v)]
+    p = ofp8.prepare_fp8(*xs, signs)
+    sv = p["sv"][0, 0]
+    assert sv.max() / sv.min() > 32
+    deq = [ofp8.dequantize_blocks(p[c], p[s]) for c, s in (("q8", "sq"), ("k8", "sk"), ("v8", "sv"))]
+    scale = inputs.softmax_scale(d)
+    O, L = run_fp8(p, causal, scale)
+    Oref, Lref = attention_forward(*deq, causal, scale)
+    compare(O, L, Oref, Lref, f"fp8 V block scales far apart causal={causal}")
+
+
 def test_rotation_study_across_outlier_layouts():
     # fp8 error against exact attention on the unquantised inputs, with and without the
     # Hadamard rotation, for four outlier layouts ("8.3 FlashAttention-3", section 5.2
