@@ -119,6 +119,16 @@ def test_full_size_sampled(name, causal, dtype):
     check(cpu, gpu, dtype, causal, rows=sample_rows(w.N), heads=heads)
 
 
+def test_metric_workload_every_head_sampled():
+    # The benchmarked call (bf16, causal, B2 H16 N8192 d128, in the launch configuration the
+    # benchmark times: fast pass, then exact pass) checked on every one of its 32 heads, on
+    # rows that include the first and last rows of query tiles and of the sequence.
+    w = inputs.WORKLOADS["H"]
+    say("case H every head, sampled rows")
+    cpu, gpu = make(w.wid, w.B, w.H, w.N, w.d, "bf16")
+    check(cpu, gpu, "bf16", True, rows=sample_rows(w.N, n_random=24, seed=11))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_long_sequence_sampled(causal):
     # One long head, N = 65536 + 33 (bf16, d = 128): 1025 key tiles with a ragged last

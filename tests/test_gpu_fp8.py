@@ -121,6 +121,19 @@ def test_fp8_attention_c5_sampled():
     compare(O[:, :, rows][idx], L[:, :, rows][idx], Oref[idx], Lref[idx], "C5 sampled")
 
 
+def test_fp8_attention_c5_every_head_sampled():
+    # The fp8 workload on every one of its 32 heads, on rows that include the first rows
+    # (few keys, where single weights dominate) and the ends of query tiles.
+    w = inputs.WORKLOADS["C5"]
+    say("case fp8 attention C5 every head, sampled rows")
+    p, deq, _, _ = oracle_inputs(w.wid, w.B, w.H, w.N, w.d)
+    O, L = run_fp8(p, True, w.scale)
+    rows = np.unique(np.concatenate([np.arange(0, 8), [255, 256, 4095, 4096, w.N - 1],
+                                     np.random.default_rng(12).integers(0, w.N, 24)]))
+    Oref, Lref = attention_forward(*deq, True, w.scale, rows=rows)
+    compare(O[:, :, rows], L[:, :, rows], Oref, Lref, "C5 every head")
+
+
 def test_fp8_end_to_end_gpu_quantiser():
     # GPU quantiser -> GPU fp8 attention, against oracle quantiser -> oracle attention.
     B, H, N, d = 1, 2, 640, 128
