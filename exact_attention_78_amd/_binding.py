@@ -217,8 +217,10 @@ def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=None
         scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
     L = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
-    _require(o.shape == (B, H, N, d) and o.dtype == torch.bfloat16 and o.is_contiguous(), "bad out")
-    _require(L.shape == (B, H, N) and L.dtype == torch.float32 and L.is_contiguous(), "bad lse")
+    _require(o.shape == (B, H, N, d) and o.dtype == torch.bfloat16 and o.is_contiguous() and o.device == q8.device,
+             "bad out")
+    _require(L.shape == (B, H, N) and L.dtype == torch.float32 and L.is_contiguous() and L.device == q8.device,
+             "bad lse")
     with torch.cuda.device(q8.device):
         st = library().attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
                                     k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), L.data_ptr(), B, H, N, d,
@@ -239,6 +241,10 @@ def attn_quant_fp8(x, signs=None, out=None, scales=None):
                  and signs.device == x.device, "signs must be fp32 [d] on x's device")
     x8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device) if out is None else out
     sc = torch.empty((B, H, nblk), dtype=torch.float32, device=x.device) if scales is None else scales
+    _require(x8.shape == (B, H, N, d) and x8.dtype == torch.uint8 and x8.is_contiguous() and x8.device == x.device,
+             "out must be a contiguous uint8 [B, H, N, d] tensor on x's device")
+    _require(sc.shape == (B, H, nblk) and sc.dtype == torch.float32 and sc.is_contiguous() and sc.device == x.device,
+             "scales must be a contiguous fp32 [B, H, ceil(N/128)] tensor on x's device")
     with torch.cuda.device(x.device):
         st = library().attn_quant_fp8(x.data_ptr(), x8.data_ptr(), sc.data_ptr(),
                                       None if signs is None else signs.data_ptr(), B, H, N, d, _stream(x))

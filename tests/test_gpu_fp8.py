@@ -149,6 +149,21 @@ def test_fp8_end_to_end_gpu_quantiser():
     compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), Oref, Lref, "end-to-end")
 
 
+def test_binding_rejects_bad_output_tensors():
+    # The binding checks caller-provided outputs before any call into the library.
+    x = torch.zeros((1, 1, 256, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        attn_quant_fp8(x, None, out=torch.empty((1, 1, 256, 128), dtype=torch.int8, device="cuda"))
+    with pytest.raises(ValueError):
+        attn_quant_fp8(x, None, scales=torch.empty((1, 1, 1), dtype=torch.float32, device="cuda"))
+    q8, sq = attn_quant_fp8(x, None)
+    with pytest.raises(ValueError):
+        attn_fwd_fp8(q8, q8, q8, sq, sq, sq, out=torch.empty((1, 1, 256, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        attn_fwd_fp8(q8, q8, q8, sq, sq, sq, lse=torch.empty((1, 1, 256), dtype=torch.float32))
+    torch.cuda.synchronize()
+
+
 def test_rotation_lowers_fp8_error_with_outliers():
     # Direction of the incoherent-processing claim ("8.3 FlashAttention-3", section 5.2):
     # with outlier channels shared by Q and K, the fp8 path's error against exact
