@@ -119,3 +119,25 @@ def test_dispatch_stream_and_determinism():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_tensors_over_2_31_elements():
+    # B1 H4100 N4096 d128 bf16, causal: Q, K, V, O, dO and the gradients each hold 2.15e9
+    # elements (> 2^31, 4.3 GB), so the heads past 4096 sit beyond 32-bit element offsets.
+    # Inputs are drawn on the device; three heads (first, middle, last) are read back and
+    # their gradients checked in full.
+    B, H, N, d = 1, 4100, 4096, 128
+    assert B * H * N * d > 2**31
+    say(f"case >2^31 elements backward: B{B} H{H} N{N} d{d} bf16 causal")
+    gq, gk, gv, gg = (inputs.normal_on_device(41, t, (B, H, N, d), torch.bfloat16) for t in range(4))
+    scale = inputs.softmax_scale(d)
+    o, lse = attn_fwd_bf16(gq, gk, gv, causal=True, scale=scale)
+    dq, dk, dv = attn_bwd_bf16(gq, gk, gv, o, lse, gg, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    hs = [0, H // 2, H - 1]
+    cpu = [t[:, hs].cpu() for t in (gq, gk, gv, gg)]
+    got = [t[:, hs].double().cpu().numpy() for t in (dq, dk, dv)]
+    del gq, gk, gv, gg, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    ref = attention_backward(*cpu, True, scale)
+    compare(got, ref, f"heads {hs}")

@@ -84,3 +84,31 @@ def test_decode_reuses_caller_buffers_and_is_deterministic():
     attn_decode_bf16(tq, tk, tv, out=o2, lse=l2, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_cache_over_2_31_elements():
+    # B16 H16, one query row against Nk = 66000 keys, d128 bf16: K and V each hold 2.16e9
+    # elements (> 2^31, 4.3 GB), so the last heads' cache rows sit beyond 32-bit element
+    # offsets. Inputs are drawn on the device; three heads (first, middle, last) are read
+    # back and checked in full.
+    B, H, Nq, Nk, d = 16, 16, 1, 66000, 128
+    assert B * H * Nk * d > 2**31
+    say(f"case >2^31 elements decode: B{B} H{H} Nq{Nq} Nk{Nk} d{d} bf16")
+    q = inputs.normal_on_device(42, inputs.Q_ID, (B, H, Nq, d), torch.bfloat16)
+    k = inputs.normal_on_device(42, inputs.K_ID, (B, H, Nk, d), torch.bfloat16)
+    v = inputs.normal_on_device(42, inputs.V_ID, (B, H, Nk, d), torch.bfloat16)
+    scale = inputs.softmax_scale(d)
+    o, lse = attn_decode_bf16(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (B // 2, H // 2), (B - 1, H - 1)]
+    O = np.stack([o[b, h].double().cpu().numpy() for b, h in heads])[None]
+    L = np.stack([lse[b, h].double().cpu().numpy() for b, h in heads])[None]
+    cpu = [torch.stack([t[b, h] for b, h in heads])[None].cpu() for t in (q, k, v)]
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    Oref, Lref = attention_forward(*cpu, False, scale)
+    assert np.isfinite(O).all() and np.isfinite(L).all()
+    eo = np.abs(O - Oref).max()
+    el = (np.abs(L - Lref) / np.maximum(1, np.abs(Lref))).max()
+    say(f"  heads {heads}: max|dO|={eo:.3e} max rel dLSE={el:.3e}")
+    assert eo <= O_TOL and el <= LSE_REL
