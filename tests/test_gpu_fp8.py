@@ -259,3 +259,37 @@ def test_rotation_study_across_outlier_layouts():
         say(f"  {name}: RMSE rotated {errs[True]:.4e}, unrotated {errs[False]:.4e}, "
             f"unrotated/rotated {ratios[name]:.2f}")
     assert ratios["shared channels"] > 1.0
+
+
+def test_tensors_over_2_31_elements():
+    # B1 H4100 N4096 d128: the bf16 activations and the E4M3 codes each hold 2.15e9
+    # elements (> 2^31), so the heads past 4096 sit beyond 32-bit element offsets. Q and K
+    # are rotated and quantised on the device, V quantised, then fp8 attention (causal).
+    # Three heads (first, middle, last) are read back: codes and scales bit-exact against
+    # the oracle's quantiser, O and LSE against the oracle on sampled rows.
+    B, H, N, d = 1, 4100, 4096, 128
+    assert B * H * N * d > 2**31
+    say(f"case >2^31 elements fp8: B{B} H{H} N{N} d{d} causal")
+    xs = [inputs.normal_on_device(43, t, (B, H, N, d), torch.bfloat16) for t in range(3)]
+    signs = np.where(inputs.generator(43, inputs.SIGN_ID).integers(0, 2, size=d) == 1, 1.0, -1.0).astype(np.float32)
+    sg = torch.from_numpy(signs).cuda()
+    q8, sq = attn_quant_fp8(xs[0], sg)
+    k8, sk = attn_quant_fp8(xs[1], sg)
+    v8, sv = attn_quant_fp8(xs[2], None)
+    scale = inputs.softmax_scale(d)
+    o, lse = attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    hs = [0, H // 2, H - 1]
+    acts = [x[:, hs].float().cpu().numpy() for x in xs]
+    got = {n: t[:, hs].cpu().numpy() for n, t in (("q8", q8), ("sq", sq), ("k8", k8), ("sk", sk), ("v8", v8), ("sv", sv))}
+    O = o[:, hs].double().cpu().numpy()
+    L = lse[:, hs].double().cpu().numpy()
+    del xs, q8, k8, v8, sq, sk, sv, o, lse
+    torch.cuda.empty_cache()
+    p = ofp8.prepare_fp8(*acts, signs)
+    for n in ("q8", "sq", "k8", "sk", "v8", "sv"):
+        np.testing.assert_array_equal(got[n], p[n])
+    deq = [ofp8.dequantize_blocks(p[c], p[s]) for c, s in (("q8", "sq"), ("k8", "sk"), ("v8", "sv"))]
+    rows = np.unique(np.concatenate([np.arange(0, 4), [255, 256, N - 1], np.random.default_rng(13).integers(0, N, 24)]))
+    Oref, Lref = attention_forward(*deq, True, scale, rows=rows)
+    compare(O[:, :, rows], L[:, :, rows], Oref, Lref, f"heads {hs}: quantiser bit-exact")
