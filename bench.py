@@ -3,16 +3,25 @@
 
 Metric: attention forward TFLOP/s for bf16, causal, head dim 128, N = 8192
 (B = 2, H = 16), counting 4*B*H*N^2*d FLOPs halved for causal, and the fraction of
-the dense bf16 MFMA peak. One step is one forward pass of the whole path (workgroup
+the dense bf16 MFMA peak. One step is one forward call of the whole path (workgroup
 order, Q/K/V loads, both MFMA contractions, masking, online softmax, epilogue) over
 one batch of seeded synthetic inputs that are already resident in HBM.
 
-Prints ONE JSON line. Also reported, outside ``value``: the backward pass of the same
-bf16 workload (dQ, dK, dV from a seeded dO; 2.5 times the forward FLOPs), the fp8 path
-on the fp8 workload (B = 2, H = 16, N = 8192, d = 128, causal: quantiser and attention
-timed separately), one split-KV decoding step (B = 16, H = 16, 1 query row against
-8192 keys; HBM-bound, reported in GB/s), and the CPU oracle timed on a bounded sample
-of the bf16 workload.
+Prints ONE JSON line. Besides the headline it reports, from the same run:
+  calibration  what a dense MFMA loop and a dense exp2 loop sustain at the loaded clock,
+               and a large bf16 GEMM through torch (hipBLASLt)
+  forward      the headline call's per-launch statistics (median, min, std over the
+               timed launches), the exact (running-max) pass alone on the same inputs,
+               the same call on inputs whose query tiles all need the exact pass, the
+               tile schedules and persistent grids, configurations C1-C4 (C2 also with
+               a cold cache), and the exponentials/s secondary bound
+  backward     dQ, dK, dV of the headline call (2.5x the forward FLOPs)
+  fp8          quantiser and fp8 attention on the fp8 workload (B2 H16 N8192 d128 causal)
+  decode       one split-KV decoding step (B16 H16, 1 query row, 8192 keys; GB/s)
+  cpu_baseline the CPU oracle on whole heads of the headline workload, on every core of
+               this process's affinity set
+The extra legs run before the headline's warm-up and timed steps, so the headline is
+timed at the clock the chip holds under sustained load.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -23,11 +32,14 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+from exact_attention_78_amd.flops import counted_flops, counted_flops_backward  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 MFMA peak
 PEAK_FP8_TFLOPS = 5000.0      # MI355X published dense fp8 MFMA peak
@@ -68,64 +80,155 @@ def read_counters(key="hbm_bytes_per_launch"):
         return None
 
 
-def counted_flops(B, H, N, d, causal):
-    """4*B*H*N^2*d (two N x N x d contractions), halved for causal."""
-    f = 4.0 * B * H * N * N * d
-    return f / 2 if causal else f
-
-
-def timed(fn, steps, warmup, torch):
-    """Average time of fn() in ms over `steps` calls on the current stream (HIP events)."""
+def time_launches(torch, fn, steps, warmup, reps=1, between=None):
+    """Run fn() `warmup` times untimed, then `steps` timed launches (each a group of `reps`
+    back-to-back calls) with one HIP event pair per launch on the current stream (the
+    stream the library launches on). `between`, if given, runs untimed before each timed
+    launch (e.g. a cache flush). Returns per-call milliseconds: mean over the whole timed
+    region, and median / min / std over the launches."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    if between is None:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for i in range(steps):
+            for _ in range(reps):
+                fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) / reps for i in range(steps)]
+        total = ev[0].elapsed_time(ev[steps]) / (steps * reps)
+    else:
+        per = []
+        for _ in range(steps):
+            between()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / reps)
+        total = sum(per) / steps
+    return {"mean_ms": total, "median_ms": statistics.median(per), "min_ms": min(per),
+            "std_ms": statistics.pstdev(per) if len(per) > 1 else 0.0, "launches": steps, "calls_per_launch": reps}
 
 
-def cpu_baseline(q, k, v, causal, scale, budget_s):
-    """Time the oracle (as it stands) on whole heads of the workload until the budget is used."""
-    from threadpoolctl import threadpool_info
+def us(t):
+    return {k: (v * 1e3 if k.endswith("_ms") else v) for k, v in t.items()}
 
-    from oracle.attention import attention_forward
 
-    B, H, N, d = q.shape
-    heads = [(b, h) for b in range(B) for h in range(H)]
-    done, t0 = 0, time.perf_counter()
-    for b, h in heads:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        attention_forward(q[sl], k[sl], v[sl], causal, scale)
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    flops = counted_flops(1, done, N, d, causal)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {B * H} heads (all {N} query rows each, causal) of the bf16 B2 H16 N8192 d128 "
-                      f"workload, fp64 NumPy, {dt:.1f} s"}
+def rate(work, t, scale=1e12):
+    return work / (t["mean_ms"] * 1e-3) / scale
+
+
+# ----------------------------------------------------------------------------- legs
+
+
+def calibration_leg(torch, ea):
+    """Dense MFMA and exp2 loops (one 8-wave workgroup per CU, the attention kernels'
+    launch shape), and an 8192^3 bf16 GEMM through torch.matmul (hipBLASLt)."""
+    res = {}
+    wg = torch.cuda.get_device_properties(0).multi_processor_count
+    for kind, iters, unit, scale in (("mfma", 4000, "TFLOP/s", 1e12), ("exp", 8000, "Gexp/s", 1e9)):
+        out, ops = ea.attn_calibrate(kind, wg, iters)
+        t = time_launches(torch, lambda: ea.attn_calibrate(kind, wg, iters, out=out), 5, 3)
+        res[f"{kind}_loop"] = {"value": rate(ops, t, scale), "unit": unit, "us": t["mean_ms"] * 1e3,
+                               "workgroups": wg}
+    res["mfma_loop"]["frac_of_published_peak"] = res["mfma_loop"]["value"] / PEAK_BF16_TFLOPS
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    t = time_launches(torch, lambda: torch.matmul(a, b, out=c), 10, 5)
+    res["gemm_bf16_8192"] = {"value": rate(2.0 * n ** 3, t), "unit": "TFLOP/s", "us": t["mean_ms"] * 1e3,
+                             "frac_of_published_peak": rate(2.0 * n ** 3, t) / PEAK_BF16_TFLOPS,
+                             "library": "torch.matmul (hipBLASLt)"}
+    del a, b, c
+    return res
+
+
+def forward_legs(torch, ea, inputs, w, gq, gk, gv, o, lse, steps, warmup, calib):
+    """Exact pass alone, all tiles needing the exact pass, schedules, C1-C4, C2 cold, exps/s."""
+    res = {}
+    flops = counted_flops(w.B, w.H, w.N, w.d, True)
+
+    def leg(fn, work=flops, n=steps, wu=warmup, **kw):
+        t = time_launches(torch, fn, n, wu, **kw)
+        return {"us": us(t), "tflops": rate(work, t), "frac_bf16_peak": rate(work, t) / PEAK_BF16_TFLOPS}
+
+    res["exact_pass_only"] = leg(lambda: ea.attn_fwd_variant(gq, gk, gv, causal=True, scale=w.scale, passes="exact",
+                                                             out=o, lse=lse))
+    res["exact_pass_only"]["what"] = ("the running-max online softmax alone on every tile (per-tile row max, lazy "
+                                      "rescale), same inputs as the headline")
+    # keys from 300 on scaled x30: every query tile past row 300 outgrows the first tile's max
+    import numpy as np
+
+    k_marked = inputs.normal_f32(w.wid, inputs.K_ID, (w.B, w.H, w.N, w.d))
+    k_marked[:, :, 300:] *= np.float32(30.0)
+    gkm = inputs.to_torch(k_marked, "bf16").cuda()
+    del k_marked
+    res["all_tiles_marked"] = leg(lambda: ea.attn_fwd_bf16(gq, gkm, gv, causal=True, scale=w.scale, out=o, lse=lse))
+    res["all_tiles_marked"]["what"] = ("the headline call on inputs whose keys from 300 on are scaled x30: the first "
+                                       "pass marks every query tile that sees them and stops, the exact pass redoes them")
+    del gkm
+
+    sched = {}
+    queue = ea.queue_workspace()
+    for s in ea._binding.SCHEDULES:
+        sched[s] = leg(lambda s=s: ea.attn_fwd_variant(gq, gk, gv, causal=True, scale=w.scale, sched=s, queue=queue,
+                                                       out=o, lse=lse), n=max(5, steps // 2), wu=3)
+    res["schedules_H"] = {k: {"us": v["us"]["mean_us"], "tflops": v["tflops"]} for k, v in sched.items()}
+    for name in ("C3", "C4"):
+        c = inputs.WORKLOADS[name]
+        q, k, v = (inputs.to_torch(x, "bf16").cuda() for x in inputs.draw_qkv(c.wid, c.B, c.H, c.N, c.d))
+        oc, lc = torch.empty_like(q), torch.empty((c.B, c.H, c.N), device="cuda", dtype=torch.float32)
+        f = counted_flops(c.B, c.H, c.N, c.d, True)
+        out = {}
+        for s in ("default", "persistent_stride", "persistent_queue", "linear_natural"):
+            r = leg(lambda s=s: ea.attn_fwd_variant(q, k, v, causal=True, scale=c.scale, sched=s, queue=queue,
+                                                    out=oc, lse=lc), work=f, n=max(5, steps // 2), wu=3)
+            out[s] = {"us": r["us"]["mean_us"], "tflops": r["tflops"]}
+        res[f"schedules_{name}_causal"] = out
+        del q, k, v, oc, lc
+
+    cfg = {}
+    for name, causal in (("C1", False), ("C1", True), ("C2", True), ("C3", True), ("C3", False), ("C4", True)):
+        c = inputs.WORKLOADS[name]
+        dt = "f32" if name == "C1" else "bf16"
+        q, k, v = (inputs.to_torch(x, dt).cuda() for x in inputs.draw_qkv(c.wid, c.B, c.H, c.N, c.d))
+        f = counted_flops(c.B, c.H, c.N, c.d, causal)
+        call = lambda: ea.fwd(q, k, v, causal=causal, scale=c.scale)   # noqa: E731
+        small = name in ("C1", "C2")
+        r = leg(call, work=f, n=10 if small else max(5, steps // 2), wu=10 if small else 3, reps=50 if small else 1)
+        key = f"{name}_{'causal' if causal else 'noncausal'}"
+        cfg[key] = {"workload": f"{dt} B{c.B} H{c.H} N{c.N} d{c.d} {'causal' if causal else 'non-causal'}",
+                    "us": r["us"], "tflops": r["tflops"], "frac_bf16_peak": r["frac_bf16_peak"] if dt == "bf16" else None}
+        if name == "C2":
+            scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+            rc = leg(call, work=f, n=10, wu=2, between=lambda: scratch.fill_(1))
+            cfg[key + "_cold"] = {"workload": cfg[key]["workload"] + ", L2/MALL flushed by a 512 MiB write before "
+                                  "each launch", "us": rc["us"], "tflops": rc["tflops"]}
+            del scratch
+        del q, k, v
+    res["configs"] = cfg
+    return res
 
 
 def backward_leg(torch, ea, inputs, w, tensors, o, lse, steps, warmup):
-    """The backward pass of the forward call just timed (same inputs, its O and LSE)."""
+    """The backward pass of the forward call timed (same inputs, its O and LSE)."""
     gq, gk, gv = tensors
     g = inputs.to_torch(inputs.draw_dout(w.wid, w.B, w.H, w.N, w.d), "bf16").cuda()
     ea.attn_fwd_bf16(gq, gk, gv, causal=True, scale=w.scale, out=o, lse=lse)
     dq, dk, dv = (torch.empty_like(gq) for _ in range(3))
     ws = torch.empty((2, w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-    ms = timed(lambda: ea.attn_bwd_bf16(gq, gk, gv, o, lse, g, causal=True, scale=w.scale, dq=dq, dk=dk, dv=dv,
-                                        workspace=ws), steps, warmup, torch)
-    flops = 2.5 * counted_flops(w.B, w.H, w.N, w.d, True)
-    assert all(bool(torch.isfinite(t.float()).all()) for t in (dq, dk, dv))
+    t = time_launches(torch, lambda: ea.attn_bwd_bf16(gq, gk, gv, o, lse, g, causal=True, scale=w.scale, dq=dq, dk=dk,
+                                                      dv=dv, workspace=ws), steps, warmup)
+    flops = counted_flops_backward(w.B, w.H, w.N, w.d, True)
+    assert all(bool(torch.isfinite(x.float()).all()) for x in (dq, dk, dv))
     return {"workload": "bf16 causal attention backward (dQ, dK, dV), B=2 H=16 N=8192 d=128",
-            "us": ms * 1e3, "tflops": flops / (ms * 1e-3) / 1e12,
-            "frac_bf16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "us": us(t), "tflops": rate(flops, t), "frac_bf16_peak": rate(flops, t) / PEAK_BF16_TFLOPS,
             "flop_convention": "2.5 x forward (five N x N x d contractions), halved for causal"}
 
 
@@ -138,17 +241,14 @@ def decode_leg(torch, ea, inputs, steps, warmup):
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
     ws = torch.empty(ea.library().attn_decode_workspace_floats(B, H, Nq, Nk, d), dtype=torch.float32, device="cuda")
-    ms = timed(lambda: ea.attn_decode_bf16(q, k, v, out=o, lse=lse, workspace=ws), steps, warmup, torch)
+    t = time_launches(torch, lambda: ea.attn_decode_bf16(q, k, v, out=o, lse=lse, workspace=ws), steps, warmup)
     nbytes = 2 * B * H * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4   # K, V, Q read; O, LSE written
     assert bool(torch.isfinite(o.float()).all())
     return {"workload": "bf16 decoding step, B=16 H=16 Nq=1 Nk=8192 d=128, no mask (split-KV)",
-            "us": ms * 1e3, "gbs": nbytes / (ms * 1e-3) / 1e9,
-            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            "us": us(t), "gbs": rate(nbytes, t, 1e9), "frac_hbm": rate(nbytes, t, 1e9) / PEAK_HBM_GBS}
 
 
 def fp8_leg(torch, ea, inputs, steps, warmup):
-    import numpy as np
-
     w = inputs.WORKLOADS["C5"]
     q, k, v, signs = inputs.draw_fp8_workload(w.wid, w.B, w.H, w.N, w.d)
     tq, tk, tv = (inputs.to_torch(x, "bf16").cuda() for x in (q, k, v))
@@ -163,8 +263,9 @@ def fp8_leg(torch, ea, inputs, steps, warmup):
         ea.attn_quant_fp8(tk, sg, out=k8, scales=sk)
         ea.attn_quant_fp8(tv, None, out=v8, scales=sv)
 
-    ms_q = timed(quant_all, steps, warmup, torch)
-    ms_a = timed(lambda: ea.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=True, out=o, lse=lse), steps, warmup, torch)
+    tqnt = time_launches(torch, quant_all, steps, warmup)
+    tatt = time_launches(torch, lambda: ea.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=True, out=o, lse=lse), steps,
+                         warmup)
     flops = counted_flops(w.B, w.H, w.N, w.d, True)
     n = w.B * w.H * w.N * w.d
     nblk = (w.N + 127) // 128
@@ -172,22 +273,39 @@ def fp8_leg(torch, ea, inputs, steps, warmup):
     assert bool(torch.isfinite(o.float()).all())
     return {
         "workload": "fp8 e4m3, causal, B=2 H=16 N=8192 d=128, Hadamard-rotated Q/K with shared outlier channels",
-        "attn_us": ms_a * 1e3, "attn_tflops": flops / (ms_a * 1e-3) / 1e12,
-        "attn_frac_fp8_peak": flops / (ms_a * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
-        "quant_qkv_us": ms_q * 1e3, "quant_gbs": qbytes / (ms_q * 1e-3) / 1e9,
-        "quant_frac_hbm": qbytes / (ms_q * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "attn_us": us(tatt), "attn_tflops": rate(flops, tatt), "attn_frac_fp8_peak": rate(flops, tatt) / PEAK_FP8_TFLOPS,
+        "quant_qkv_us": us(tqnt), "quant_gbs": rate(qbytes, tqnt, 1e9),
+        "quant_frac_hbm": rate(qbytes, tqnt, 1e9) / PEAK_HBM_GBS,
     }
+
+
+def cpu_baseline(q, k, v, causal, scale, budget_s):
+    """Time the oracle (as it stands) on whole heads of the workload, every core of this
+    process's affinity set working on (head, 1024-row chunk) units, until the budget is used."""
+    from oracle.pool import forward_pooled, host_cores
+
+    B, H, N, d = q.shape
+    cores = host_cores()
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    done, t0 = 0, time.perf_counter()
+    while done < len(heads) and time.perf_counter() - t0 < budget_s:
+        batch = heads[done:done + max(1, cores // 4)]
+        forward_pooled(q, k, v, causal, scale, heads=batch, workers=cores)
+        done += len(batch)
+    dt = time.perf_counter() - t0
+    flops = counted_flops(1, done, N, d, causal)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {B * H} heads (all {N} query rows each, causal) of the bf16 B2 H16 N8192 d128 "
+                      f"workload, fp64 NumPy on {cores} worker threads (one BLAS thread each), {dt:.1f} s"}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # The GPU needs a few tens of milliseconds of sustained load to reach its steady clock;
-    # 100 untimed steps (~60 ms here) get there before the timed region starts.
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--no-extra", action="store_true", help="skip the backward, fp8 and decode legs")
+    ap.add_argument("--no-extra", action="store_true", help="headline only: skip every other leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB x 4 (HBM counter calibration) and exit")
@@ -196,7 +314,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one MI355X only: --gpus {args.gpus} (WORLD_SIZE {world}) is not supported; "
-              f"run with --gpus 1", file=sys.stderr)
+              f"nothing here uses a second GPU. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -216,17 +334,30 @@ def main():
     w = inputs.WORKLOADS["H"]
     q, k, v = inputs.draw_qkv(w.wid, w.B, w.H, w.N, w.d)
     cpu = tuple(inputs.to_torch(x, "bf16") for x in (q, k, v))
+    del q, k, v
     gq, gk, gv = (t.cuda() for t in cpu)
     o = torch.empty_like(gq)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-    scale = w.scale
+    flops = counted_flops(w.B, w.H, w.N, w.d, True)
 
     def step():
-        ea.attn_fwd_bf16(gq, gk, gv, causal=True, scale=scale, out=o, lse=lse)
+        ea.attn_fwd_bf16(gq, gk, gv, causal=True, scale=w.scale, out=o, lse=lse)
 
-    ms = timed(step, args.steps, args.warmup, torch)
-    sclk = read_counters("sclk_ghz_estimate")
-    flops = counted_flops(w.B, w.H, w.N, w.d, True)
+    extra = {}
+    if not args.no_extra:
+        legs_steps, legs_warm = max(5, min(args.steps, 20)), max(3, min(args.warmup, 10))
+        extra["calibration"] = calibration_leg(torch, ea)
+        extra["forward"] = forward_legs(torch, ea, inputs, w, gq, gk, gv, o, lse, legs_steps, legs_warm,
+                                        extra["calibration"])
+        extra["backward"] = backward_leg(torch, ea, inputs, w, (gq, gk, gv), o, lse, legs_steps, legs_warm)
+        extra["fp8"] = fp8_leg(torch, ea, inputs, legs_steps, legs_warm)
+        extra["decode"] = decode_leg(torch, ea, inputs, legs_steps, 4 * legs_warm)
+
+    # the headline: W untimed steps, then exactly K timed steps, one event pair per launch
+    torch.cuda.synchronize()
+    t = time_launches(torch, step, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    ms = t["mean_ms"]
     tflops = flops / (ms * 1e-3) / 1e12
 
     out = {
@@ -245,22 +376,22 @@ def main():
         "config": {"workload": "bf16 causal attention forward, B=2 H=16 N=8192 d=128", "B": w.B, "H": w.H,
                    "N": w.N, "d": w.d, "causal": True, "flop_per_step": flops},
         "pct_of_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
-        # the engine clock under this load (counter run) and the peak scaled to it
-        "sclk_ghz": sclk,
-        "pct_of_peak_at_measured_clock": None if sclk is None else 100.0 * tflops / (PEAK_BF16_TFLOPS * sclk / 2.4),
+        "launch_us": us(t),
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": read_counters()},
     }
-    if not args.no_extra:
-        # each leg gets untimed calls of its own first (its kernels' first launches, and
-        # ~20 ms of load so the clock is at its steady state for that kernel mix)
-        legw = min(args.warmup, 10)
-        out["backward"] = backward_leg(torch, ea, inputs, w, (gq, gk, gv), o, lse, max(3, args.steps // 2), legw)
-        out["fp8"] = fp8_leg(torch, ea, inputs, max(3, args.steps // 2), 4 * legw)
-        out["decode"] = decode_leg(torch, ea, inputs, max(3, args.steps), 10 * legw)
+    if extra:
+        cal = extra["calibration"]
+        out["pct_of_attainable_mfma_loop"] = 100.0 * tflops / cal["mfma_loop"]["value"]
+        # secondary bound: one exponential per unmasked score (causal: N(N+1)/2 per head)
+        exps = w.B * w.H * w.N * (w.N + 1) / 2
+        extra["forward"]["exp_bound"] = {
+            "exps_per_call": exps, "exps_per_s": exps / (ms * 1e-3),
+            "frac_of_exp_loop": exps / (ms * 1e-3) / (cal["exp_loop"]["value"] * 1e9)}
+        out.update(extra)
     if not args.no_cpu_baseline:
-        qf, kf, vf = (t.float().numpy() for t in cpu)     # the bf16 values, upcast exactly
-        out["cpu_baseline"] = cpu_baseline(qf, kf, vf, True, scale, args.cpu_budget)
+        qf, kf, vf = (x.double().numpy() for x in cpu)    # the bf16 values, upcast exactly
+        out["cpu_baseline"] = cpu_baseline(qf, kf, vf, True, w.scale, args.cpu_budget)
     print(json.dumps(out))
 
 

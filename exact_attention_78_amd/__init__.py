@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     SIGNATURES,
     attn_bwd_bf16,
+    attn_calibrate,
     attn_bwd_f16,
     attn_decode_bf16,
     attn_decode_f16,
@@ -17,6 +18,8 @@ from ._binding import (  # noqa: F401
     attn_fwd_f16,
     attn_fwd_f32,
     attn_fwd_fp8,
+    attn_fwd_variant,
+    queue_workspace,
     attn_quant_fp8,
     bwd,
     fwd,

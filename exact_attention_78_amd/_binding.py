@@ -27,6 +27,7 @@ SIGNATURES = {
     "attn_fwd_bf16": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_fwd_f16": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_fwd_f32": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
+    "attn_fwd_variant": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _INT, _INT, _INT, _P, _P],
     "attn_fwd_fp8": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_quant_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "attn_bwd_bf16": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
@@ -34,6 +35,8 @@ SIGNATURES = {
     "attn_decode_bf16": [_P] * 6 + [_I64, _I64, _I64, _I64, _I64, _F32, _P],
     "attn_decode_f16": [_P] * 6 + [_I64, _I64, _I64, _I64, _I64, _F32, _P],
     "attn_decode_workspace_floats": [_I64, _I64, _I64, _I64, _I64],
+    "attn_calibrate": [_INT, _P, _P, _I64, _INT, _P],
+    "attn_calibrate_ops": [_INT, _INT],
     "attn_status_string": [_INT],
     "attn_abi_version": [],
 }
@@ -55,8 +58,8 @@ def library():
         for name, args in SIGNATURES.items():
             fn = getattr(lib, name)
             fn.argtypes = args
-            fn.restype = {"attn_status_string": ctypes.c_char_p,
-                          "attn_decode_workspace_floats": ctypes.c_int64}.get(name, ctypes.c_int)
+            fn.restype = {"attn_status_string": ctypes.c_char_p, "attn_decode_workspace_floats": ctypes.c_int64,
+                          "attn_calibrate_ops": ctypes.c_int64}.get(name, ctypes.c_int)
         _lib = lib
     return _lib
 
@@ -115,6 +118,65 @@ def attn_fwd_f16(q, k, v, causal=False, scale=None, out=None, lse=None):
 def attn_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None):
     """fp32 exact attention forward; returns (O fp32, LSE fp32)."""
     return _fwd("attn_fwd_f32", torch.float32, q, k, v, causal, scale, out, lse)
+
+
+# attn_sched_t / attn_passes_t / attn_dtype_t of attn.h
+SCHEDULES = {"default": 0, "xcd_all_heads": 1, "xcd_head": 2, "xcd_natural": 3, "linear_longest": 4,
+             "linear_natural": 5, "persistent_stride": 6, "persistent_queue": 7}
+PASSES = {"auto": 0, "exact": 1, "two": 2}
+
+
+def queue_workspace(device=None):
+    """Zeroed queue memory for the persistent-queue schedule (16 int32 values); each call
+    returns it to zero, so one tensor serves every call on one stream."""
+    return torch.zeros(16, dtype=torch.int32, device=device if device is not None else "cuda")
+
+
+def attn_fwd_variant(q, k, v, causal=False, scale=None, sched="default", passes="auto", queue=None, out=None,
+                     lse=None):
+    """16-bit forward with a chosen tile schedule and pass selection (same O and LSE as
+    attn_fwd_bf16 / attn_fwd_f16). ``queue`` (from ``queue_workspace``) is required for
+    sched="persistent_queue"."""
+    _require(q.dtype in (torch.bfloat16, torch.float16), "q must be bf16 or fp16")
+    _qkv_checks(q, k, v, q.dtype)
+    _require(sched in SCHEDULES, f"sched must be one of {sorted(SCHEDULES)}")
+    _require(passes in PASSES, f"passes must be one of {sorted(PASSES)}")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o.shape == q.shape and o.dtype == q.dtype and o.is_contiguous() and o.device == q.device, "bad out")
+    _require(L.shape == (B, H, N) and L.dtype == torch.float32 and L.is_contiguous() and L.device == q.device,
+             "bad lse")
+    qp = None
+    if sched == "persistent_queue":
+        _require(isinstance(queue, torch.Tensor) and queue.dtype == torch.int32 and queue.numel() >= 16
+                 and queue.is_contiguous() and queue.device == q.device,
+                 "persistent_queue needs queue = queue_workspace(device)")
+        qp = queue.data_ptr()
+    with torch.cuda.device(q.device):
+        st = library().attn_fwd_variant(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(),
+                                        B, H, N, d, int(bool(causal)), float(scale),
+                                        0 if q.dtype == torch.bfloat16 else 1, SCHEDULES[sched], PASSES[passes], qp,
+                                        _stream(q))
+    _check("attn_fwd_variant", st)
+    return o, L
+
+
+def attn_calibrate(kind, workgroups, iters, seed=None, out=None):
+    """Launch a calibration loop (kind "mfma" or "exp") on the current stream; returns the
+    output tensor and the operations it performs (FLOPs or exponentials)."""
+    k = {"mfma": 0, "exp": 1}[kind]
+    dev = torch.device("cuda", torch.cuda.current_device())
+    seed = torch.tensor([0x3F803F80, 0x3F003F00, 0x3F403F40, 0x3E803E80], dtype=torch.int64).to(torch.int32).to(dev) \
+        if seed is None else seed
+    out = torch.empty(workgroups * 512, dtype=torch.float32, device=dev) if out is None else out
+    _require(out.numel() >= workgroups * 512 and out.dtype == torch.float32, "out: workgroups * 512 fp32 values")
+    st = library().attn_calibrate(k, seed.data_ptr(), out.data_ptr(), workgroups, iters,
+                                  torch.cuda.current_stream(dev).cuda_stream)
+    _check("attn_calibrate", st)
+    return out, library().attn_calibrate_ops(k, iters) * workgroups
 
 
 def fwd(q, k, v, causal=False, scale=None, out=None, lse=None):

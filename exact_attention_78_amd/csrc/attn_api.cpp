@@ -139,6 +139,34 @@ attn_status_t attn_fwd_f16(const void* q, const void* k, const void* v, void* o,
   return from_hip(attn::launch_fwd_f16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, (hipStream_t)stream));
 }
 
+attn_status_t attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                               int64_t H, int64_t N, int64_t d, int causal, float scale, int dtype, int sched,
+                               int passes, int32_t* queue, void* stream) {
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_INVALID_ARG;
+  if (sched < ATTN_SCHED_DEFAULT || sched > ATTN_SCHED_PERSISTENT_QUEUE) return ATTN_ERR_INVALID_ARG;
+  if (passes < ATTN_PASSES_AUTO || passes > ATTN_PASSES_TWO) return ATTN_ERR_INVALID_ARG;
+  attn_status_t st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, 2, attn::max_workgroups_fwd16);
+  if (st != ATTN_OK) return st;
+  attn::FwdVariant var;
+  var.sched = sched;
+  var.passes = passes;
+  if (sched == ATTN_SCHED_PERSISTENT_QUEUE) {
+    if (!queue || !aligned16(queue)) return ATTN_ERR_INVALID_ARG;
+    const uintptr_t tb = (uintptr_t)(B * H * N * d) * 2;   // checked by check_fwd: no overflow
+    const Range rq{(uintptr_t)queue, (uintptr_t)queue + 16 * sizeof(int32_t)};
+    const Range others[5] = {{(uintptr_t)q, (uintptr_t)q + tb}, {(uintptr_t)k, (uintptr_t)k + tb},
+                             {(uintptr_t)v, (uintptr_t)v + tb}, {(uintptr_t)o, (uintptr_t)o + tb},
+                             {(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(B * H * N) * sizeof(float)}};
+    for (const Range& r : others)
+      if (overlaps(rq, r)) return ATTN_ERR_INVALID_ARG;
+    var.queue = queue;
+  }
+  const hipStream_t s = (hipStream_t)stream;
+  return from_hip(dtype == ATTN_DTYPE_BF16
+                      ? attn::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, s, var)
+                      : attn::launch_fwd_f16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, s, var));
+}
+
 attn_status_t attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int64_t B, int64_t H,
                            int64_t N, int64_t d, int causal, float scale, void* stream) {
   attn_status_t st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, 4, attn::max_workgroups_fwd32);
@@ -231,6 +259,19 @@ attn_status_t attn_decode_f16(const void* q, const void* k, const void* v, void*
   attn_status_t st = check_decode(q, k, v, o, lse, workspace, B, H, Nq, Nk, d, scale);
   if (st != ATTN_OK) return st;
   return from_hip(attn::launch_decode_f16(q, k, v, o, lse, workspace, B * H, Nq, Nk, d, scale, (hipStream_t)stream));
+}
+
+attn_status_t attn_calibrate(int kind, const uint32_t* seed, float* out, int64_t workgroups, int iters,
+                             void* stream) {
+  if ((kind != 0 && kind != 1) || !seed || !out || workgroups < 1 || workgroups > INT32_MAX || iters < 1)
+    return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(seed) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_calib(kind, seed, out, workgroups, iters, (hipStream_t)stream));
+}
+
+int64_t attn_calibrate_ops(int kind, int iters) {
+  if ((kind != 0 && kind != 1) || iters < 1) return -1;
+  return attn::calib_ops_per_workgroup(kind, iters);
 }
 
 const char* attn_status_string(attn_status_t s) {

@@ -76,7 +76,9 @@ template <typename Tag, int D, bool CAUSAL, int W, bool FAST>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int total_wg, float c /* scale*log2 e */,
-    int check_marks /* exact pass: redo marked tiles only (1) or every tile (0) */) {
+    int check_marks /* exact pass: redo marked tiles only (1) or every tile (0) */,
+    int order /* TileOrder of a plain grid */, int persist /* 0: plain grid, 1: persistent stride, 2: queue */,
+    int* __restrict__ queue /* persist 2: 8 tile counters, then 8 exit counts */) {
   constexpr int BM = W * 32;                        // query rows per workgroup
   constexpr int NSTEP = D / 16;                     // MFMA k-steps over the head dim
   constexpr int NKB = kBN / 32;                     // 32-key blocks per tile
@@ -404,51 +406,98 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     }
     if (half == 0) LSE[(int64_t)bh * N + qrow] = lse;
   };
-  int bh, mt;
-  xcd_query_tile(blockIdx.x, total_wg, n_mtiles, CAUSAL, bh, mt);
-  tile(bh, mt);
+  // The query tiles of this workgroup. A plain grid has one workgroup per tile, picked by
+  // the tile order from the workgroup id. A persistent grid has one workgroup per CU and
+  // 8 queues, one per XCD (queue x = workgroups x, x + 8, ..., which the dispatcher
+  // places on XCD x): queue x serves the tiles that the default order gives XCD x, in
+  // that order (longest first when causal). Its workgroups take either every P-th of them
+  // (P workgroups per queue: a fixed stride, as a persistent kernel that walks its share
+  // in a loop does), or the next one from the queue's counter, an atomic in caller memory.
+  __shared__ int ticket;
+  const int xq = blockIdx.x % 8, per_q = gridDim.x / 8;
+  for (int it = 0;; ++it) {
+    int w = blockIdx.x;
+    if (persist != 0) {
+      int tk = blockIdx.x / 8 + it * per_q;
+      __syncthreads();             // every wave is done with the previous tile's LDS flags and ticket
+      if (persist == 2) {
+        if (threadIdx.x == 0) ticket = atomicAdd(queue + xq, 1);
+        __syncthreads();
+        tk = ticket;
+      }
+      const int64_t wl = (int64_t)tk * 8 + xq;
+      if (wl < 0 || wl >= total_wg) break;   // every workgroup reaches this: the tickets only grow
+      w = (int)wl;
+    } else if (it > 0) {
+      break;
+    }
+    int bh, mt;
+    query_tile_ordered(persist != 0 ? (int)kOrderXcdPairs : order, w, total_wg, n_mtiles, CAUSAL, bh, mt);
+    tile(bh, mt);
+  }
+  if (persist == 2 && threadIdx.x == 0) {
+    // Every workgroup of queue xq has drawn its last (failing) ticket before counting its
+    // exit, so the last one to exit may return the queue to zero for the next call.
+    if (atomicAdd(queue + 8 + xq, 1) == per_q - 1) {
+      atomicExch(queue + xq, 0);
+      atomicExch(queue + 8 + xq, 0);
+    }
+  }
+}
+
+// Workgroups of a persistent grid: one per CU (this kernel's LDS allows one workgroup per
+// CU), rounded up to a multiple of the 8 queues.
+int persistent_workgroups() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  return (cus + 7) / 8 * 8;
 }
 
 template <typename Tag, int D, bool CAUSAL, int W>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
-                      float scale, hipStream_t stream) {
+                      float scale, const FwdVariant& var, hipStream_t stream) {
   constexpr int BM = W * 32;
   const int n_mtiles = (int)((N + BM - 1) / BM);
   const int64_t total = BH * n_mtiles;
   // Below ~1e11 counted FLOPs (~0.1 ms of work) the fast pass saves less than the exact
   // pass's launch costs, so such calls run the exact pass alone, on every tile.
   const double flops = 4.0 * (double)BH * (double)N * (double)N * D / (CAUSAL ? 2 : 1);
-  const bool two_pass = flops >= kTwoPassFlops;
+  const bool two_pass = var.passes == kPassesTwo || (var.passes == kPassesAuto && flops >= kTwoPassFlops);
+  const int persist = var.sched >= kSchedPersistentStride ? var.sched - kSchedPersistentStride + 1 : 0;
+  const int order = persist ? 0 : var.sched;
+  const unsigned grid = persist ? (unsigned)persistent_workgroups() : (unsigned)total;
   if (two_pass)
-    hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, true>), dim3((unsigned)total), dim3(W * 64), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, true>), dim3(grid), dim3(W * 64), 0,
                        stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
-                       n_mtiles, (int)total, scale * kLog2e, 1);
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, false>), dim3((unsigned)total), dim3(W * 64), 0,
+                       n_mtiles, (int)total, scale * kLog2e, 1, order, persist, var.queue);
+  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, false>), dim3(grid), dim3(W * 64), 0,
                      stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
-                     n_mtiles, (int)total, scale * kLog2e, two_pass ? 1 : 0);
+                     n_mtiles, (int)total, scale * kLog2e, two_pass ? 1 : 0, order, persist, var.queue);
   return hipGetLastError();
 }
 
 template <typename Tag>
 hipError_t launch_16bit(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
-                        int64_t d, bool causal, float scale, hipStream_t stream) {
+                        int64_t d, bool causal, float scale, const FwdVariant& var, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_one<Tag, 128, true, kWaves>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch_one<Tag, 128, false, kWaves>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch_one<Tag, 64, true, kWaves>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_one<Tag, 64, false, kWaves>(q, k, v, o, lse, BH, N, scale, stream);
+    return causal ? launch_one<Tag, 128, true, kWaves>(q, k, v, o, lse, BH, N, scale, var, stream)
+                  : launch_one<Tag, 128, false, kWaves>(q, k, v, o, lse, BH, N, scale, var, stream);
+  return causal ? launch_one<Tag, 64, true, kWaves>(q, k, v, o, lse, BH, N, scale, var, stream)
+                : launch_one<Tag, 64, false, kWaves>(q, k, v, o, lse, BH, N, scale, var, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
-                           int64_t d, bool causal, float scale, hipStream_t stream) {
-  return launch_16bit<Bf16Tag>(q, k, v, o, lse, BH, N, d, causal, scale, stream);
+                           int64_t d, bool causal, float scale, hipStream_t stream, const FwdVariant& var) {
+  return launch_16bit<Bf16Tag>(q, k, v, o, lse, BH, N, d, causal, scale, var, stream);
 }
 
 hipError_t launch_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
-                          int64_t d, bool causal, float scale, hipStream_t stream) {
-  return launch_16bit<F16Tag>(q, k, v, o, lse, BH, N, d, causal, scale, stream);
+                          int64_t d, bool causal, float scale, hipStream_t stream, const FwdVariant& var) {
+  return launch_16bit<F16Tag>(q, k, v, o, lse, BH, N, d, causal, scale, var, stream);
 }
 
 int64_t max_workgroups_fwd16(int64_t BH, int64_t N) {

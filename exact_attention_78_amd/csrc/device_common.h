@@ -95,15 +95,36 @@ __device__ __forceinline__ int xcd_logical_id(int w, int total) {
   return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
 }
 
+// Orders of the query tiles over the workgroup ids of a 1D grid. kOrderXcdPairs is the one
+// every kernel uses; the others are kept as launch variants of the 16-bit forward pass so
+// that the orders can be measured against each other.
+enum TileOrder : int {
+  kOrderXcdPairs = 0,        // per XCD, each pair of its heads, longest query tile first
+  kOrderXcdAllHeads = 1,     // per XCD, all its heads' tiles together, longest first
+  kOrderXcdHead = 2,         // per XCD, one head at a time, longest first
+  kOrderXcdNatural = 3,      // per XCD, one head at a time, natural order
+  kOrderLinearLongest = 4,   // no XCD remap (consecutive ids share a head), longest first
+  kOrderLinearNatural = 5,   // no XCD remap, natural order
+};
+
 // Query tile (bh, mt) of workgroup w in a grid of total = BH * n_mtiles workgroups.
-// Each XCD gets a contiguous set of heads, so their K/V stay in its L2. Causal grids go
-// longest query tile first, per group of two heads when BH is a multiple of 16 (the XCD
-// starts both heads' longest tiles before any shorter one: the tail of short tiles
-// shrinks, while only two heads' K/V compete for the L2), else per head.
-__device__ __forceinline__ void xcd_query_tile(int w, int total, int n_mtiles, bool causal, int& bh, int& mt) {
+// The XCD orders give each XCD a contiguous set of heads, so their K/V stay in its L2.
+// Causal grids go longest query tile first, over groups of g heads of the XCD when BH is
+// a multiple of 8 (the XCD starts all the group's longest tiles before any shorter one:
+// the tail of short tiles shrinks, while only g heads' K/V compete for the L2), else per
+// head. Non-causal tiles all have one length, so only the XCD remap matters there.
+__device__ __forceinline__ void query_tile_ordered(int order, int w, int total, int n_mtiles, bool causal, int& bh,
+                                                   int& mt) {
   const int n_bh = total / n_mtiles;
-  if (causal && n_bh % 8 == 0) {
-    const int nh = n_bh / 8, g = nh % 2 == 0 ? 2 : 1, loc = w / 8;
+  if (order >= kOrderLinearLongest) {
+    bh = w / n_mtiles;
+    const int m = w % n_mtiles;
+    mt = causal && order == kOrderLinearLongest ? n_mtiles - 1 - m : m;
+    return;
+  }
+  if (causal && order != kOrderXcdNatural && n_bh % 8 == 0) {
+    const int nh = n_bh / 8, loc = w / 8;
+    const int g = order == kOrderXcdAllHeads ? nh : order == kOrderXcdHead ? 1 : (nh % 2 == 0 ? 2 : 1);
     const int grp = loc / (g * n_mtiles), r = loc % (g * n_mtiles);
     bh = (w % 8) * nh + grp * g + r % g;
     mt = n_mtiles - 1 - r / g;
@@ -111,8 +132,13 @@ __device__ __forceinline__ void xcd_query_tile(int w, int total, int n_mtiles, b
     const int logical = xcd_logical_id(w, total);
     const int m = logical % n_mtiles;
     bh = logical / n_mtiles;
-    mt = causal ? n_mtiles - 1 - m : m;
+    mt = causal && order != kOrderXcdNatural ? n_mtiles - 1 - m : m;
   }
+}
+
+// The order all kernels use by default (per XCD, pairs of heads, longest first).
+__device__ __forceinline__ void xcd_query_tile(int w, int total, int n_mtiles, bool causal, int& bh, int& mt) {
+  query_tile_ordered(kOrderXcdPairs, w, total, n_mtiles, causal, bh, mt);
 }
 
 // Wait until at most N vector-memory loads of this wave are outstanding.
@@ -130,14 +156,14 @@ __device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
 }
 
 // One 16-byte-per-lane global->LDS DMA (global_load_lds_dwordx4): lane i's 16 bytes land
-// at LDS byte lds_base + 16*i; lds_base must be wave-uniform (it goes through M0). The load
-// is written as inline assembly so that the compiler does not see an LDS write it would
-// guard with a full vmcnt(0) drain before every later LDS read: completion is tracked by
-// hand with wait_vmcnt<>() and barrier_lds(). No compiler-generated code in these kernels
-// uses M0, so setting it here is safe.
+// at LDS byte lds_base + 16*i; lds_base must be wave-uniform. The LDS base goes through
+// M0, which the operand constraint binds, so the compiler itself writes M0 before the
+// instruction and knows what M0 holds afterwards. The load is written as inline assembly
+// so that the compiler does not see an LDS write it would guard with a full vmcnt(0)
+// drain before every later LDS read: completion is tracked by hand with wait_vmcnt<>()
+// and barrier_lds(). (The s_nop separates the M0 write from the instruction that reads it.)
 __device__ __forceinline__ void dma_load16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gptr), "s"(lds_base) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gptr), "{m0}"(lds_base) : "memory");
 }
 
 // Workgroup barrier for LDS hand-over only: LDS reads of this wave are complete, then

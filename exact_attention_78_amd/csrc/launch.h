@@ -7,10 +7,20 @@
 
 namespace attn {
 
+// Launch variants of the 16-bit forward pass: tile order or persistent grid (sched), and
+// which passes run. The values match attn_sched_t and attn_passes_t of attn.h.
+enum : int { kSchedPersistentStride = 6, kSchedPersistentQueue = 7 };
+enum : int { kPassesAuto = 0, kPassesExact = 1, kPassesTwo = 2 };
+struct FwdVariant {
+  int sched = 0;             // 0..5: TileOrder of a plain grid; 6, 7: persistent grids
+  int passes = kPassesAuto;
+  int* queue = nullptr;      // kSchedPersistentQueue: 16 ints of caller memory, zero between calls
+};
+
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
-                           int64_t d, bool causal, float scale, hipStream_t stream);
+                           int64_t d, bool causal, float scale, hipStream_t stream, const FwdVariant& var = {});
 hipError_t launch_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
-                          int64_t d, bool causal, float scale, hipStream_t stream);
+                          int64_t d, bool causal, float scale, hipStream_t stream, const FwdVariant& var = {});
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int64_t BH, int64_t N,
                           int64_t d, bool causal, float scale, hipStream_t stream);
 hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* sq, const float* sk,
@@ -32,6 +42,11 @@ hipError_t launch_decode_f16(const void* q, const void* k, const void* v, void* 
                              int64_t BH, int64_t Nq, int64_t Nk, int64_t d, float scale, hipStream_t stream);
 // Floats of workspace the decode launches use.
 int64_t decode_workspace_floats(int64_t BH, int64_t Nq, int64_t Nk, int64_t d);
+
+// Calibration loops (kind 0: dense bf16 MFMA, kind 1: v_exp_f32) and the operations one
+// workgroup of them performs.
+hipError_t launch_calib(int kind, const uint32_t* seed, float* out, int64_t workgroups, int iters, hipStream_t stream);
+int64_t calib_ops_per_workgroup(int kind, int iters);
 
 // Workgroup counts of the launches above (validated against the 32-bit grid limit).
 int64_t max_workgroups_fwd16(int64_t BH, int64_t N);

@@ -119,7 +119,19 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __r
   // theorem: with y within half an ulp of 1/s and q0 = RN(x*y) close to x/s, the residual
   // r = x - s*q0 is exact and RN(q0 + r*y) is the correctly rounded quotient; checked
   // against exact rational arithmetic on the CPU and bit-exactly against the oracle).
-  const float y_rcp = 1.0f / s;
+  // The theorem needs 1/s finite and r clear of the subnormal range. For a block of tiny
+  // values (s < 2^-64, s possibly subnormal) both x and s are first multiplied by 2^64:
+  // the products are exact, so the quotient is the same, and with the scaled divisor
+  // s' >= 2^-78 every quotient that can reach a nonzero code keeps r normal.
+  float sd = s;
+  if (s < 0x1p-64f) {                                          // block-uniform, rare
+    sd = s * 0x1p64f;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[p][e] *= 0x1p64f;
+  }
+  const float y_rcp = 1.0f / sd;
 
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
@@ -134,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __r
         const float xv = x[p][e + k];
         const float q0 = xv * y_rcp;
         // (copysign keeps the sign of a zero input: -0 / s is -0, but the correction sums +0 and -0)
-        const float q = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, s, xv), y_rcp, q0), xv);
+        const float q = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, sd, xv), y_rcp, q0), xv);
         y[k] = fminf(fmaxf(q, -448.0f), 448.0f);
       }
       if (e % 4 == 0) w[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);

@@ -71,6 +71,57 @@ attn_status_t attn_fwd_bf16(const void* q, const void* k, const void* v, void* o
                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                             void* stream);
 
+/* Launch variants of the 16-bit forward pass, for measuring its design choices against
+ * each other; every variant computes the same O and LSE as attn_fwd_bf16 / attn_fwd_f16.
+ *
+ * sched: how query tiles map to workgroups. The 1D grid over (batch*head, query tile)
+ * with neighbouring ids on one head is item 4 of the Method section of "Triton 07: Flash
+ * Attention v3"; its section on the persistent kernel describes the alternative of one
+ * program per multiprocessor that walks its share of the tiles in a loop (slower there,
+ * from work imbalance). On MI355X workgroup w runs on XCD w mod 8 (8 XCDs, each with
+ * its own L2), so the orders below either keep a head's tiles on one XCD or not.
+ *   ATTN_SCHED_DEFAULT            per XCD, pairs of heads, longest query tile first (causal)
+ *   ATTN_SCHED_XCD_ALL_HEADS      per XCD, all its heads together, longest first
+ *   ATTN_SCHED_XCD_HEAD           per XCD, one head at a time, longest first
+ *   ATTN_SCHED_XCD_NATURAL        per XCD, one head at a time, natural order
+ *   ATTN_SCHED_LINEAR_LONGEST     no XCD remap (consecutive ids on one head), longest first
+ *   ATTN_SCHED_LINEAR_NATURAL     no XCD remap, natural order
+ *   ATTN_SCHED_PERSISTENT_STRIDE  one workgroup per CU; the workgroups of XCD x walk XCD x's
+ *                                 tiles of the default order with a fixed stride
+ *   ATTN_SCHED_PERSISTENT_QUEUE   one workgroup per CU; each XCD's workgroups take XCD x's
+ *                                 tiles of the default order one at a time from a counter
+ *                                 in `queue` (dynamic: a workgroup that finishes early
+ *                                 takes the next tile)
+ * passes: ATTN_PASSES_AUTO as attn_fwd_bf16 (two passes at >= 1e11 counted FLOPs);
+ *   ATTN_PASSES_EXACT the running-max pass alone, on every tile (the online softmax of the
+ *   FlashAttention-2 digest, glossary: a per-tile max and a rescaled running sum);
+ *   ATTN_PASSES_TWO the first-tile-reference pass, then the running-max pass on the query
+ *   tiles it marked, at any size.
+ * dtype: ATTN_DTYPE_BF16 or ATTN_DTYPE_F16 (q, k, v, o of that type).
+ * queue: ATTN_SCHED_PERSISTENT_QUEUE only (else ignored, may be NULL): caller-owned device
+ *   memory of 16 int32 values, all zero before the first call; every call leaves them zero
+ *   again when its kernels have run. Calls that share one queue array must not overlap in
+ *   time (use one array per stream). A sched, passes or dtype value outside these lists,
+ *   or a NULL or misaligned queue for ATTN_SCHED_PERSISTENT_QUEUE, is ATTN_ERR_INVALID_ARG. */
+typedef enum {
+  ATTN_SCHED_DEFAULT = 0,
+  ATTN_SCHED_XCD_ALL_HEADS = 1,
+  ATTN_SCHED_XCD_HEAD = 2,
+  ATTN_SCHED_XCD_NATURAL = 3,
+  ATTN_SCHED_LINEAR_LONGEST = 4,
+  ATTN_SCHED_LINEAR_NATURAL = 5,
+  ATTN_SCHED_PERSISTENT_STRIDE = 6,
+  ATTN_SCHED_PERSISTENT_QUEUE = 7
+} attn_sched_t;
+
+typedef enum { ATTN_PASSES_AUTO = 0, ATTN_PASSES_EXACT = 1, ATTN_PASSES_TWO = 2 } attn_passes_t;
+
+typedef enum { ATTN_DTYPE_BF16 = 0, ATTN_DTYPE_F16 = 1 } attn_dtype_t;
+
+attn_status_t attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                               int dtype, int sched, int passes, int32_t* queue, void* stream);
+
 /* fp16 Q/K/V in, fp16 O out; as attn_fwd_bf16 with fp16 in place of bf16. */
 attn_status_t attn_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
@@ -153,6 +204,20 @@ attn_status_t attn_decode_f16(const void* q, const void* k, const void* v, void*
 /* Workspace size (fp32 values) that attn_decode_* needs for these sizes; -1 if the sizes
  * are invalid. Host-only, no HIP call. */
 int64_t attn_decode_workspace_floats(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d);
+
+/* Calibration loops: what the part sustains at the clock it runs under load. kind 0 runs
+ * a dense loop of independent 32x32x16 bf16 MFMAs, kind 1 a dense loop of v_exp_f32
+ * (exponentials; "8.3 FlashAttention-3", section 1, names the exponential unit as the
+ * softmax's bottleneck next to the matrix units), each in `workgroups` workgroups of 512
+ * threads (the attention kernels' launch shape) for `iters` iterations. seed: device
+ * memory of 4 uint32 values (operands, so that nothing folds); out: device memory of
+ * workgroups * 512 floats, overwritten with one value per thread. attn_calibrate_ops
+ * gives the operations (FLOPs for kind 0, exponentials for kind 1) of one workgroup, so
+ * that rate = ops * workgroups / elapsed time. kind outside {0, 1}, workgroups or iters
+ * < 1, or a NULL pointer is ATTN_ERR_INVALID_ARG (attn_calibrate_ops returns -1). */
+attn_status_t attn_calibrate(int kind, const uint32_t* seed, float* out, int64_t workgroups, int iters,
+                             void* stream);
+int64_t attn_calibrate_ops(int kind, int iters);
 
 /* Static description of a status code; never NULL. */
 const char* attn_status_string(attn_status_t s);

@@ -143,16 +143,3 @@ def attention_backward(q, k, v, dout, causal: bool, scale: float, heads=None, ro
             dQ[b, h, r] = scale * (dS @ k[b, h])
             dK[b, h] += scale * (dS.T @ q[b, h, r, :])
     return dQ, dK, dV
-
-
-def counted_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
-    """Forward FLOP count by the convention the pages' throughput figures use:
-    4*B*H*N^2*d (two N x N x d contractions), halved when causal."""
-    f = 4.0 * B * H * N * N * d
-    return f / 2 if causal else f
-
-
-def counted_flops_backward(B: int, H: int, N: int, d: int, causal: bool) -> float:
-    """Backward FLOP count: the five N x N x d contractions of the gradient (S again,
-    dV, dP, dQ, dK), 2.5 times the forward count, halved when causal."""
-    return 2.5 * counted_flops(B, H, N, d, causal)

@@ -41,6 +41,7 @@ def lib():
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = header_functions()
     assert set(names) == {"attn_fwd_bf16", "attn_fwd_f16", "attn_fwd_f32", "attn_fwd_fp8", "attn_quant_fp8",
+                          "attn_fwd_variant", "attn_calibrate", "attn_calibrate_ops",
                           "attn_bwd_bf16", "attn_bwd_f16", "attn_decode_bf16", "attn_decode_f16",
                           "attn_decode_workspace_floats", "attn_status_string", "attn_abi_version"}
     for n in names:
@@ -77,6 +78,22 @@ def call_fwd(lib, fn, q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=2, N=64, 
 ])
 def test_fwd_validation(lib, fn, defect, expect):
     assert call_fwd(lib, fn, **defect) == expect
+
+
+@no_gpu_only
+@pytest.mark.parametrize("defect,expect", [
+    (dict(q=None), INVALID), (dict(N=0), INVALID), (dict(d=96), UNSUPPORTED), (dict(scale=0.0), INVALID),
+    (dict(o=A[0]), INVALID), (dict(dtype=2), INVALID), (dict(dtype=-1), INVALID), (dict(sched=8), INVALID),
+    (dict(sched=-1), INVALID), (dict(passes=3), INVALID), (dict(passes=-1), INVALID),
+    (dict(sched=7, queue=None), INVALID), (dict(sched=7, queue=A[5] + 4), INVALID),
+    (dict(sched=7, queue=A[3] + 64), INVALID), (dict(sched=7, queue=A[4]), INVALID),
+    (dict(sched=7, queue=A[5], N=0), INVALID),
+])
+def test_fwd_variant_validation(lib, defect, expect):
+    args = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=2, N=64, d=64, causal=1, scale=0.125, dtype=0,
+                sched=0, passes=0, queue=A[5])
+    args.update(defect)
+    assert lib.attn_fwd_variant(*args.values(), None) == expect
 
 
 @no_gpu_only
@@ -134,6 +151,22 @@ def test_decode_validation(lib, fn, defect, expect):
     args = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], ws=A[5], B=2, H=2, Nq=1, Nk=1000, d=128, scale=0.0884)
     args.update(defect)
     assert getattr(lib, fn)(*args.values(), None) == expect
+
+
+@no_gpu_only
+@pytest.mark.parametrize("defect", [dict(kind=2), dict(kind=-1), dict(seed=None), dict(out=None), dict(wg=0),
+                                    dict(iters=0), dict(seed=A[0] + 4), dict(wg=1 << 33)])
+def test_calibrate_validation(lib, defect):
+    args = dict(kind=0, seed=A[0], out=A[1], wg=256, iters=10)
+    args.update(defect)
+    assert lib.attn_calibrate(*args.values(), None) == INVALID
+
+
+def test_calibrate_ops(lib):
+    # 8 waves x iters x 8 chains x 32x32x16x2 FLOPs; 512 lanes x iters x 16 exponentials
+    assert lib.attn_calibrate_ops(0, 10) == 8 * 10 * 8 * 32768
+    assert lib.attn_calibrate_ops(1, 10) == 512 * 10 * 16
+    assert lib.attn_calibrate_ops(2, 10) == -1 and lib.attn_calibrate_ops(0, 0) == -1
 
 
 def test_decode_workspace_size(lib):

@@ -5,8 +5,9 @@ the seeded generators; the oracle sees exactly the rounded values the GPU sees.
 
 Tolerances (stated for this path, see the library header): O max-abs error <= 2e-2
 and |dLSE| <= 1e-3 * max(1, |LSE|) for bf16/fp16; fp32 is held to the same hard bound
-and must also reach O max-abs <= 1e-4. Full-size workloads are checked on sampled rows
-that the oracle evaluates one by one.
+and must also reach O max-abs <= 1e-4. The named workloads are checked on every head
+and every row (the oracle runs on a pool of host threads); only tensors of more than
+2^31 elements and the single 65569-row head are checked on sampled rows.
 """
 
 import math
@@ -16,8 +17,10 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_78_amd import attn_fwd_bf16, attn_fwd_f16, attn_fwd_f32, fwd, inputs
+from exact_attention_78_amd import attn_fwd_bf16, attn_fwd_f16, attn_fwd_f32, attn_fwd_variant, fwd, inputs, \
+    queue_workspace
 from oracle.attention import attention_forward
+from oracle.pool import forward_pooled
 
 pytestmark = pytest.mark.gpu
 
@@ -44,15 +47,18 @@ def lse_err(L, Lref):
     return np.max(np.abs(L - Lref) / np.maximum(1.0, np.abs(Lref)))
 
 
-def check(cpu, gpu, dtype, causal, rows=None, heads=None, o_tol=O_TOL_16):
+def check(cpu, gpu, dtype, causal, rows=None, heads=None, o_tol=O_TOL_16, call=None, ref=None):
+    """Run the forward (``call``, default the dtype's entry point) and compare O and LSE
+    with the oracle on the requested rows and heads (all by default). ``ref`` passes an
+    oracle result computed earlier for the same inputs."""
     tq, tk, tv = cpu
     B, H, N, d = tq.shape
     scale = inputs.softmax_scale(d)
-    o, lse = FN[dtype](*gpu, causal=causal, scale=scale)
+    o, lse = (call or FN[dtype])(*gpu, causal=causal, scale=scale)
     torch.cuda.synchronize()
     O = o.float().cpu().numpy().astype(np.float64)
     L = lse.cpu().numpy().astype(np.float64)
-    Oref, Lref = attention_forward(tq, tk, tv, causal, scale, rows=rows, heads=heads)
+    Oref, Lref = ref if ref is not None else forward_pooled(tq, tk, tv, causal, scale, rows=rows, heads=heads)
     if rows is not None:
         O, L = O[:, :, rows], L[:, :, rows]
     if heads is not None:
@@ -111,22 +117,25 @@ def sample_rows(N, n_random=96, seed=0):
 
 @pytest.mark.parametrize("name,causal,dtype", [("C3", True, "bf16"), ("C3", False, "bf16"), ("C3", True, "f16"),
                                                ("C4", True, "bf16"), ("H", True, "bf16"), ("H", True, "f16")])
-def test_full_size_sampled(name, causal, dtype):
+def test_full_size_every_row(name, causal, dtype):
+    # The named workloads on every head and every row. H in bf16 is the benchmarked call
+    # in the launch configuration the benchmark times (fast pass, then exact pass).
     w = inputs.WORKLOADS[name]
-    say(f"case {name} causal={causal} dtype={dtype}")
+    say(f"case {name} causal={causal} dtype={dtype}: every head, every row")
     cpu, gpu = make(w.wid, w.B, w.H, w.N, w.d, dtype)
-    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2), (0, w.H - 1)]
-    check(cpu, gpu, dtype, causal, rows=sample_rows(w.N), heads=heads)
+    check(cpu, gpu, dtype, causal)
 
 
-def test_metric_workload_every_head_sampled():
-    # The benchmarked call (bf16, causal, B2 H16 N8192 d128, in the launch configuration the
-    # benchmark times: fast pass, then exact pass) checked on every one of its 32 heads, on
-    # rows that include the first and last rows of query tiles and of the sequence.
-    w = inputs.WORKLOADS["H"]
-    say("case H every head, sampled rows")
-    cpu, gpu = make(w.wid, w.B, w.H, w.N, w.d, "bf16")
-    check(cpu, gpu, "bf16", True, rows=sample_rows(w.N, n_random=24, seed=11))
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_d64_two_pass_every_row(causal, dtype):
+    # Head dim 64 above the two-pass threshold (B2 H16 N8192 d64: 2.7e11 FLOPs causal,
+    # 5.5e11 non-causal), so the first-tile-reference pass and the exact pass both run in
+    # their d = 64 instantiations; every head, every row.
+    B, H, N, d = 2, 16, 8192, 64
+    say(f"case d64 two-pass B{B} H{H} N{N} causal={causal} dtype={dtype}: every head, every row")
+    cpu, gpu = make(14, B, H, N, d, dtype)
+    check(cpu, gpu, dtype, causal)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -221,11 +230,11 @@ def test_scores_jumping_past_the_first_tile_max(factor, causal, dtype):
     # Keys from 300 on are scaled up: their scores exceed the first tile's row max by about
     # 25 (x8) or far more than 64 (x30) in log2 units. Probabilities against the first
     # tile's max would then overflow fp16 (x8) or any 16-bit type (x30). At N = 700 the
-    # call runs the exact pass alone (per-tile max); at B2 H16 N4096 (above the two-pass
-    # threshold of 1e11 FLOPs) the fast pass must mark those rows and the exact pass redo
-    # their query tiles, checked on sampled rows of two heads.
+    # call runs the exact pass alone (per-tile max); at B2 H16 N4096 d128 and B2 H16 N8192
+    # d64 (above the two-pass threshold of 1e11 FLOPs) the fast pass must mark those rows
+    # and the exact pass redo their query tiles, checked on sampled rows of two heads.
     say(f"case jumping scores x{factor} causal={causal} dtype={dtype}")
-    for B, H, N, d in ((1, 2, 700, 128), (2, 16, 4096, 128)):
+    for B, H, N, d in ((1, 2, 700, 128), (2, 16, 4096, 128), (2, 16, 8192, 64)):
         q, k, v = inputs.draw_qkv(12, B, H, N, d)
         k = k.copy()
         k[:, :, 300:] *= np.float32(factor)

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.attention import attention_forward, counted_flops
+from oracle.attention import attention_forward
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 rng = np.random.default_rng(1234)
@@ -211,10 +211,3 @@ def test_accepts_low_precision_torch_inputs():
     O, L = attention_forward(x, x, x, False, 0.5)
     O2, L2 = attention_forward(x.float().numpy(), x.float().numpy(), x.float().numpy(), False, 0.5)
     np.testing.assert_array_equal(O, O2)
-
-
-def test_counted_flops_convention():
-    # 4*B*H*N^2*d, halved for causal: the headline shape is 549.8 GFLOP causal.
-    assert counted_flops(2, 16, 8192, 128, True) == 4 * 2 * 16 * 8192 ** 2 * 128 / 2
-    assert round(counted_flops(2, 16, 8192, 128, True) / 1e9, 1) == 549.8
-    assert counted_flops(1, 2, 128, 64, False) == 2 * counted_flops(1, 2, 128, 64, True)

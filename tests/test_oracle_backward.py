@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.attention import attention_backward, attention_forward, counted_flops, counted_flops_backward
+from oracle.attention import attention_backward, attention_forward
 
 rng = np.random.default_rng(4321)
 
@@ -110,8 +110,3 @@ def test_head_subset_leaves_others_nan():
     for f, p in zip(full, part):
         np.testing.assert_array_equal(p[1, 0], f[1, 0])
         assert np.isnan(p[0]).all()
-
-
-def test_backward_flop_convention():
-    # five contractions against the forward's two
-    assert counted_flops_backward(2, 16, 8192, 128, True) == 2.5 * counted_flops(2, 16, 8192, 128, True)
