@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     attn_calibrate,
     attn_bwd_f16,
     attn_decode_bf16,
+    attn_decode_bf16_noalloc,
     attn_decode_f16,
     attn_fwd_bf16,
     attn_fwd_f16,

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libattn.so")
 
 _lib = None
 
-STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_LAUNCH"}
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_LAUNCH",
+          4: "ATTN_ERR_SCRATCH_TOO_SMALL"}
 
 # Exported symbols and their C signatures (mirrors include/attn.h).
 _P, _I64, _INT, _F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
@@ -35,6 +36,7 @@ SIGNATURES = {
     "attn_decode_bf16": [_P] * 6 + [_I64, _I64, _I64, _I64, _I64, _F32, _P],
     "attn_decode_f16": [_P] * 6 + [_I64, _I64, _I64, _I64, _I64, _F32, _P],
     "attn_decode_workspace_floats": [_I64, _I64, _I64, _I64, _I64],
+    "attn_decode_bf16_noalloc": [_P] * 5 + [_I64, _I64, _I64, _I64, _I64, _F32, _P],
     "attn_calibrate": [_INT, _P, _P, _I64, _INT, _P],
     "attn_calibrate_ops": [_INT, _INT],
     "attn_status_string": [_INT],
@@ -259,6 +261,31 @@ def attn_decode_bf16(q, k, v, scale=None, out=None, lse=None, workspace=None):
     """Split-KV decoding step: bf16 q [B,H,Nq<=32,d] against k, v [B,H,Nk,d], no mask.
     Returns (O bf16 [B,H,Nq,d], LSE fp32 [B,H,Nq])."""
     return _decode("attn_decode_bf16", torch.bfloat16, q, k, v, scale, out, lse, workspace)
+
+
+def attn_decode_bf16_noalloc(q, k, v, scale=None, out=None, lse=None):
+    """attn_decode_bf16 with the partials in the library's static device scratch (no
+    workspace; the library allocates nothing). Pass ``out`` and ``lse`` to allocate
+    nothing here either. Calls that overlap in time on one GPU race."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.bfloat16 and t.dim() == 4
+                 and t.is_contiguous() and t.device == q.device, f"{name} must be a contiguous bf16 GPU tensor")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _require(k.shape == (B, H, Nk, d) and v.shape == k.shape, "k and v must be [B, H, Nk, d] with q's B, H, d")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o.shape == q.shape and o.dtype == torch.bfloat16 and o.is_contiguous() and o.device == q.device,
+             "bad out")
+    _require(L.shape == (B, H, Nq) and L.dtype == torch.float32 and L.is_contiguous() and L.device == q.device,
+             "bad lse")
+    with torch.cuda.device(q.device):
+        st = library().attn_decode_bf16_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(),
+                                                B, H, Nq, Nk, d, float(scale), _stream(q))
+    _check("attn_decode_bf16_noalloc", st)
+    return o, L
 
 
 def attn_decode_f16(q, k, v, scale=None, out=None, lse=None, workspace=None):

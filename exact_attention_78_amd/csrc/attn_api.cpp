@@ -95,20 +95,22 @@ attn_status_t check_decode_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nk, i
   return ATTN_OK;
 }
 
+// Validation of the decode entry points; ws == NULL with no_ws: the static-scratch variant.
 attn_status_t check_decode(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                           const float* ws, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale) {
-  if (!q || !k || !v || !o || !lse || !ws) return ATTN_ERR_INVALID_ARG;
+                           const float* ws, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                           bool no_ws = false) {
+  if (!q || !k || !v || !o || !lse || (!ws && !no_ws)) return ATTN_ERR_INVALID_ARG;
   int64_t qe, kve, rows;
   attn_status_t st = check_decode_shape(B, H, Nq, Nk, d, &qe, &kve, &rows);
   if (st != ATTN_OK) return st;
   if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
-  const void* ptrs[6] = {q, k, v, o, lse, ws};
+  const void* ptrs[6] = {q, k, v, o, lse, no_ws ? q : ws};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (attn::max_workgroups_decode(B * H, Nq, Nk) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
   auto span = [](const void* p, uintptr_t n) { return Range{(uintptr_t)p, (uintptr_t)p + n}; };
-  const int64_t wsf = attn::decode_workspace_floats(B * H, Nq, Nk, d);
+  const int64_t wsf = no_ws ? 0 : attn::decode_workspace_floats(B * H, Nq, Nk, d);
   const Range ins[3] = {span(q, (uintptr_t)qe * 2), span(k, (uintptr_t)kve * 2), span(v, (uintptr_t)kve * 2)};
   const Range outs[3] = {span(o, (uintptr_t)qe * 2), span(lse, (uintptr_t)rows * sizeof(float)),
                          span(ws, (uintptr_t)wsf * sizeof(float))};
@@ -254,6 +256,15 @@ attn_status_t attn_decode_bf16(const void* q, const void* k, const void* v, void
   return from_hip(attn::launch_decode_bf16(q, k, v, o, lse, workspace, B * H, Nq, Nk, d, scale, (hipStream_t)stream));
 }
 
+attn_status_t attn_decode_bf16_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                       int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, void* stream) {
+  attn_status_t st = check_decode(q, k, v, o, lse, nullptr, B, H, Nq, Nk, d, scale, true);
+  if (st != ATTN_OK) return st;
+  if (attn::decode_workspace_floats(B * H, Nq, Nk, d) > attn::kDecodeScratchFloats) return ATTN_ERR_SCRATCH_TOO_SMALL;
+  return from_hip(
+      attn::launch_decode_bf16_noalloc(q, k, v, o, lse, B * H, Nq, Nk, d, scale, (hipStream_t)stream));
+}
+
 attn_status_t attn_decode_f16(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
                               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, void* stream) {
   attn_status_t st = check_decode(q, k, v, o, lse, workspace, B, H, Nq, Nk, d, scale);
@@ -280,6 +291,7 @@ const char* attn_status_string(attn_status_t s) {
     case ATTN_ERR_INVALID_ARG: return "invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_SCRATCH_TOO_SMALL: return "sizes need more than the library's static scratch (64 MiB per GPU)";
   }
   return "unknown status";
 }

@@ -23,6 +23,8 @@
 //   combine  one workgroup per (batch*head, query row): the weights exp(LSE_s - LSE) and
 //            the weighted sum of the O_s (chunks spread over 8 (d=128) or 16 (d=64)
 //            groups of threads, added through LDS), rounded once to 16 bits.
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 #include "tile_lds.h"
@@ -234,6 +236,46 @@ int64_t max_workgroups_decode(int64_t BH, int64_t Nq, int64_t Nk) {
 
 hipError_t launch_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* ws,
                               int64_t BH, int64_t Nq, int64_t Nk, int64_t d, float scale, hipStream_t stream) {
+  return launch_16bit<Bf16Tag>(q, k, v, o, lse, ws, BH, Nq, Nk, d, scale, stream);
+}
+
+// Scratch of the allocation-free decoding entry point: the per-chunk partials (O and LSE
+// of every (head, key chunk, query row)) live in this file-scope device array instead of
+// a caller workspace. Each GPU the library runs on holds its own copy, at its own address,
+// until the process ends. Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address of each GPU's copy is
+// looked up once per device with hipGetSymbolAddress and kept in scratch_ptr.
+static __device__ __align__(256) float scratch[kDecodeScratchFloats];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float* scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(float** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // the current device's copy
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = (float*)p;
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_decode_bf16_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
+                                      int64_t Nq, int64_t Nk, int64_t d, float scale, hipStream_t stream) {
+  float* ws = nullptr;
+  const hipError_t e = decode_scratch(&ws);
+  if (e != hipSuccess) return e;
+  // every partial the combine kernel reads is written by the split kernel first: nothing
+  // in the scratch needs clearing between calls
   return launch_16bit<Bf16Tag>(q, k, v, o, lse, ws, BH, Nq, Nk, d, scale, stream);
 }
 

@@ -42,6 +42,12 @@ hipError_t launch_decode_f16(const void* q, const void* k, const void* v, void* 
                              int64_t BH, int64_t Nq, int64_t Nk, int64_t d, float scale, hipStream_t stream);
 // Floats of workspace the decode launches use.
 int64_t decode_workspace_floats(int64_t BH, int64_t Nq, int64_t Nk, int64_t d);
+// The bf16 decoding step with its partials in the library's static device scratch of
+// kDecodeScratchFloats floats per GPU (sizes already checked against it by the caller);
+// the first call on a device looks up that device's copy (hipGetSymbolAddress).
+constexpr int64_t kDecodeScratchFloats = int64_t(16) << 20;   // 64 MiB
+hipError_t launch_decode_bf16_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
+                                      int64_t Nq, int64_t Nk, int64_t d, float scale, hipStream_t stream);
 
 // Calibration loops (kind 0: dense bf16 MFMA, kind 1: v_exp_f32) and the operations one
 // workgroup of them performs.

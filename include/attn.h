@@ -55,10 +55,11 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,
   ATTN_ERR_UNSUPPORTED = 2,
-  ATTN_ERR_LAUNCH = 3
+  ATTN_ERR_LAUNCH = 3,
+  ATTN_ERR_SCRATCH_TOO_SMALL = 4
 } attn_status_t;
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /* bf16 Q/K/V in, bf16 O out (round to nearest even), fp32 LSE out. P is rounded to
  * bf16 before the P.V contraction; both contractions accumulate in fp32. A call of at
@@ -200,6 +201,20 @@ attn_status_t attn_decode_bf16(const void* q, const void* k, const void* v, void
 attn_status_t attn_decode_f16(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
                               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                               void* stream);
+
+/* attn_decode_bf16 for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * results, with the per-chunk partials in a static device array of the library (64 MiB,
+ * 2^24 floats, per GPU, held until the process ends) instead of a caller workspace. The
+ * call allocates and frees nothing; the first call on a device looks up that device's
+ * copy of the array. Sizes whose attn_decode_workspace_floats(...) exceeds 2^24 return
+ * ATTN_ERR_SCRATCH_TOO_SMALL before anything is enqueued (at Nq = 32, d = 128 that is up
+ * to 4064 (head, key chunk) pairs: any B*H <= 2016 at any Nk). Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (two streams, two threads) race and give
+ * undefined results; calls enqueued on one stream do not overlap. */
+attn_status_t attn_decode_bf16_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                       int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                                       void* stream);
 
 /* Workspace size (fp32 values) that attn_decode_* needs for these sizes; -1 if the sizes
  * are invalid. Host-only, no HIP call. */
