@@ -116,7 +116,8 @@ def time_launches(torch, fn, steps, warmup, reps=1, between=None):
 
 
 def us(t):
-    return {k: (v * 1e3 if k.endswith("_ms") else v) for k, v in t.items()}
+    """The timing dict in microseconds (keys *_ms -> *_us)."""
+    return {(k[:-3] + "_us" if k.endswith("_ms") else k): (v * 1e3 if k.endswith("_ms") else v) for k, v in t.items()}
 
 
 def rate(work, t, scale=1e12):
