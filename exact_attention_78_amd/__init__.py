@@ -19,9 +19,11 @@ from ._binding import (  # noqa: F401
     attn_fwd_f16,
     attn_fwd_f32,
     attn_fwd_fp8,
+    attn_fwd_fp8_rotq,
     attn_fwd_variant,
     queue_workspace,
     attn_quant_fp8,
+    attn_quant_fp8_kv,
     bwd,
     fwd,
     library,

@@ -31,6 +31,8 @@ SIGNATURES = {
     "attn_fwd_variant": [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _INT, _INT, _INT, _P, _P],
     "attn_fwd_fp8": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_quant_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
+    "attn_quant_fp8_kv": [_P] * 7 + [_I64, _I64, _I64, _I64, _P],
+    "attn_fwd_fp8_rotq": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_bwd_bf16": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_bwd_f16": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_decode_bf16": [_P] * 6 + [_I64, _I64, _I64, _I64, _I64, _F32, _P],
@@ -339,3 +341,69 @@ def attn_quant_fp8(x, signs=None, out=None, scales=None):
                                       None if signs is None else signs.data_ptr(), B, H, N, d, _stream(x))
     _check("attn_quant_fp8", st)
     return x8, sc
+
+
+def attn_quant_fp8_kv(k, v, signs, k8=None, v8=None, k_scale=None, v_scale=None):
+    """Quantise K (rotated with ``signs``) and V (unrotated) in one launch; returns
+    (k8, k_scale, v8, v_scale) as two attn_quant_fp8 calls would."""
+    for name, t in (("k", k), ("v", v)):
+        _require(isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.bfloat16 and t.dim() == 4
+                 and t.is_contiguous() and t.shape == k.shape and t.device == k.device,
+                 f"{name} must be a contiguous bf16 [B, H, N, d] GPU tensor like k")
+    B, H, N, d = k.shape
+    nblk = (N + 127) // 128
+    _require(isinstance(signs, torch.Tensor) and signs.dtype == torch.float32 and signs.shape == (d,)
+             and signs.is_contiguous() and signs.device == k.device, "signs must be fp32 [d] on k's device")
+    outs = []
+    for name, t, shape, dt in (("k8", k8, (B, H, N, d), torch.uint8), ("v8", v8, (B, H, N, d), torch.uint8),
+                               ("k_scale", k_scale, (B, H, nblk), torch.float32),
+                               ("v_scale", v_scale, (B, H, nblk), torch.float32)):
+        t = torch.empty(shape, dtype=dt, device=k.device) if t is None else t
+        _require(t.shape == shape and t.dtype == dt and t.is_contiguous() and t.device == k.device, f"bad {name}")
+        outs.append(t)
+    with torch.cuda.device(k.device):
+        st = library().attn_quant_fp8_kv(k.data_ptr(), v.data_ptr(), signs.data_ptr(), outs[0].data_ptr(),
+                                         outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(), B, H, N, d,
+                                         _stream(k))
+    _check("attn_quant_fp8_kv", st)
+    return outs[0], outs[2], outs[1], outs[3]
+
+
+def attn_fwd_fp8_rotq(q, signs, k8, v8, k_scale, v_scale, causal=False, scale=None, out=None, lse=None,
+                      q8_out=None, q_scale_out=None):
+    """fp8 attention that rotates and quantises bf16 q itself (codes and scales optionally
+    written to q8_out / q_scale_out). Returns (O bf16 [B,H,N,d], LSE fp32 [B,H,N])."""
+    _require(isinstance(q, torch.Tensor) and q.is_cuda and q.dtype == torch.bfloat16 and q.dim() == 4
+             and q.is_contiguous(), "q must be a contiguous bf16 [B, H, N, d] GPU tensor")
+    B, H, N, d = q.shape
+    nblk = (N + 127) // 128
+    for name, t in (("k8", k8), ("v8", v8)):
+        _require(isinstance(t, torch.Tensor) and t.dtype == torch.uint8 and t.shape == q.shape and t.is_contiguous()
+                 and t.device == q.device, f"{name} must be uint8 [B, H, N, d] on q's device")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _require(isinstance(t, torch.Tensor) and t.dtype == torch.float32 and t.shape == (B, H, nblk)
+                 and t.is_contiguous() and t.device == q.device, f"{name} must be fp32 [B, H, ceil(N/128)]")
+    _require(isinstance(signs, torch.Tensor) and signs.dtype == torch.float32 and signs.shape == (d,)
+             and signs.is_contiguous() and signs.device == q.device, "signs must be fp32 [d] on q's device")
+    if q8_out is not None:
+        _require(q8_out.dtype == torch.uint8 and q8_out.shape == q.shape and q8_out.is_contiguous()
+                 and q8_out.device == q.device, "bad q8_out")
+    if q_scale_out is not None:
+        _require(q_scale_out.dtype == torch.float32 and q_scale_out.shape == (B, H, nblk)
+                 and q_scale_out.is_contiguous() and q_scale_out.device == q.device, "bad q_scale_out")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device) if out is None else out
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o.shape == (B, H, N, d) and o.dtype == torch.bfloat16 and o.is_contiguous() and o.device == q.device,
+             "bad out")
+    _require(L.shape == (B, H, N) and L.dtype == torch.float32 and L.is_contiguous() and L.device == q.device,
+             "bad lse")
+    with torch.cuda.device(q.device):
+        st = library().attn_fwd_fp8_rotq(q.data_ptr(), signs.data_ptr(), k8.data_ptr(), v8.data_ptr(),
+                                         k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), L.data_ptr(),
+                                         None if q8_out is None else q8_out.data_ptr(),
+                                         None if q_scale_out is None else q_scale_out.data_ptr(),
+                                         B, H, N, d, int(bool(causal)), float(scale), _stream(q))
+    _check("attn_fwd_fp8_rotq", st)
+    return o, L

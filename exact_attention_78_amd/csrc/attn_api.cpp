@@ -225,6 +225,68 @@ attn_status_t attn_quant_fp8(const void* x, uint8_t* x8, float* scales, const fl
   return from_hip(attn::launch_quant_fp8(x, x8, scales, signs, B * H, N, d, (hipStream_t)stream));
 }
 
+attn_status_t attn_quant_fp8_kv(const void* k, const void* v, const float* signs, uint8_t* k8, uint8_t* v8,
+                                float* k_scale, float* v_scale, int64_t B, int64_t H, int64_t N, int64_t d,
+                                void* stream) {
+  if (!k || !v || !signs || !k8 || !v8 || !k_scale || !v_scale) return ATTN_ERR_INVALID_ARG;
+  int64_t elems, rows;
+  attn_status_t st = check_shape(B, H, N, d, &elems, &rows);
+  if (st != ATTN_OK) return st;
+  const void* ptrs[7] = {k, v, signs, k8, v8, k_scale, v_scale};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (2 * attn::max_workgroups_quant(B * H, N) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  const int64_t nblk = (N + 127) / 128;
+  const uintptr_t sb = (uintptr_t)(B * H * nblk) * sizeof(float);
+  auto span = [](const void* p, uintptr_t n) { return Range{(uintptr_t)p, (uintptr_t)p + n}; };
+  const Range ins[3] = {span(k, (uintptr_t)elems * 2), span(v, (uintptr_t)elems * 2),
+                        span(signs, (uintptr_t)d * sizeof(float))};
+  const Range outs[4] = {span(k8, (uintptr_t)elems), span(v8, (uintptr_t)elems), span(k_scale, sb),
+                         span(v_scale, sb)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return ATTN_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return ATTN_ERR_INVALID_ARG;
+  }
+  return from_hip(attn::launch_quant_fp8_kv(k, v, k8, v8, k_scale, v_scale, signs, B * H, N, d, (hipStream_t)stream));
+}
+
+attn_status_t attn_fwd_fp8_rotq(const void* q, const float* signs, const uint8_t* k8, const uint8_t* v8,
+                                const float* k_scale, const float* v_scale, void* o, float* lse, uint8_t* q8_out,
+                                float* q_scale_out, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                                float scale, void* stream) {
+  if (!q || !signs || !k8 || !v8 || !k_scale || !v_scale || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  int64_t elems, rows;
+  attn_status_t st = check_shape(B, H, N, d, &elems, &rows);
+  if (st != ATTN_OK) return st;
+  if (!scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  const void* ptrs[10] = {q, signs, k8, v8, k_scale, v_scale, o, lse, q8_out ? q8_out : q,
+                          q_scale_out ? (const void*)q_scale_out : q};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  if (d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (attn::max_workgroups_fwd8(B * H, N) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  const int64_t nblk = (N + 127) / 128;
+  const uintptr_t sb = (uintptr_t)(B * H * nblk) * sizeof(float);
+  auto span = [](const void* p, uintptr_t n) { return Range{(uintptr_t)p, (uintptr_t)p + n}; };
+  const Range ins[6] = {span(q, (uintptr_t)elems * 2), span(signs, (uintptr_t)d * sizeof(float)),
+                        span(k8, (uintptr_t)elems), span(v8, (uintptr_t)elems), span(k_scale, sb),
+                        span(v_scale, sb)};
+  const Range outs[4] = {span(o, (uintptr_t)elems * 2), span(lse, (uintptr_t)rows * sizeof(float)),
+                         span(q8_out, q8_out ? (uintptr_t)elems : 0), span(q_scale_out, q_scale_out ? sb : 0)};
+  for (int i = 0; i < 4; ++i) {
+    if (outs[i].lo == outs[i].hi) continue;
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return ATTN_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[j].lo != outs[j].hi && overlaps(outs[i], outs[j])) return ATTN_ERR_INVALID_ARG;
+  }
+  return from_hip(attn::launch_fwd_fp8_rotq(q, signs, k8, v8, k_scale, v_scale, o, lse, q8_out, q_scale_out, B * H, N,
+                                            d, causal != 0, scale, (hipStream_t)stream));
+}
+
 attn_status_t attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                             const void* dout, void* dq, void* dk, void* dv, float* workspace, int64_t B, int64_t H,
                             int64_t N, int64_t d, int causal, float scale, void* stream) {

@@ -62,11 +62,115 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
 // tiles use the same swizzle. It depends on row bits 1..3 only.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-template <bool CAUSAL>
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
+
+// Q preparation fused into the attention kernel ("8.3 FlashAttention-3", section 5.2: the
+// rotation is folded into the kernel's own preprocessing): this lane's 64 elements of its
+// query row, rotated (signs, fast Walsh-Hadamard butterfly, 1/sqrt(d)) and quantised with
+// the scale of the row's 128-row block into the B operand of S^T = K Q^T. The lane holds
+// elements m*64 + half*32 + j (m = 0, 1; j = 0..31), the bytes of qreg[m]. Every value
+// is rounded as attn_quant_fp8 rounds it (the butterfly's stages in order, spans 1..64,
+// each output one rounded add or subtract; one fp32 multiply by 1/sqrt(d); amax/448; the
+// correctly rounded x/scale; clamp; E4M3 round to nearest even), so the codes and scales
+// equal that kernel's. Returns the block's scale; `blk_max` is LDS for one float per wave.
+__device__ __forceinline__ float fused_q_prep(const uint16_t* __restrict__ Qr, bool valid,
+                                              const float* __restrict__ signs, float inv_sqrt_d, int half,
+                                              int wave, int lane, float* blk_max, i32x8 (&qreg)[2]) {
+  float x[64];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e0 = m * 64 + half * 32 + i * 8;
+      const u32x4 raw = valid ? *(const u32x4*)(Qr + e0) : u32x4{0, 0, 0, 0};
+      const f32x4 s0 = *(const f32x4*)(signs + e0), s1 = *(const f32x4*)(signs + e0 + 4);
+      const float sg[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[m * 32 + i * 8 + 2 * e] = bf16_bits_to_f32(raw[e] & 0xFFFFu) * sg[2 * e];     // exact (+-1)
+        x[m * 32 + i * 8 + 2 * e + 1] = bf16_bits_to_f32(raw[e] >> 16) * sg[2 * e + 1];
+      }
+    }
+  // spans 1 .. 16: inside the lane
+#pragma unroll
+  for (int h = 1; h < 32; h *= 2)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if (!(j & h)) {
+          const float a = x[m * 32 + j], b = x[m * 32 + j + h];
+          x[m * 32 + j] = a + b;
+          x[m * 32 + j + h] = a - b;
+        }
+  // span 32: element bit 5 is the lane's half. After the swap lo holds the pair's element
+  // with bit 5 clear (from the lower lane) and hi the one with bit 5 set, in both lanes; the
+  // lower lane keeps lo + hi, the upper lo - hi (one rounded fma with a +-1 factor each).
+  const float hs = half ? -1.f : 1.f;
+#pragma unroll
+  for (int e = 0; e < 64; ++e) {
+    float lo = x[e], hi = x[e];
+    permlane32_swap_pair(lo, hi);
+    x[e] = __builtin_fmaf(hs, hi, lo);
+  }
+  // span 64: inside the lane (m = 0 with m = 1)
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float a = x[j], b = x[32 + j];
+    x[j] = a + b;
+    x[32 + j] = a - b;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 64; ++e) {
+    x[e] *= inv_sqrt_d;
+    amax = __builtin_elementwise_maximum(amax, __builtin_fabsf(x[e]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off /= 2) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if (lane == 0) blk_max[wave] = amax;
+  barrier_lds();
+  const int w0 = (wave / 4) * 4;                       // the 4 waves of this 128-row block
+  amax = fmaxf(fmaxf(blk_max[w0], blk_max[w0 + 1]), fmaxf(blk_max[w0 + 2], blk_max[w0 + 3]));
+  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+  // x / s as the quantiser divides (correctly rounded; a tiny scale is divided in the form
+  // scaled by 2^64, which gives the same quotient)
+  float sd = s;
+  if (s < 0x1p-64f) {
+    sd = s * 0x1p64f;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) x[e] *= 0x1p64f;
+  }
+  const float y_rcp = 1.0f / sd;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    int w[8];
+#pragma unroll
+    for (int e = 0; e < 32; e += 2) {
+      float y[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float xv = x[m * 32 + e + k];
+        const float q0 = xv * y_rcp;
+        const float q = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, sd, xv), y_rcp, q0), xv);
+        y[k] = fminf(fmaxf(q, -448.0f), 448.0f);
+      }
+      if (e % 4 == 0) w[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      else w[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], w[e / 4], true);
+    }
+    qreg[m] = i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
+  }
+  return s;
+}
+
+template <bool CAUSAL, bool FUSEQ>
 __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int nblk, int total_wg, float c_base) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int nblk, int total_wg, float c_base,
+    const uint16_t* __restrict__ Qbf /* FUSEQ: bf16 Q */, const float* __restrict__ signs /* FUSEQ */,
+    uint8_t* __restrict__ q8_out /* FUSEQ, may be null */, float* __restrict__ sq_out /* FUSEQ, may be null */,
+    float inv_sqrt_d /* FUSEQ: fp32 nearest 1/sqrt(d) */) {
   constexpr int ROW = kD;                            // bytes per K/V row
   constexpr int TB = kBN * ROW;                      // bytes per K (or V) tile: 8 KiB
   constexpr int LPW = TB / 1024 / kWaves;            // 1 KiB direct loads per wave per tile
@@ -92,18 +196,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
 
   const int q0 = mt * kBM + wave * 32;               // this wave's 32 rows (inside one Q scale block)
   const int qrow = q0 + l32;
-  const float cq = c_base * SQ[(int64_t)bh * nblk + min(q0 / kScaleRows, nblk - 1)];
+  float cq = 0.f;
+  __shared__ float q_blk_max[kWaves];
 
-  // Q^T as the B operand: for MFMA m (head-dim half), bytes [m*64 + half*32, +32) of the row.
+  // Q^T as the B operand: for MFMA m (head-dim half), bytes [m*64 + half*32, +32) of the row
+  // (FUSEQ: made in the prologue, after the first K/V tile loads are issued).
   i32x8 qreg[2];
+  if constexpr (!FUSEQ) {
+    cq = c_base * SQ[(int64_t)bh * nblk + min(q0 / kScaleRows, nblk - 1)];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    if (qrow < N) {
-      const i32x4 a = *(const i32x4*)(Qh + (int64_t)qrow * kD + m * 64 + half * 32);
-      const i32x4 b = *(const i32x4*)(Qh + (int64_t)qrow * kD + m * 64 + half * 32 + 16);
-      qreg[m] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    } else {
-      qreg[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int m = 0; m < 2; ++m) {
+      if (qrow < N) {
+        const i32x4 a = *(const i32x4*)(Qh + (int64_t)qrow * kD + m * 64 + half * 32);
+        const i32x4 b = *(const i32x4*)(Qh + (int64_t)qrow * kD + m * 64 + half * 32 + 16);
+        qreg[m] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      } else {
+        qreg[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
     }
   }
 
@@ -351,6 +460,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   load_tile(Vh, 0, vbuf(IC<0>{}));
   load_tile(Vh, min(1, T - 1), vbuf(IC<1>{}));
   load_tile(Vh, min(2, T - 1), vbuf(IC<2>{}));
+  if constexpr (FUSEQ) {
+    // rotate and quantise this wave's query rows while the first tiles load
+    const float sqb = fused_q_prep(Qbf + head_off + (int64_t)qrow * kD, qrow < N, signs, inv_sqrt_d, half, wave, lane,
+                                   q_blk_max, qreg);
+    cq = c_base * sqb;
+    if (q8_out != nullptr && qrow < N) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        uint8_t* dst = q8_out + head_off + (int64_t)qrow * kD + m * 64 + half * 32;
+        *(i32x4*)dst = i32x4{qreg[m][0], qreg[m][1], qreg[m][2], qreg[m][3]};
+        *(i32x4*)(dst + 16) = i32x4{qreg[m][4], qreg[m][5], qreg[m][6], qreg[m][7]};
+      }
+    }
+    const int blk = q0 / kScaleRows;
+    if (sq_out != nullptr && wave % 4 == 0 && lane == 0 && blk < nblk) sq_out[(int64_t)bh * nblk + blk] = sqb;
+  }
   wait_vmcnt<0>();
   barrier_lds();
   qk(IC<0>{}, Sa);
@@ -402,14 +527,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   if (half == 0) LSE[(int64_t)bh * N + qrow] = (M + __builtin_log2f(l_tot)) * kLn2;
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool FUSEQ>
 hipError_t launch(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* sq, const float* sk,
-                  const float* sv, void* o, float* lse, int64_t BH, int64_t N, float scale, hipStream_t stream) {
+                  const float* sv, void* o, float* lse, int64_t BH, int64_t N, float scale, const void* qbf,
+                  const float* signs, uint8_t* q8_out, float* sq_out, hipStream_t stream) {
   const int n_mtiles = (int)((N + kBM - 1) / kBM);
   const int nblk = (int)((N + kScaleRows - 1) / kScaleRows);
   const int64_t total = BH * n_mtiles;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL>), dim3((unsigned)total), dim3(kWaves * 64), 0, stream, q8, k8, v8,
-                     sq, sk, sv, (uint16_t*)o, lse, (int)N, n_mtiles, nblk, (int)total, scale * kLog2e);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, FUSEQ>), dim3((unsigned)total), dim3(kWaves * 64), 0, stream, q8, k8,
+                     v8, sq, sk, sv, (uint16_t*)o, lse, (int)N, n_mtiles, nblk, (int)total, scale * kLog2e,
+                     (const uint16_t*)qbf, signs, q8_out, sq_out, (float)(1.0 / __builtin_sqrt((double)kD)));
   return hipGetLastError();
 }
 
@@ -418,8 +545,19 @@ hipError_t launch(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const
 hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* sq, const float* sk,
                           const float* sv, void* o, float* lse, int64_t BH, int64_t N, int64_t /*d*/, bool causal,
                           float scale, hipStream_t stream) {
-  return causal ? launch<true>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, stream)
-                : launch<false>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, stream);
+  return causal ? launch<true, false>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, nullptr, nullptr, nullptr,
+                                      nullptr, stream)
+                : launch<false, false>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, nullptr, nullptr, nullptr,
+                                       nullptr, stream);
+}
+
+hipError_t launch_fwd_fp8_rotq(const void* q, const float* signs, const uint8_t* k8, const uint8_t* v8,
+                               const float* sk, const float* sv, void* o, float* lse, uint8_t* q8_out, float* sq_out,
+                               int64_t BH, int64_t N, int64_t /*d*/, bool causal, float scale, hipStream_t stream) {
+  return causal ? launch<true, true>(nullptr, k8, v8, nullptr, sk, sv, o, lse, BH, N, scale, q, signs, q8_out, sq_out,
+                                     stream)
+                : launch<false, true>(nullptr, k8, v8, nullptr, sk, sv, o, lse, BH, N, scale, q, signs, q8_out,
+                                      sq_out, stream);
 }
 
 int64_t max_workgroups_fwd8(int64_t BH, int64_t N) { return BH * ((N + kBM - 1) / kBM); }

@@ -32,18 +32,17 @@ __device__ __forceinline__ float xor_lane(float x) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
 
+// One (batch*head, 128-row block) of one tensor: workgroup `wg` of a grid over BH * nblk.
 template <int D, bool ROTATE>
-__global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
-                                                             float* __restrict__ scales,
-                                                             const float* __restrict__ signs, int N, int nblk,
-                                                             float inv_sqrt_d) {
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
+                                            float* __restrict__ scales, const float* __restrict__ signs, int N,
+                                            int nblk, float inv_sqrt_d, int wg, float* wave_max) {
   constexpr int EPL = 32;                                      // elements per lane segment
   constexpr int LPR = D / EPL;                                 // lanes per row (4 or 2)
   constexpr int RPP = kThreads / LPR;                          // rows per pass
   constexpr int PASSES = kRowsPerBlock / RPP;                  // 2 or 1
-  __shared__ float wave_max[kThreads / 64];
 
-  const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+  const int bh = wg / nblk, blk = wg % nblk;
   const int tid = threadIdx.x, lane = tid % 64;
   const int seg = tid % LPR;                                   // this lane's segment of a row
   const int64_t base = ((int64_t)bh * N + (int64_t)blk * kRowsPerBlock) * D;
@@ -159,6 +158,31 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __r
   if (tid == 0) scales[(int64_t)bh * nblk + blk] = s;
 }
 
+template <int D, bool ROTATE>
+__global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8,
+                                                             float* __restrict__ scales,
+                                                             const float* __restrict__ signs, int N, int nblk,
+                                                             float inv_sqrt_d) {
+  __shared__ float wave_max[kThreads / 64];
+  quant_block<D, ROTATE>(X, X8, scales, signs, N, nblk, inv_sqrt_d, blockIdx.x, wave_max);
+}
+
+// K (rotated) and V (unrotated) of one attention call in one launch: the first BH * nblk
+// workgroups take K's blocks, the rest V's.
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_fp8_kv_kernel(const uint16_t* __restrict__ K,
+                                                                const uint16_t* __restrict__ V,
+                                                                uint8_t* __restrict__ K8, uint8_t* __restrict__ V8,
+                                                                float* __restrict__ sk, float* __restrict__ sv,
+                                                                const float* __restrict__ signs, int N, int nblk,
+                                                                int n_wg_k, float inv_sqrt_d) {
+  __shared__ float wave_max[kThreads / 64];
+  if ((int)blockIdx.x < n_wg_k)
+    quant_block<D, true>(K, K8, sk, signs, N, nblk, inv_sqrt_d, blockIdx.x, wave_max);
+  else
+    quant_block<D, false>(V, V8, sv, nullptr, N, nblk, inv_sqrt_d, blockIdx.x - n_wg_k, wave_max);
+}
+
 template <int D>
 hipError_t launch(const void* x, uint8_t* x8, float* sc, const float* signs, int64_t BH, int64_t N,
                   hipStream_t stream) {
@@ -174,7 +198,26 @@ hipError_t launch(const void* x, uint8_t* x8, float* sc, const float* signs, int
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_kv(const void* k, const void* v, uint8_t* k8, uint8_t* v8, float* sk, float* sv, const float* signs,
+                     int64_t BH, int64_t N, hipStream_t stream) {
+  const int nblk = (int)((N + kRowsPerBlock - 1) / kRowsPerBlock);
+  const float inv_sqrt_d = (float)(1.0 / __builtin_sqrt((double)D));
+  const int64_t n_wg = BH * nblk;
+  hipLaunchKernelGGL((quant_fp8_kv_kernel<D>), dim3((unsigned)(2 * n_wg)), dim3(kThreads), 0, stream,
+                     (const uint16_t*)k, (const uint16_t*)v, k8, v8, sk, sv, signs, (int)N, nblk, (int)n_wg,
+                     inv_sqrt_d);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_quant_fp8_kv(const void* k, const void* v, uint8_t* k8, uint8_t* v8, float* k_scales,
+                               float* v_scales, const float* signs, int64_t BH, int64_t N, int64_t d,
+                               hipStream_t stream) {
+  return d == 128 ? launch_kv<128>(k, v, k8, v8, k_scales, v_scales, signs, BH, N, stream)
+                  : launch_kv<64>(k, v, k8, v8, k_scales, v_scales, signs, BH, N, stream);
+}
 
 hipError_t launch_quant_fp8(const void* x, uint8_t* x8, float* scales, const float* signs, int64_t BH, int64_t N,
                             int64_t d, hipStream_t stream) {

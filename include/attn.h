@@ -161,6 +161,31 @@ attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* 
 attn_status_t attn_quant_fp8(const void* x, uint8_t* x8, float* scales, const float* signs,
                              int64_t B, int64_t H, int64_t N, int64_t d, void* stream);
 
+/* K and V preparation of one fp8 attention call in a single launch: k (bf16 [B, H, N, d])
+ * rotated with `signs` and quantised, v quantised unrotated, each exactly as
+ * attn_quant_fp8(k, signs) and attn_quant_fp8(v, NULL) would (same codes and scales).
+ * signs must not be NULL. Outputs must not overlap each other or the inputs. */
+attn_status_t attn_quant_fp8_kv(const void* k, const void* v, const float* signs, uint8_t* k8, uint8_t* v8,
+                                float* k_scale, float* v_scale, int64_t B, int64_t H, int64_t N, int64_t d,
+                                void* stream);
+
+/* fp8 attention with the preparation of Q fused into the attention kernel ("8.3
+ * FlashAttention-3", section 5.2: the Hadamard rotation is folded into the preprocessing
+ * the kernel already does, at almost no extra cost). q is bf16 [B, H, N, d] (d = 128);
+ * each workgroup owns 256 query rows, i.e. two whole 128-row scale blocks, so it rotates
+ * its rows (x * signs * H_d / sqrt(d), the fp32 butterfly of attn_quant_fp8), takes each
+ * block's amax, scale and E4M3 codes in registers, and runs the attention of attn_fwd_fp8
+ * on them. k8, v8, k_scale, v_scale as for attn_fwd_fp8 (e.g. from attn_quant_fp8_kv with
+ * the same signs). If q8_out / q_scale_out are not NULL they receive the Q codes
+ * (uint8 [B, H, N, d]) and scales (fp32 [B, H, ceil(N/128)]) the kernel made, which equal
+ * those of attn_quant_fp8(q, signs); O and LSE then equal attn_fwd_fp8's on those codes
+ * bit for bit. signs must not be NULL. */
+attn_status_t attn_fwd_fp8_rotq(const void* q, const float* signs, const uint8_t* k8, const uint8_t* v8,
+                                const float* k_scale, const float* v_scale, void* o, float* lse,
+                                uint8_t* q8_out, float* q_scale_out,
+                                int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                                void* stream);
+
 /* Backward pass of attn_fwd_bf16 (FlashAttention-2 digest, key technical points and
  * method summary: the gradients are recomputed from the one stored log-sum-exp per row,
  * with the same split of the work as the forward pass). Inputs: q, k, v, the forward

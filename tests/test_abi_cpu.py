@@ -42,6 +42,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
     names = header_functions()
     assert set(names) == {"attn_fwd_bf16", "attn_fwd_f16", "attn_fwd_f32", "attn_fwd_fp8", "attn_quant_fp8",
                           "attn_fwd_variant", "attn_calibrate", "attn_calibrate_ops", "attn_decode_bf16_noalloc",
+                          "attn_quant_fp8_kv", "attn_fwd_fp8_rotq",
                           "attn_bwd_bf16", "attn_bwd_f16", "attn_decode_bf16", "attn_decode_f16",
                           "attn_decode_workspace_floats", "attn_status_string", "attn_abi_version"}
     for n in names:
@@ -107,6 +108,32 @@ def test_fp8_validation(lib, defect, expect):
                 causal=1, scale=0.0884)
     args.update(defect)
     assert lib.attn_fwd_fp8(*args.values(), None) == expect
+
+
+@no_gpu_only
+@pytest.mark.parametrize("defect,expect", [
+    (dict(k=None), INVALID), (dict(signs=None), INVALID), (dict(v8=None), INVALID), (dict(sv=None), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(N=0), INVALID), (dict(k8=A[0]), INVALID), (dict(v8=A[3]), INVALID),
+    (dict(sk=A[6]), INVALID), (dict(sv=A[5] + 4), INVALID), (dict(signs=A[2] + 4), INVALID),
+])
+def test_quant_kv_validation(lib, defect, expect):
+    args = dict(k=A[0], v=A[1], signs=A[2], k8=A[3], v8=A[4], sk=A[5], sv=A[6], B=1, H=1, N=256, d=128)
+    args.update(defect)
+    assert lib.attn_quant_fp8_kv(*args.values(), None) == expect
+
+
+@no_gpu_only
+@pytest.mark.parametrize("defect,expect", [
+    (dict(q=None), INVALID), (dict(signs=None), INVALID), (dict(k8=None), INVALID), (dict(o=None), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(N=0), INVALID), (dict(scale=0.0), INVALID), (dict(o=A[0]), INVALID),
+    (dict(q8o=A[2]), INVALID), (dict(sqo=A[4] + 8), INVALID), (dict(q8o=A[6]), INVALID),
+    (dict(q8o=A[8] + 4), INVALID), (dict(sqo=A[7]), INVALID),
+])
+def test_fp8_rotq_validation(lib, defect, expect):
+    args = dict(q=A[0], signs=A[1], k8=A[2], v8=A[3], sk=A[4], sv=A[5], o=A[6], lse=A[7], q8o=A[8], sqo=A[9],
+                B=1, H=1, N=256, d=128, causal=1, scale=0.0884)
+    args.update(defect)
+    assert lib.attn_fwd_fp8_rotq(*args.values(), None) == expect
 
 
 @no_gpu_only

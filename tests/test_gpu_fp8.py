@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_78_amd import attn_fwd_fp8, attn_quant_fp8, inputs
+from exact_attention_78_amd import attn_fwd_fp8, attn_fwd_fp8_rotq, attn_quant_fp8, attn_quant_fp8_kv, inputs
 from oracle import fp8 as ofp8
 from oracle.attention import attention_forward
 from oracle.pool import forward_pooled
@@ -302,3 +302,81 @@ def test_tensors_over_2_31_elements():
     rows = np.unique(np.concatenate([np.arange(0, 4), [255, 256, N - 1], np.random.default_rng(13).integers(0, N, 24)]))
     Oref, Lref = attention_forward(*deq, True, scale, rows=rows)
     compare(O[:, :, rows], L[:, :, rows], Oref, Lref, f"heads {hs}: quantiser bit-exact")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("N", [300, 1000, 1])
+def test_quant_kv_one_launch_bit_exact(N, d):
+    # K rotated and V unrotated in one launch: the codes and scales of the oracle's quantiser
+    say(f"case quant kv N={N} d={d}")
+    _, k, v, signs = inputs.draw_fp8_workload(24 + N % 7, 2, 3, N, d)
+    tk, kx = bf16_activations(k)
+    tv, vx = bf16_activations(v)
+    k8, sk, v8, sv = attn_quant_fp8_kv(tk.cuda(), tv.cuda(), torch.from_numpy(signs).cuda())
+    torch.cuda.synchronize()
+    rk, rsk = ofp8.quantize_blocks(ofp8.rotate_f32(kx, signs))
+    rv, rsv = ofp8.quantize_blocks(vx)
+    for got, ref in ((k8, rk), (sk, rsk), (v8, rv), (sv, rsv)):
+        np.testing.assert_array_equal(got.cpu().numpy(), ref)
+
+
+def fused_case(wid, B, H, N, d, tweak=None):
+    q, k, v, signs = inputs.draw_fp8_workload(wid, B, H, N, d)
+    if tweak is not None:
+        tweak(q)
+    xs = [bf16_activations(t) for t in (q, k, v)]
+    sg = torch.from_numpy(signs).cuda()
+    gq, gk, gv = (x[0].cuda() for x in xs)
+    k8, sk, v8, sv = attn_quant_fp8_kv(gk, gv, sg)
+    return xs, signs, sg, gq, (k8, sk, v8, sv)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", [(1, 2, 1000, 128), (2, 2, 256, 128), (1, 1, 77, 128), (1, 1, 1, 128),
+                                   (1, 3, 300, 128)])
+def test_fused_q_preparation(shape, causal):
+    # The attention kernel rotates and quantises Q itself: its codes and scales equal the
+    # oracle's quantiser bit for bit (also for an all-zero block and a block whose scale is
+    # subnormal), its O and LSE equal attn_fwd_fp8's on the separately quantised Q bit for
+    # bit, and both meet the fp8 gate against the oracle.
+    B, H, N, d = shape
+    say(f"case fused Q shape={shape} causal={causal}")
+
+    def tweak(q):
+        if N >= 256 and H >= 3:
+            q[0, 2, 128:256] = 0.0
+            q[0, 1, 0:128] *= np.float32(1e-39)
+    xs, signs, sg, gq, (k8, sk, v8, sv) = fused_case(34 + N % 5, B, H, N, d, tweak)
+    scale = inputs.softmax_scale(d)
+    nblk = (N + 127) // 128
+    q8o = torch.full((B, H, N, d), 0x7F, dtype=torch.uint8, device="cuda")
+    sqo = torch.full((B, H, nblk), float("nan"), dtype=torch.float32, device="cuda")
+    o_f, l_f = attn_fwd_fp8_rotq(gq, sg, k8, v8, sk, sv, causal=causal, scale=scale, q8_out=q8o, q_scale_out=sqo)
+    q8, sq = attn_quant_fp8(gq, sg)
+    o_s, l_s = attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rq, rsq = ofp8.quantize_blocks(ofp8.rotate_f32(xs[0][1], signs))
+    np.testing.assert_array_equal(q8o.cpu().numpy(), rq)
+    np.testing.assert_array_equal(sqo.cpu().numpy(), rsq)
+    assert torch.equal(o_f, o_s) and torch.equal(l_f, l_s)
+    p = {"q8": rq, "sq": rsq, "k8": k8.cpu().numpy(), "sk": sk.cpu().numpy(), "v8": v8.cpu().numpy(),
+         "sv": sv.cpu().numpy()}
+    deq = [ofp8.dequantize_blocks(p[c], p[s_]) for c, s_ in (("q8", "sq"), ("k8", "sk"), ("v8", "sv"))]
+    Oref, Lref = attention_forward(*deq, causal, scale)
+    compare(o_f.double().cpu().numpy(), l_f.double().cpu().numpy(), Oref, Lref, f"fused Q {shape} causal={causal}")
+
+
+def test_fused_fp8_path_c5_every_row():
+    # The fp8 workload through the two-launch path (K/V quantiser, attention with fused Q
+    # preparation) against the oracle on every head and every row.
+    w = inputs.WORKLOADS["C5"]
+    say("case fused fp8 path C5: every head, every row")
+    xs, signs, sg, gq, (k8, sk, v8, sv) = fused_case(w.wid, w.B, w.H, w.N, w.d)
+    o, lse = attn_fwd_fp8_rotq(gq, sg, k8, v8, sk, sv, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    p = ofp8.prepare_fp8(*[x[1] for x in xs], signs)
+    for name, t in (("k8", k8), ("sk", sk), ("v8", v8), ("sv", sv)):
+        np.testing.assert_array_equal(t.cpu().numpy(), p[name])
+    deq = [ofp8.dequantize_blocks(p[c], p[s_]) for c, s_ in (("q8", "sq"), ("k8", "sk"), ("v8", "sv"))]
+    Oref, Lref = forward_pooled(*deq, True, w.scale)
+    compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), Oref, Lref, "C5 fused path, every row")
