@@ -187,7 +187,7 @@ attn_status_t attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* 
   const void* ptrs[8] = {q8, k8, v8, q_scale, k_scale, v_scale, o, lse};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
-  if (d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (attn::max_workgroups_fwd8(B * H, N) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
   const int64_t nblk = (N + 127) / 128;
   const uintptr_t sb = (uintptr_t)(B * H * nblk) * sizeof(float);
@@ -266,7 +266,7 @@ attn_status_t attn_fwd_fp8_rotq(const void* q, const float* signs, const uint8_t
                           q_scale_out ? (const void*)q_scale_out : q};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
-  if (d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (attn::max_workgroups_fwd8(B * H, N) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
   const int64_t nblk = (N + 127) / 128;
   const uintptr_t sb = (uintptr_t)(B * H * nblk) * sizeof(float);

@@ -1,4 +1,4 @@
-// fp8 (E4M3FN) exact attention forward on gfx950, head dim 128.
+// fp8 (E4M3FN) exact attention forward on gfx950, head dim 64 or 128.
 //
 // Inputs are E4M3 codes with one fp32 scale per 128-row block of each (batch, head)
 // ("8.3 FlashAttention-3", section 5.1: block quantisation; section 5: fp8 operands,
@@ -36,7 +36,6 @@
 namespace attn {
 namespace {
 
-constexpr int kD = 128;
 constexpr int kBN = 64;
 constexpr int kWaves = 8;
 constexpr int kBM = kWaves * 32;
@@ -58,27 +57,31 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(p));
 }
 
-// 16-byte chunk c (of 8 per 128-byte row) of tile row r lives at chunk c ^ swz(r); K and V
-// tiles use the same swizzle. It depends on row bits 1..3 only.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// 16-byte chunk c (of D/16 per row of D bytes) of tile row r lives at chunk c ^ swz(r); K
+// and V tiles use the same swizzle. It depends on row bits 1..3 (d = 128) or 1..2 (d = 64).
+template <int D>
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & (D / 16 - 1); }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
 
 // Q preparation fused into the attention kernel ("8.3 FlashAttention-3", section 5.2: the
-// rotation is folded into the kernel's own preprocessing): this lane's 64 elements of its
+// rotation is folded into the kernel's own preprocessing): this lane's D/2 elements of its
 // query row, rotated (signs, fast Walsh-Hadamard butterfly, 1/sqrt(d)) and quantised with
 // the scale of the row's 128-row block into the B operand of S^T = K Q^T. The lane holds
-// elements m*64 + half*32 + j (m = 0, 1; j = 0..31), the bytes of qreg[m]. Every value
+// elements m*64 + half*32 + j (m < D/64; j = 0..31), the bytes of qreg[m]. Every value
 // is rounded as attn_quant_fp8 rounds it (the butterfly's stages in order, spans 1..64,
 // each output one rounded add or subtract; one fp32 multiply by 1/sqrt(d); amax/448; the
 // correctly rounded x/scale; clamp; E4M3 round to nearest even), so the codes and scales
-// equal that kernel's. Returns the block's scale; `blk_max` is LDS for one float per wave.
+// equal that kernel's (spans 1..16 inside the lane, 32 across the lane pair l, l^32, 64
+// inside the lane). Returns the block's scale; `blk_max` is LDS for one float per wave.
+template <int D>
 __device__ __forceinline__ float fused_q_prep(const uint16_t* __restrict__ Qr, bool valid,
                                               const float* __restrict__ signs, float inv_sqrt_d, int half,
-                                              int wave, int lane, float* blk_max, i32x8 (&qreg)[2]) {
-  float x[64];
+                                              int wave, int lane, float* blk_max, i32x8 (&qreg)[D / 64]) {
+  constexpr int NM = D / 64;                           // 64-element groups per row (MFMA k-steps)
+  float x[NM * 32];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e0 = m * 64 + half * 32 + i * 8;
@@ -95,7 +98,7 @@ __device__ __forceinline__ float fused_q_prep(const uint16_t* __restrict__ Qr, b
 #pragma unroll
   for (int h = 1; h < 32; h *= 2)
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < NM; ++m)
 #pragma unroll
       for (int j = 0; j < 32; ++j)
         if (!(j & h)) {
@@ -108,21 +111,23 @@ __device__ __forceinline__ float fused_q_prep(const uint16_t* __restrict__ Qr, b
   // lower lane keeps lo + hi, the upper lo - hi (one rounded fma with a +-1 factor each).
   const float hs = half ? -1.f : 1.f;
 #pragma unroll
-  for (int e = 0; e < 64; ++e) {
+  for (int e = 0; e < NM * 32; ++e) {
     float lo = x[e], hi = x[e];
     permlane32_swap_pair(lo, hi);
     x[e] = __builtin_fmaf(hs, hi, lo);
   }
-  // span 64: inside the lane (m = 0 with m = 1)
+  // span 64 (d = 128): inside the lane (m = 0 with m = 1)
+  if constexpr (NM == 2) {
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float a = x[j], b = x[32 + j];
-    x[j] = a + b;
-    x[32 + j] = a - b;
+    for (int j = 0; j < 32; ++j) {
+      const float a = x[j], b = x[32 + j];
+      x[j] = a + b;
+      x[32 + j] = a - b;
+    }
   }
   float amax = 0.f;
 #pragma unroll
-  for (int e = 0; e < 64; ++e) {
+  for (int e = 0; e < NM * 32; ++e) {
     x[e] *= inv_sqrt_d;
     amax = __builtin_elementwise_maximum(amax, __builtin_fabsf(x[e]));
   }
@@ -139,11 +144,11 @@ __device__ __forceinline__ float fused_q_prep(const uint16_t* __restrict__ Qr, b
   if (s < 0x1p-64f) {
     sd = s * 0x1p64f;
 #pragma unroll
-    for (int e = 0; e < 64; ++e) x[e] *= 0x1p64f;
+    for (int e = 0; e < NM * 32; ++e) x[e] *= 0x1p64f;
   }
   const float y_rcp = 1.0f / sd;
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < NM; ++m) {
     int w[8];
 #pragma unroll
     for (int e = 0; e < 32; e += 2) {
@@ -163,7 +168,7 @@ __device__ __forceinline__ float fused_q_prep(const uint16_t* __restrict__ Qr, b
   return s;
 }
 
-template <bool CAUSAL, bool FUSEQ>
+template <int D, bool CAUSAL, bool FUSEQ>
 __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ SQ, const float* __restrict__ SK, const float* __restrict__ SV,
@@ -171,13 +176,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     const uint16_t* __restrict__ Qbf /* FUSEQ: bf16 Q */, const float* __restrict__ signs /* FUSEQ */,
     uint8_t* __restrict__ q8_out /* FUSEQ, may be null */, float* __restrict__ sq_out /* FUSEQ, may be null */,
     float inv_sqrt_d /* FUSEQ: fp32 nearest 1/sqrt(d) */) {
-  constexpr int ROW = kD;                            // bytes per K/V row
-  constexpr int TB = kBN * ROW;                      // bytes per K (or V) tile: 8 KiB
-  constexpr int LPW = TB / 1024 / kWaves;            // 1 KiB direct loads per wave per tile
+  constexpr int ROW = D;                             // bytes per K/V row
+  constexpr int TB = kBN * ROW;                      // bytes per K (or V) tile: 8 KiB (d = 128), 4 KiB (d = 64)
+  constexpr int LOADERS = TB / 1024;                 // waves that load a tile, 1 KiB each: 8 or 4
   constexpr int NS = 4;                              // ring slots per operand
   constexpr int NKB = kBN / 32;                      // 32-key blocks per tile
-  constexpr int NDB = kD / 32;                       // 32-wide head-dim blocks of O
-  static_assert(LPW == 1, "one direct load per wave per tile");
+  constexpr int NM = D / 64;                         // 64-element MFMA k-steps over the head dim
+  constexpr int NDB = D / 32;                        // 32-wide head-dim blocks of O
+  static_assert(LOADERS >= 1 && LOADERS <= kWaves && LOADERS * 1024 == TB, "whole 1 KiB loads");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];   // K ring, then V ring
 
   int bh, mt;
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64;
   const int half = lane / 32, l32 = lane % 32;
-  const int64_t head_off = (int64_t)bh * N * kD;
+  const int64_t head_off = (int64_t)bh * N * D;
   const uint8_t* Qh = Q + head_off;
   const uint8_t* Kh = K + head_off;
   const uint8_t* Vh = V + head_off;
@@ -201,14 +207,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
 
   // Q^T as the B operand: for MFMA m (head-dim half), bytes [m*64 + half*32, +32) of the row
   // (FUSEQ: made in the prologue, after the first K/V tile loads are issued).
-  i32x8 qreg[2];
+  i32x8 qreg[NM];
   if constexpr (!FUSEQ) {
     cq = c_base * SQ[(int64_t)bh * nblk + min(q0 / kScaleRows, nblk - 1)];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < NM; ++m) {
       if (qrow < N) {
-        const i32x4 a = *(const i32x4*)(Qh + (int64_t)qrow * kD + m * 64 + half * 32);
-        const i32x4 b = *(const i32x4*)(Qh + (int64_t)qrow * kD + m * 64 + half * 32 + 16);
+        const i32x4 a = *(const i32x4*)(Qh + (int64_t)qrow * D + m * 64 + half * 32);
+        const i32x4 b = *(const i32x4*)(Qh + (int64_t)qrow * D + m * 64 + half * 32 + 16);
         qreg[m] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
       } else {
         qreg[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -220,9 +226,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * kBM + kBN - 1) / kBN) : n_ktiles;
 
   // K fragment (kb, m): row kb*32 + l32, chunks m*4 + half*2 and +1 (32 bytes).
-  uint32_t kaddr[2];
+  uint32_t kaddr[NM];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) kaddr[m] = l32 * ROW + (((m * 4 + half * 2) ^ swz(l32)) << 4);
+  for (int m = 0; m < NM; ++m) kaddr[m] = l32 * ROW + (((m * 4 + half * 2) ^ swz<D>(l32)) << 4);
   // V^T fragment (db): four 8-byte transpose reads; read m covers the keys
   // (m/2)*32 + ((m%2)*2 + j/4)*8 + tr_h*4 + j%4, the order of this lane's P bytes. The
   // row offsets of m (multiples of 16) leave the swizzle unchanged.
@@ -234,19 +240,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     const int col = db * 32 + tr_col;
-    vaddr[db] = tr_row * ROW + (((col >> 4) ^ swz(tr_row)) << 4) + (col & 15);
+    vaddr[db] = tr_row * ROW + (((col >> 4) ^ swz<D>(tr_row)) << 4) + (col & 15);
   }
 
-  // Direct global -> LDS loads: wave w fills bytes [w*1024, +1024) of a tile, 16 per lane.
+  // Direct global -> LDS loads: wave w < LOADERS fills bytes [w*1024, +1024) of a tile, 16
+  // per lane; the other waves load nothing (their waits on their own loads pass at once,
+  // and every wave waits at the barrier for the loaders).
   const int ld_slot = wave * 1024 + lane * 16;
   const int ld_row = ld_slot / ROW;
-  const int ld_ch = ((ld_slot % ROW) / 16) ^ swz(ld_row);
+  const int ld_ch = ((ld_slot % ROW) / 16) ^ swz<D>(ld_row);
   const int ld_off = ld_row * ROW + ld_ch * 16;
   auto kbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* { return lds + decltype(SLOT)::value * TB; };
   auto vbuf = [&](auto SLOT) __attribute__((always_inline)) -> uint8_t* {
     return lds + (NS + decltype(SLOT)::value) * TB;
   };
   auto load_tile = [&](const uint8_t* src, int kt, uint8_t* dst) __attribute__((always_inline)) {
+    if (LOADERS < kWaves && wave >= LOADERS) return;
     if (kt * kBN + kBN <= N) {
       dma_load16(src + (int64_t)kt * TB + ld_off, lds_u32(dst) + wave * 1024);
     } else {   // rows past the end re-read the last row (masked scores, P = 0)
@@ -265,7 +274,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     for (int kb = 0; kb < NKB; ++kb) {
       S[kb] = f32x16{};
 #pragma unroll
-      for (int m = 0; m < 2; ++m) S[kb] = mfma_fp8(kfrag(kbuf(SLOT), kb, m), qreg[m], S[kb]);
+      for (int m = 0; m < NM; ++m) S[kb] = mfma_fp8(kfrag(kbuf(SLOT), kb, m), qreg[m], S[kb]);
     }
   };
 
@@ -386,10 +395,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
       const float ct = cq * sk_next;
       const bool uchg = weight(sv_next, w_soft);
       const float lw = __builtin_amdgcn_logf(w_soft);     // log2 w
-      // Main block in issue order: 4 S^T MFMAs (K fragments one MFMA ahead) and 4 P.V
+      // Main block in issue order: NQ S^T MFMAs (K fragments one MFMA ahead) and NDB P.V
       // MFMAs (V^T fragments one MFMA ahead); the row max runs beside the first two S^T
-      // MFMAs, the exponentials beside the other six.
-      i32x8 kf[4], vf[NDB];
+      // MFMAs, the exponentials beside the others (d = 128: 4 + 4, six slots; d = 64: 2 + 2,
+      // two slots).
+      constexpr int NQ = NKB * NM;
+      i32x8 kf[NQ], vf[NDB];
       auto kread = [&](int i) __attribute__((always_inline)) { kf[i] = kfrag(kbuf(KRD), i % NKB, i / NKB); };
       auto vread = [&](int db) __attribute__((always_inline)) {
         int av[8];
@@ -403,9 +414,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
       };
       float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
       float lsum[2] = {0.f, 0.f}, bias = 0.f;
-      // six slots (S^T MFMAs 2, 3 and the four P.V MFMAs) share the 32 scores; slot k issues
-      // the arguments of slot k+1, the exponentials of slot k and the sums of slot k-1
-      constexpr int NSLOT = 6;
+      // NSLOT slots (the S^T MFMAs after the first two, and the P.V MFMAs) share the 32
+      // scores; slot k issues the arguments of slot k+1, the exponentials of slot k and the
+      // sums of slot k-1
+      constexpr int NSLOT = NQ - 2 + NDB;
+      static_assert(NQ >= 2, "the row max needs two S^T MFMAs");
       auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
       auto exps_slot = [&](int slot) __attribute__((always_inline)) {
         if (slot + 1 < NSLOT) args(S_soft, ct, bias, lo(slot + 1), lo(slot + 2));
@@ -414,8 +427,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
       };
       kread(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {               // i = m * NKB + kb
-        if (i + 1 < 4) kread(i + 1);
+      for (int i = 0; i < NQ; ++i) {              // i = m * NKB + kb
+        if (i + 1 < NQ) kread(i + 1);
         else vread(0);
         const int kb = i % NKB, m = i / NKB;
         S_new[kb] = mfma_fp8(kf[i], qreg[m], m == 0 ? f32x16{} : S_new[kb]);
@@ -441,14 +454,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
           const int one4 = 0x38383838 + (t >> 30);
           lacc = mfma_fp8(i32x8{one4, one4, one4, one4, one4, one4, one4, one4}, pb, f32x16{});
         }
-        exps_slot(2 + db);
+        exps_slot(NQ - 2 + db);
       }
       finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
       l_part = __builtin_fmaf(lsum[0] + lsum[1], w_soft, l_part);
       sk_next = tile_sk(t + 2);
       sv_next = tile_sv(t + 2);
     }
-    wait_vmcnt<2 * LPW>();   // K(t+3) and V(t+1), issued a step earlier, have landed
+    wait_vmcnt<2>();         // K(t+3) and V(t+1), issued a step earlier, have landed
     barrier_lds();
   };
 
@@ -462,13 +475,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   load_tile(Vh, min(2, T - 1), vbuf(IC<2>{}));
   if constexpr (FUSEQ) {
     // rotate and quantise this wave's query rows while the first tiles load
-    const float sqb = fused_q_prep(Qbf + head_off + (int64_t)qrow * kD, qrow < N, signs, inv_sqrt_d, half, wave, lane,
-                                   q_blk_max, qreg);
+    const float sqb = fused_q_prep<D>(Qbf + head_off + (int64_t)qrow * D, qrow < N, signs, inv_sqrt_d, half, wave,
+                                      lane, q_blk_max, qreg);
     cq = c_base * sqb;
     if (q8_out != nullptr && qrow < N) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        uint8_t* dst = q8_out + head_off + (int64_t)qrow * kD + m * 64 + half * 32;
+      for (int m = 0; m < NM; ++m) {
+        uint8_t* dst = q8_out + head_off + (int64_t)qrow * D + m * 64 + half * 32;
         *(i32x4*)dst = i32x4{qreg[m][0], qreg[m][1], qreg[m][2], qreg[m][3]};
         *(i32x4*)(dst + 16) = i32x4{qreg[m][4], qreg[m][5], qreg[m][6], qreg[m][7]};
       }
@@ -513,7 +526,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   const float l_tot = add_halves(l_part) * (1.f / (1 << (int)kPShift));   // sum of probabilities
   if (qrow >= N) return;
   const float inv = U / l_rnd;
-  uint16_t* Orow = O + head_off + (int64_t)qrow * kD;
+  uint16_t* Orow = O + head_off + (int64_t)qrow * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -527,37 +540,48 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   if (half == 0) LSE[(int64_t)bh * N + qrow] = (M + __builtin_log2f(l_tot)) * kLn2;
 }
 
-template <bool CAUSAL, bool FUSEQ>
+template <int D, bool CAUSAL, bool FUSEQ>
 hipError_t launch(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* sq, const float* sk,
                   const float* sv, void* o, float* lse, int64_t BH, int64_t N, float scale, const void* qbf,
                   const float* signs, uint8_t* q8_out, float* sq_out, hipStream_t stream) {
   const int n_mtiles = (int)((N + kBM - 1) / kBM);
   const int nblk = (int)((N + kScaleRows - 1) / kScaleRows);
   const int64_t total = BH * n_mtiles;
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, FUSEQ>), dim3((unsigned)total), dim3(kWaves * 64), 0, stream, q8, k8,
-                     v8, sq, sk, sv, (uint16_t*)o, lse, (int)N, n_mtiles, nblk, (int)total, scale * kLog2e,
-                     (const uint16_t*)qbf, signs, q8_out, sq_out, (float)(1.0 / __builtin_sqrt((double)kD)));
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, CAUSAL, FUSEQ>), dim3((unsigned)total), dim3(kWaves * 64), 0, stream, q8,
+                     k8, v8, sq, sk, sv, (uint16_t*)o, lse, (int)N, n_mtiles, nblk, (int)total, scale * kLog2e,
+                     (const uint16_t*)qbf, signs, q8_out, sq_out, (float)(1.0 / __builtin_sqrt((double)D)));
   return hipGetLastError();
+}
+
+template <bool FUSEQ>
+hipError_t launch_d(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* sq, const float* sk,
+                    const float* sv, void* o, float* lse, int64_t BH, int64_t N, int64_t d, bool causal, float scale,
+                    const void* qbf, const float* signs, uint8_t* q8_out, float* sq_out, hipStream_t stream) {
+  if (d == 128)
+    return causal ? launch<128, true, FUSEQ>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, qbf, signs, q8_out, sq_out,
+                                             stream)
+                  : launch<128, false, FUSEQ>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, qbf, signs, q8_out,
+                                              sq_out, stream);
+  return causal ? launch<64, true, FUSEQ>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, qbf, signs, q8_out, sq_out,
+                                          stream)
+                : launch<64, false, FUSEQ>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, qbf, signs, q8_out, sq_out,
+                                           stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* sq, const float* sk,
-                          const float* sv, void* o, float* lse, int64_t BH, int64_t N, int64_t /*d*/, bool causal,
+                          const float* sv, void* o, float* lse, int64_t BH, int64_t N, int64_t d, bool causal,
                           float scale, hipStream_t stream) {
-  return causal ? launch<true, false>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, nullptr, nullptr, nullptr,
-                                      nullptr, stream)
-                : launch<false, false>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, scale, nullptr, nullptr, nullptr,
-                                       nullptr, stream);
+  return launch_d<false>(q8, k8, v8, sq, sk, sv, o, lse, BH, N, d, causal, scale, nullptr, nullptr, nullptr, nullptr,
+                         stream);
 }
 
 hipError_t launch_fwd_fp8_rotq(const void* q, const float* signs, const uint8_t* k8, const uint8_t* v8,
                                const float* sk, const float* sv, void* o, float* lse, uint8_t* q8_out, float* sq_out,
-                               int64_t BH, int64_t N, int64_t /*d*/, bool causal, float scale, hipStream_t stream) {
-  return causal ? launch<true, true>(nullptr, k8, v8, nullptr, sk, sv, o, lse, BH, N, scale, q, signs, q8_out, sq_out,
-                                     stream)
-                : launch<false, true>(nullptr, k8, v8, nullptr, sk, sv, o, lse, BH, N, scale, q, signs, q8_out,
-                                      sq_out, stream);
+                               int64_t BH, int64_t N, int64_t d, bool causal, float scale, hipStream_t stream) {
+  return launch_d<true>(nullptr, k8, v8, nullptr, sk, sv, o, lse, BH, N, d, causal, scale, q, signs, q8_out, sq_out,
+                        stream);
 }
 
 int64_t max_workgroups_fwd8(int64_t BH, int64_t N) { return BH * ((N + kBM - 1) / kBM); }

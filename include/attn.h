@@ -35,7 +35,7 @@
  *                            > 0, a pointer not 16-byte aligned, an element count that
  *                            overflows int64, or an output range overlapping an input
  *                            or another output;
- *      ATTN_ERR_UNSUPPORTED  d not in {64, 128} (fp8 entry points: d = 128 only);
+ *      ATTN_ERR_UNSUPPORTED  d not in {64, 128};
  *      ATTN_ERR_LAUNCH       the kernel launch itself failed (hipGetLastError).
  *  - Numbers: inputs with NaN or Inf give undefined outputs (not checked on the device).
  *    Any N >= 1 is accepted; partial tiles are masked.
@@ -134,7 +134,7 @@ attn_status_t attn_fwd_f32(const float* q, const float* k, const float* v, float
                            void* stream);
 
 /* fp8 attention ("8.3 FlashAttention-3", section 5: fp8 inputs with per-block scales).
- * q8/k8/v8 are OCP E4M3FN codes [B, H, N, d] (d = 128); q_scale/k_scale/v_scale are the
+ * q8/k8/v8 are OCP E4M3FN codes [B, H, N, d] (d = 64 or 128); q_scale/k_scale/v_scale are the
  * fp32 scales of each 128-row block, so the value of a code x in block t is
  * decode(x) * scale[b, h, t]. O is bf16 [B, H, N, d], LSE fp32 [B, H, N]. Scores
  * accumulate e4m3 x e4m3 products in fp32 and are scaled by q_scale * k_scale * scale;
@@ -171,7 +171,7 @@ attn_status_t attn_quant_fp8_kv(const void* k, const void* v, const float* signs
 
 /* fp8 attention with the preparation of Q fused into the attention kernel ("8.3
  * FlashAttention-3", section 5.2: the Hadamard rotation is folded into the preprocessing
- * the kernel already does, at almost no extra cost). q is bf16 [B, H, N, d] (d = 128);
+ * the kernel already does, at almost no extra cost). q is bf16 [B, H, N, d] (d = 64, 128);
  * each workgroup owns 256 query rows, i.e. two whole 128-row scale blocks, so it rotates
  * its rows (x * signs * H_d / sqrt(d), the fp32 butterfly of attn_quant_fp8), takes each
  * block's amax, scale and E4M3 codes in registers, and runs the attention of attn_fwd_fp8

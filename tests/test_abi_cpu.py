@@ -99,7 +99,8 @@ def test_fwd_variant_validation(lib, defect, expect):
 
 @no_gpu_only
 @pytest.mark.parametrize("defect,expect", [
-    (dict(q8=None), INVALID), (dict(sk=None), INVALID), (dict(o=None), INVALID), (dict(d=64), UNSUPPORTED),
+    (dict(q8=None), INVALID), (dict(sk=None), INVALID), (dict(o=None), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(d=32), UNSUPPORTED),
     (dict(N=0), INVALID), (dict(scale=0.0), INVALID), (dict(sv=A[5] + 4), INVALID), (dict(o=A[0]), INVALID),
     (dict(lse=A[3]), INVALID), (dict(o=A[7] - 16), INVALID),
 ])
@@ -125,7 +126,7 @@ def test_quant_kv_validation(lib, defect, expect):
 @no_gpu_only
 @pytest.mark.parametrize("defect,expect", [
     (dict(q=None), INVALID), (dict(signs=None), INVALID), (dict(k8=None), INVALID), (dict(o=None), INVALID),
-    (dict(d=64), UNSUPPORTED), (dict(N=0), INVALID), (dict(scale=0.0), INVALID), (dict(o=A[0]), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(N=0), INVALID), (dict(scale=0.0), INVALID), (dict(o=A[0]), INVALID),
     (dict(q8o=A[2]), INVALID), (dict(sqo=A[4] + 8), INVALID), (dict(q8o=A[6]), INVALID),
     (dict(q8o=A[8] + 4), INVALID), (dict(sqo=A[7]), INVALID),
 ])

@@ -121,7 +121,8 @@ def compare(O, L, Oref, Lref, label):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("shape", [(1, 2, 1000, 128), (2, 2, 256, 128), (1, 1, 77, 128), (1, 1, 1, 128)])
+@pytest.mark.parametrize("shape", [(1, 2, 1000, 128), (2, 2, 256, 128), (1, 1, 77, 128), (1, 1, 1, 128),
+                                   (1, 2, 1000, 64), (2, 2, 256, 64), (1, 1, 77, 64), (1, 1, 1, 64)])
 def test_fp8_attention_small(shape, causal):
     B, H, N, d = shape
     say(f"case fp8 attention shape={shape} causal={causal}")
@@ -191,15 +192,16 @@ def test_rotation_lowers_fp8_error_with_outliers():
     assert errs[True] < errs[False]
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("factor", [1.5, 4.0, 30.0])
-def test_fp8_scores_jumping_past_the_first_tile_max(factor, causal):
+def test_fp8_scores_jumping_past_the_first_tile_max(factor, causal, d):
     # K activations from key 300 on are scaled up before quantisation, so their scores rise
     # far above the first key tile's row max (x4, x30), or a little above it for some rows
     # (x1.5). The running max must then move, with the accumulators rescaled, so that the
     # E4M3 codes of the probabilities stay in range.
-    B, H, N, d = 1, 2, 700, 128
-    say(f"case fp8 jumping scores x{factor} causal={causal}")
+    B, H, N = 1, 2, 700
+    say(f"case fp8 jumping scores x{factor} causal={causal} d={d}")
     q, k, v, signs = inputs.draw_fp8_workload(52, B, H, N, d)
     k = k.copy()
     k[:, :, 300:] *= np.float32(factor)
@@ -333,7 +335,7 @@ def fused_case(wid, B, H, N, d, tweak=None):
 
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("shape", [(1, 2, 1000, 128), (2, 2, 256, 128), (1, 1, 77, 128), (1, 1, 1, 128),
-                                   (1, 3, 300, 128)])
+                                   (1, 3, 300, 128), (1, 2, 1000, 64), (1, 3, 300, 64), (1, 1, 1, 64)])
 def test_fused_q_preparation(shape, causal):
     # The attention kernel rotates and quantises Q itself: its codes and scales equal the
     # oracle's quantiser bit for bit (also for an all-zero block and a block whose scale is
@@ -380,3 +382,24 @@ def test_fused_fp8_path_c5_every_row():
     deq = [ofp8.dequantize_blocks(p[c], p[s_]) for c, s_ in (("q8", "sq"), ("k8", "sk"), ("v8", "sv"))]
     Oref, Lref = forward_pooled(*deq, True, w.scale)
     compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), Oref, Lref, "C5 fused path, every row")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_head_dim_64_every_row(causal):
+    # fp8 at head dim 64 on B2 H16 N8192 (the fp8 workload's shape with d = 64, the same
+    # outlier recipe): the separate path and the fused-Q path, every head and every row.
+    B, H, N, d = 2, 16, 8192, 64
+    say(f"case fp8 d64 B{B} H{H} N{N} causal={causal}: every head, every row")
+    xs, signs, sg, gq, (k8, sk, v8, sv) = fused_case(15, B, H, N, d)
+    scale = inputs.softmax_scale(d)
+    q8, sq = attn_quant_fp8(gq, sg)
+    o_s, l_s = attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal, scale=scale)
+    o_f, l_f = attn_fwd_fp8_rotq(gq, sg, k8, v8, sk, sv, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_f, o_s) and torch.equal(l_f, l_s)
+    p = ofp8.prepare_fp8(*[x[1] for x in xs], signs)
+    for name, t in (("q8", q8), ("sq", sq), ("k8", k8), ("sk", sk), ("v8", v8), ("sv", sv)):
+        np.testing.assert_array_equal(t.cpu().numpy(), p[name])
+    deq = [ofp8.dequantize_blocks(p[c], p[s_]) for c, s_ in (("q8", "sq"), ("k8", "sk"), ("v8", "sv"))]
+    Oref, Lref = forward_pooled(*deq, causal, scale)
+    compare(o_f.double().cpu().numpy(), l_f.double().cpu().numpy(), Oref, Lref, f"fp8 d64 causal={causal}")
