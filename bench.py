@@ -150,6 +150,31 @@ def calibration_leg(torch, ea):
     return res
 
 
+def schedules(torch, ea, flops, rounds, calls, call):
+    """Every tile schedule of the forward pass on one workload, timed in interleaved rounds
+    (each round times `calls` back-to-back calls of every schedule in turn), so that all
+    schedules see the same clock; per schedule the median over rounds."""
+    names = list(ea._binding.SCHEDULES)
+    for s in names:
+        call(s)
+    torch.cuda.synchronize()
+    per = {s: [] for s in names}
+    for _ in range(rounds):
+        for s in names:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(calls):
+                call(s)
+            e1.record()
+            torch.cuda.synchronize()
+            per[s].append(e0.elapsed_time(e1) / calls)
+    out = {}
+    for s in names:
+        ms = statistics.median(per[s])
+        out[s] = {"us": ms * 1e3, "tflops": flops / (ms * 1e-3) / 1e12}
+    return out
+
+
 def forward_legs(torch, ea, inputs, w, gq, gk, gv, o, lse, steps, warmup, calib):
     """Exact pass alone, all tiles needing the exact pass, schedules, C1-C4, C2 cold, exps/s."""
     res = {}
@@ -158,41 +183,6 @@ def forward_legs(torch, ea, inputs, w, gq, gk, gv, o, lse, steps, warmup, calib)
     def leg(fn, work=flops, n=steps, wu=warmup, **kw):
         t = time_launches(torch, fn, n, wu, **kw)
         return {"us": us(t), "tflops": rate(work, t), "frac_bf16_peak": rate(work, t) / PEAK_BF16_TFLOPS}
-
-    res["exact_pass_only"] = leg(lambda: ea.attn_fwd_variant(gq, gk, gv, causal=True, scale=w.scale, passes="exact",
-                                                             out=o, lse=lse))
-    res["exact_pass_only"]["what"] = ("the running-max online softmax alone on every tile (per-tile row max, lazy "
-                                      "rescale), same inputs as the headline")
-    # keys from 300 on scaled x30: every query tile past row 300 outgrows the first tile's max
-    import numpy as np
-
-    k_marked = inputs.normal_f32(w.wid, inputs.K_ID, (w.B, w.H, w.N, w.d))
-    k_marked[:, :, 300:] *= np.float32(30.0)
-    gkm = inputs.to_torch(k_marked, "bf16").cuda()
-    del k_marked
-    res["all_tiles_marked"] = leg(lambda: ea.attn_fwd_bf16(gq, gkm, gv, causal=True, scale=w.scale, out=o, lse=lse))
-    res["all_tiles_marked"]["what"] = ("the headline call on inputs whose keys from 300 on are scaled x30: the first "
-                                       "pass marks every query tile that sees them and stops, the exact pass redoes them")
-    del gkm
-
-    sched = {}
-    queue = ea.queue_workspace()
-    for s in ea._binding.SCHEDULES:
-        sched[s] = leg(lambda s=s: ea.attn_fwd_variant(gq, gk, gv, causal=True, scale=w.scale, sched=s, queue=queue,
-                                                       out=o, lse=lse), n=max(5, steps // 2), wu=3)
-    res["schedules_H"] = {k: {"us": v["us"]["mean_us"], "tflops": v["tflops"]} for k, v in sched.items()}
-    for name in ("C3", "C4"):
-        c = inputs.WORKLOADS[name]
-        q, k, v = (inputs.to_torch(x, "bf16").cuda() for x in inputs.draw_qkv(c.wid, c.B, c.H, c.N, c.d))
-        oc, lc = torch.empty_like(q), torch.empty((c.B, c.H, c.N), device="cuda", dtype=torch.float32)
-        f = counted_flops(c.B, c.H, c.N, c.d, True)
-        out = {}
-        for s in ("default", "persistent_stride", "persistent_queue", "linear_natural"):
-            r = leg(lambda s=s: ea.attn_fwd_variant(q, k, v, causal=True, scale=c.scale, sched=s, queue=queue,
-                                                    out=oc, lse=lc), work=f, n=max(5, steps // 2), wu=3)
-            out[s] = {"us": r["us"]["mean_us"], "tflops": r["tflops"]}
-        res[f"schedules_{name}_causal"] = out
-        del q, k, v, oc, lc
 
     cfg = {}
     for name, causal in (("C1", False), ("C1", True), ("C2", True), ("C3", True), ("C3", False), ("C4", True)):
@@ -214,6 +204,37 @@ def forward_legs(torch, ea, inputs, w, gq, gk, gv, o, lse, steps, warmup, calib)
             del scratch
         del q, k, v
     res["configs"] = cfg
+
+    res["exact_pass_only"] = leg(lambda: ea.attn_fwd_variant(gq, gk, gv, causal=True, scale=w.scale, passes="exact",
+                                                             out=o, lse=lse))
+    res["exact_pass_only"]["what"] = ("the running-max online softmax alone on every tile (per-tile row max, lazy "
+                                      "rescale), same inputs as the headline")
+    # keys from 300 on scaled x30: every query tile past row 300 outgrows the first tile's max
+    import numpy as np
+
+    k_marked = inputs.normal_f32(w.wid, inputs.K_ID, (w.B, w.H, w.N, w.d))
+    k_marked[:, :, 300:] *= np.float32(30.0)
+    gkm = inputs.to_torch(k_marked, "bf16").cuda()
+    del k_marked
+    res["all_tiles_marked"] = leg(lambda: ea.attn_fwd_bf16(gq, gkm, gv, causal=True, scale=w.scale, out=o, lse=lse))
+    res["all_tiles_marked"]["what"] = ("the headline call on inputs whose keys from 300 on are scaled x30: the first "
+                                       "pass marks every query tile that sees them and stops, the exact pass redoes them")
+    del gkm
+
+    queue = ea.queue_workspace()
+    for name in ("C3", "C4", "H"):
+        c = inputs.WORKLOADS[name]
+        if name == "H":
+            q, k, v, oc, lc = gq, gk, gv, o, lse
+        else:
+            q, k, v = (inputs.to_torch(x, "bf16").cuda() for x in inputs.draw_qkv(c.wid, c.B, c.H, c.N, c.d))
+            oc, lc = torch.empty_like(q), torch.empty((c.B, c.H, c.N), device="cuda", dtype=torch.float32)
+        res[f"schedules_{name}_causal"] = schedules(
+            torch, ea, counted_flops(c.B, c.H, c.N, c.d, True), rounds=4, calls=max(3, steps // 4),
+            call=lambda s, q=q, k=k, v=v, oc=oc, lc=lc, sc=c.scale: ea.attn_fwd_variant(
+                q, k, v, causal=True, scale=sc, sched=s, queue=queue, out=oc, lse=lc))
+        del q, k, v, oc, lc
+
     return res
 
 
@@ -267,6 +288,11 @@ def fp8_leg(torch, ea, inputs, steps, warmup):
     tqnt = time_launches(torch, quant_all, steps, warmup)
     tatt = time_launches(torch, lambda: ea.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=True, out=o, lse=lse), steps,
                          warmup)
+    # the two-launch path: K and V quantised in one launch, Q prepared inside the attention kernel
+    tkv = time_launches(torch, lambda: ea.attn_quant_fp8_kv(tk, tv, sg, k8=k8, v8=v8, k_scale=sk, v_scale=sv), steps,
+                        warmup)
+    trq = time_launches(torch, lambda: ea.attn_fwd_fp8_rotq(tq, sg, k8, v8, sk, sv, causal=True, out=o, lse=lse),
+                        steps, warmup)
     flops = counted_flops(w.B, w.H, w.N, w.d, True)
     n = w.B * w.H * w.N * w.d
     nblk = (w.N + 127) // 128
@@ -277,6 +303,13 @@ def fp8_leg(torch, ea, inputs, steps, warmup):
         "attn_us": us(tatt), "attn_tflops": rate(flops, tatt), "attn_frac_fp8_peak": rate(flops, tatt) / PEAK_FP8_TFLOPS,
         "quant_qkv_us": us(tqnt), "quant_gbs": rate(qbytes, tqnt, 1e9),
         "quant_frac_hbm": rate(qbytes, tqnt, 1e9) / PEAK_HBM_GBS,
+        "path_three_quant_launches_plus_attention_us": (tqnt["mean_ms"] + tatt["mean_ms"]) * 1e3,
+        "fused_q": {
+            "what": "K and V quantised in one launch (attn_quant_fp8_kv), Q rotated and quantised inside the "
+                    "attention kernel (attn_fwd_fp8_rotq)",
+            "quant_kv_us": us(tkv), "quant_kv_gbs": rate(2 * qbytes / 3, tkv, 1e9),
+            "attn_rotq_us": us(trq), "attn_rotq_tflops": rate(flops, trq),
+            "path_us": (tkv["mean_ms"] + trq["mean_ms"]) * 1e3},
     }
 
 
@@ -308,6 +341,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-extra", action="store_true", help="headline only: skip every other leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--only", choices=["fp8", "backward", "decode"],
+                    help="run only this leg (for profiler runs) and print its JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB x 4 (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -332,6 +367,11 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": 2 * (1 << 30), "launches": 4}))
         return
 
+    if args.only in ("fp8", "decode"):
+        fn = fp8_leg if args.only == "fp8" else decode_leg
+        print(json.dumps({args.only: fn(torch, ea, inputs, args.steps, args.warmup)}))
+        return
+
     w = inputs.WORKLOADS["H"]
     q, k, v = inputs.draw_qkv(w.wid, w.B, w.H, w.N, w.d)
     cpu = tuple(inputs.to_torch(x, "bf16") for x in (q, k, v))
@@ -344,15 +384,22 @@ def main():
     def step():
         ea.attn_fwd_bf16(gq, gk, gv, causal=True, scale=w.scale, out=o, lse=lse)
 
+    if args.only == "backward":
+        print(json.dumps({"backward": backward_leg(torch, ea, inputs, w, (gq, gk, gv), o, lse, args.steps,
+                                                   args.warmup)}))
+        return
+
     extra = {}
     if not args.no_extra:
         legs_steps, legs_warm = max(5, min(args.steps, 20)), max(3, min(args.warmup, 10))
+        # the forward legs come last: the headline then starts with the chip already at the
+        # clock it holds under this kernel's load
         extra["calibration"] = calibration_leg(torch, ea)
-        extra["forward"] = forward_legs(torch, ea, inputs, w, gq, gk, gv, o, lse, legs_steps, legs_warm,
-                                        extra["calibration"])
         extra["backward"] = backward_leg(torch, ea, inputs, w, (gq, gk, gv), o, lse, legs_steps, legs_warm)
         extra["fp8"] = fp8_leg(torch, ea, inputs, legs_steps, legs_warm)
         extra["decode"] = decode_leg(torch, ea, inputs, legs_steps, 4 * legs_warm)
+        extra["forward"] = forward_legs(torch, ea, inputs, w, gq, gk, gv, o, lse, legs_steps, legs_warm,
+                                        extra["calibration"])
 
     # the headline: W untimed steps, then exactly K timed steps, one event pair per launch
     torch.cuda.synchronize()

@@ -77,12 +77,12 @@ template <> struct Swz<64> {
   static __device__ __forceinline__ int v(int r) { return ((r >> 1) & 1) << 2; }
 };
 
-template <typename Tag, int D, bool CAUSAL, int W, bool FAST>
+template <typename Tag, int D, bool CAUSAL, int W, bool FAST, bool PERSIST>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int total_wg, float c /* scale*log2 e */,
     int check_marks /* exact pass: redo marked tiles only (1) or every tile (0) */,
-    int order /* TileOrder of a plain grid */, int persist /* 0: plain grid, 1: persistent stride, 2: queue */,
+    int order /* TileOrder of a plain grid */, int persist /* PERSIST: 1 fixed stride, 2 queue */,
     int* __restrict__ queue /* persist 2: 8 tile counters, then 8 exit counts */) {
   constexpr int BM = W * 32;                        // query rows per workgroup
   constexpr int NSTEP = D / 16;                     // MFMA k-steps over the head dim
@@ -418,26 +418,28 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   // that order (longest first when causal). Its workgroups take either every P-th of them
   // (P workgroups per queue: a fixed stride, as a persistent kernel that walks its share
   // in a loop does), or the next one from the queue's counter, an atomic in caller memory.
+  // (The plain grid is a separate instantiation without the loop, so that the compiler
+  // keeps the one-tile kernel's code as it is.)
+  if constexpr (!PERSIST) {
+    int bh, mt;
+    query_tile_ordered(order, blockIdx.x, total_wg, n_mtiles, CAUSAL, bh, mt);
+    tile(bh, mt);
+    return;
+  }
   __shared__ int ticket;
   const int xq = blockIdx.x % 8, per_q = gridDim.x / 8;
   for (int it = 0;; ++it) {
-    int w = blockIdx.x;
-    if (persist != 0) {
-      int tk = blockIdx.x / 8 + it * per_q;
-      __syncthreads();             // every wave is done with the previous tile's LDS flags and ticket
-      if (persist == 2) {
-        if (threadIdx.x == 0) ticket = atomicAdd(queue + xq, 1);
-        __syncthreads();
-        tk = ticket;
-      }
-      const int64_t wl = (int64_t)tk * 8 + xq;
-      if (wl < 0 || wl >= total_wg) break;   // every workgroup reaches this: the tickets only grow
-      w = (int)wl;
-    } else if (it > 0) {
-      break;
+    int tk = blockIdx.x / 8 + it * per_q;
+    __syncthreads();               // every wave is done with the previous tile's LDS flags and ticket
+    if (persist == 2) {
+      if (threadIdx.x == 0) ticket = atomicAdd(queue + xq, 1);
+      __syncthreads();
+      tk = ticket;
     }
+    const int64_t wl = (int64_t)tk * 8 + xq;
+    if (wl < 0 || wl >= total_wg) break;   // every workgroup reaches this: the tickets only grow
     int bh, mt;
-    query_tile_ordered(persist != 0 ? (int)kOrderXcdPairs : order, w, total_wg, n_mtiles, CAUSAL, bh, mt);
+    query_tile_ordered(kOrderXcdPairs, (int)wl, total_wg, n_mtiles, CAUSAL, bh, mt);
     tile(bh, mt);
   }
   if (persist == 2 && threadIdx.x == 0) {
@@ -473,13 +475,21 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
   const int persist = var.sched >= kSchedPersistentStride ? var.sched - kSchedPersistentStride + 1 : 0;
   const int order = persist ? 0 : var.sched;
   const unsigned grid = persist ? (unsigned)persistent_workgroups() : (unsigned)total;
-  if (two_pass)
-    hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, true>), dim3(grid), dim3(W * 64), 0,
-                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
-                       n_mtiles, (int)total, scale * kLog2e, 1, order, persist, var.queue);
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, false>), dim3(grid), dim3(W * 64), 0,
-                     stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, (int)N,
-                     n_mtiles, (int)total, scale * kLog2e, two_pass ? 1 : 0, order, persist, var.queue);
+  auto run = [&](auto FASTC, auto PERSISTC) {
+    hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, decltype(FASTC)::value, decltype(PERSISTC)::value>),
+                       dim3(grid), dim3(W * 64), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
+                       (const uint16_t*)v, (uint16_t*)o, lse, (int)N, n_mtiles, (int)total, scale * kLog2e,
+                       decltype(FASTC)::value ? 1 : (two_pass ? 1 : 0), order, persist, var.queue);
+  };
+  using T1 = std::true_type;
+  using F0 = std::false_type;
+  if (persist) {
+    if (two_pass) run(T1{}, T1{});
+    run(F0{}, T1{});
+  } else {
+    if (two_pass) run(T1{}, F0{});
+    run(F0{}, F0{});
+  }
   return hipGetLastError();
 }
 
