@@ -354,7 +354,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     for (int e = e0; e < e1; ++e) {
       const float pe = S[e / 16][e % 16];
       lsum[e % 2] += pe;
-      if (e % 4 == 1) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(S[e / 16][e % 16 - 1], pe, 0, false);
+      // (the first pair of a word writes bytes 0-1 over the word's previous contents, a
+      // tile's codes that were consumed a step earlier: bytes 2-3 are written next)
+      if (e % 4 == 1) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(S[e / 16][e % 16 - 1], pe, P[e / 4], false);
       if (e % 4 == 3) P[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(S[e / 16][e % 16 - 1], pe, P[e / 4], true);
     }
   };
@@ -369,7 +371,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   };
 
   f32x16 Sa[NKB], Sb[NKB];
-  int Pa[8], Pb[8];
+  int Pa[8] = {}, Pb[8] = {};
+  // all-ones A operand (E4M3 1.0) of the code-sum MFMA, kept in eight registers for the
+  // whole loop: eight distinct per-lane expressions (0 <= qrow < 2^31 - 8, so each shift
+  // adds 0) that the compiler can neither merge into one register nor fold to a constant
+  i32x8 ones;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ones[k] = 0x38383838 + ((qrow + k) >> 31);
   bool pend = false;     // wave-uniform: an O rescale is owed
   // w of the tile whose code sum lacc holds, and of the tile whose softmax ran last; the
   // K and V block scales of the tile whose softmax runs next, loaded one step early so
@@ -449,10 +457,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
         const i32x8 pb = {P_use[0], P_use[1], P_use[2], P_use[3], P_use[4], P_use[5], P_use[6], P_use[7]};
         oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
         if (db == NDB - 1) {
-          // all-ones A operand (E4M3 1.0), built here from a value tied to t so that it is
-          // not kept live across the loop (t < 2^30, so the shift adds 0)
-          const int one4 = 0x38383838 + (t >> 30);
-          lacc = mfma_fp8(i32x8{one4, one4, one4, one4, one4, one4, one4, one4}, pb, f32x16{});
+          lacc = mfma_fp8(ones, pb, f32x16{});
         }
         exps_slot(NQ - 2 + db);
       }
