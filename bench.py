@@ -138,6 +138,16 @@ def calibration_leg(torch, ea):
         res[f"{kind}_loop"] = {"value": rate(ops, t, scale), "unit": unit, "us": t["mean_ms"] * 1e3,
                                "workgroups": wg}
     res["mfma_loop"]["frac_of_published_peak"] = res["mfma_loop"]["value"] / PEAK_BF16_TFLOPS
+    # MFMA loops with the attention kernels' work between MFMAs (one fma, exp and add each)
+    mixes = {}
+    for kind, what in (("mix_nolds_2w", "no LDS read, 2 waves/SIMD"),
+                       ("mix_lds1_2w", "one 16-byte LDS read per MFMA, 2 waves/SIMD"),
+                       ("mix_lds0.5_2w", "one LDS read per 2 MFMAs, 2 waves/SIMD"),
+                       ("mix_lds0.5_1w", "one LDS read per 2 MFMAs, 1 wave/SIMD")):
+        out, ops = ea.attn_calibrate(kind, wg, 400)
+        t = time_launches(torch, lambda: ea.attn_calibrate(kind, wg, 400, out=out), 5, 2)
+        mixes[kind] = {"tflops": rate(ops, t), "what": what}
+    res["mfma_mix_loops"] = mixes
     n = 8192
     a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
     b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)

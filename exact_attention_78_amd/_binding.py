@@ -168,10 +168,16 @@ def attn_fwd_variant(q, k, v, causal=False, scale=None, sched="default", passes=
     return o, L
 
 
+# attn_calibrate kinds (see attn.h): the dense loops, and MFMA loops with the kernels' mix
+# of work between MFMAs (one fma, exp and add each; LDS reads per MFMA; waves per SIMD)
+CALIBRATION_KINDS = {"mfma": 0, "exp": 1, "mix_lds1_2w": 2, "mix_lds0.5_2w": 3, "mix_lds0.5_1w": 4,
+                     "mix_nolds_2w": 5}
+
+
 def attn_calibrate(kind, workgroups, iters, seed=None, out=None):
     """Launch a calibration loop (kind "mfma" or "exp") on the current stream; returns the
     output tensor and the operations it performs (FLOPs or exponentials)."""
-    k = {"mfma": 0, "exp": 1}[kind]
+    k = CALIBRATION_KINDS[kind]
     dev = torch.device("cuda", torch.cuda.current_device())
     seed = torch.tensor([0x3F803F80, 0x3F003F00, 0x3F403F40, 0x3E803E80], dtype=torch.int64).to(torch.int32).to(dev) \
         if seed is None else seed

@@ -336,14 +336,14 @@ attn_status_t attn_decode_f16(const void* q, const void* k, const void* v, void*
 
 attn_status_t attn_calibrate(int kind, const uint32_t* seed, float* out, int64_t workgroups, int iters,
                              void* stream) {
-  if ((kind != 0 && kind != 1) || !seed || !out || workgroups < 1 || workgroups > INT32_MAX || iters < 1)
+  if (kind < 0 || kind > 5 || !seed || !out || workgroups < 1 || workgroups > INT32_MAX || iters < 1)
     return ATTN_ERR_INVALID_ARG;
   if (!aligned16(seed) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
   return from_hip(attn::launch_calib(kind, seed, out, workgroups, iters, (hipStream_t)stream));
 }
 
 int64_t attn_calibrate_ops(int kind, int iters) {
-  if ((kind != 0 && kind != 1) || iters < 1) return -1;
+  if (kind < 0 || kind > 5 || iters < 1) return -1;
   return attn::calib_ops_per_workgroup(kind, iters);
 }
 

@@ -45,6 +45,7 @@ constexpr int kBN = 64;        // keys per tile
 constexpr int kWaves = 8;      // waves per workgroup (32 query rows each)
 constexpr int kKD = 4;         // S^T MFMAs by which a K fragment read runs ahead
 constexpr int kVD = 2;         // P.V MFMAs by which a V fragment read runs ahead
+constexpr int kTail = 1;       // last MFMAs of a step that carry no exponentials (they cover the step's last sums and packing)
 constexpr float kTau = 8.0f;   // lazy-rescale threshold for the running max, in log2 units
 // Two launches per call. The fast pass computes no per-tile row max: every tile uses the
 // max of the first tile, which softmax allows (the result does not depend on the
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
                       __attribute__((always_inline)) {
 #pragma unroll
       for (int e = e0; e < e1; ++e) {
-        lsum[e % 2] += S[e / 16][e % 16];
+        lsum[e % 2] = e < 2 ? S[e / 16][e % 16] : lsum[e % 2] + S[e / 16][e % 16];   // chains start at e = 0, 1
         if (e % 2 == 1) P[e / 16][(e % 16) / 8][(e % 8) / 2] = pack2(Tag{}, S[e / 16][e % 16 - 1], S[e / 16][e % 16]);
       }
     };
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
         // one or two per MFMA; (fast pass) the exponentials from the second MFMA on.
         constexpr int NQ = NKB * NSTEP, NP = NDB * NKB * 2, KD = kKD, VD = kVD;
         constexpr int NMAX = FAST ? 1 : 5;                 // MFMAs before the first exponential
-        constexpr int NSLOT = NQ + NP - NMAX;              // MFMAs that carry exponentials
+        constexpr int NSLOT = NQ + NP - NMAX - kTail;      // MFMAs that carry exponentials
         u32x4 kf[NQ], vf[NP];
         auto kread = [&](int i) __attribute__((always_inline)) {   // i = s * NKB + kb
           kf[i] = *(const u32x4*)(kread_base(KRD) + (i % NKB) * 32 * ROW + kaddr[i / NKB]);
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
         float m4[4] = {S_soft[0][0], S_soft[0][1], S_soft[0][2], S_soft[0][3]};
         float lsum[2] = {0.f, 0.f};
         // slot k: arguments of slot k+1, exponentials of slot k, sums and packing of slot k-1
-        auto lo = [&](int slot) __attribute__((always_inline)) { return slot * (NKB * 16) / NSLOT; };
+        auto lo = [&](int slot) __attribute__((always_inline)) { return min(slot * (NKB * 16) / NSLOT, NKB * 16); };
         auto exps_slot = [&](int slot) __attribute__((always_inline)) {
           if (slot + 1 < NSLOT) args(S_soft, lo(slot + 1), lo(slot + 2));
           exps(S_soft, lo(slot), lo(slot + 1));
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
           oacc[db] = mfma32(Tag{}, vf[i], P_use[kb][h], oacc[db]);
           exps_slot(NQ - NMAX + i);
         }
-        finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
+        if constexpr (kTail == 0) finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
         const float lt = lsum[0] + lsum[1];
         l_part += lt;
         if constexpr (FAST) ovf |= !(lt <= kGuard);

@@ -56,22 +56,82 @@ __global__ __launch_bounds__(kCalWaves * 64, 1) void calib_exp_kernel(const uint
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// MFMA loop with other work between the MFMAs, to price what the attention kernels put
+// there: after every 32x32x16 bf16 MFMA, NF fp32 FMAs, NE exponentials and NA adds on
+// registers independent of the MFMAs, and one 16-byte LDS read (ds_read_b128) every
+// 16/ND MFMAs that feeds the next MFMA's A operand (ND = 0: none). WV waves per
+// workgroup (8: two per SIMD, 4: one per SIMD; the 128 KiB of LDS keep one workgroup per
+// CU). Each wave runs iters x 16 MFMAs over four accumulators.
+template <int NF, int NE, int NA, int ND, int WV>
+__global__ __launch_bounds__(WV * 64, 1) void calib_mix_kernel(const uint32_t* __restrict__ seed, float* out,
+                                                               int iters) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[131072];
+  const int lane = threadIdx.x % 64;
+  for (int i = threadIdx.x; i < 131072 / 4; i += WV * 64) ((uint32_t*)lds)[i] = seed[i % 4];
+  __syncthreads();
+  const u32x4 a = {seed[lane % 4], seed[(lane + 1) % 4], seed[(lane + 2) % 4], seed[(lane + 3) % 4]};
+  const u32x4 b = a;
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f32x16{};
+  float x[16], y[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    x[j] = 0.5f + 0.001f * lane + j * 0.01f;
+    y[j] = 0.25f + j * 0.02f;
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      u32x4 aa = a;
+      // lane * 16 + m * 1024 + (it % 4) * 16384 + 16 <= 131072: inside the array
+      if (ND > 0 && m % (16 / ND) == 0) aa = *(const u32x4*)(lds + lane * 16 + m * 1024 + (it & 3) * 16384);
+      acc[m % 4] = mfma32(Bf16Tag{}, aa, b, acc[m % 4]);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) x[(m * 3 + f) % 16] = __builtin_fmaf(x[(m * 3 + f) % 16], 0.999f, y[f % 16]);
+#pragma unroll
+      for (int e = 0; e < NE; ++e) y[(m * 5 + e) % 16] = fast_exp2(-y[(m * 5 + e) % 16]);
+#pragma unroll
+      for (int d = 0; d < NA; ++d) x[(m * 7 + d + 1) % 16] += y[(m + d) % 16];
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += acc[c][r];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sum += x[j] + y[j];
+  out[(int64_t)blockIdx.x * 512 + threadIdx.x] = sum;
+}
+
+// kinds 2..5 of attn_calibrate: the mixes above
+struct Mix {
+  int waves;
+};
+constexpr Mix kMix[4] = {{8}, {8}, {4}, {8}};
+
 }  // namespace
 
 hipError_t launch_calib(int kind, const uint32_t* seed, float* out, int64_t workgroups, int iters,
                         hipStream_t stream) {
-  if (kind == 0)
-    hipLaunchKernelGGL(calib_mfma_kernel, dim3((unsigned)workgroups), dim3(kCalWaves * 64), 0, stream, seed, out,
-                       iters);
-  else
-    hipLaunchKernelGGL(calib_exp_kernel, dim3((unsigned)workgroups), dim3(kCalWaves * 64), 0, stream, seed, out,
-                       iters);
+  const dim3 grid((unsigned)workgroups);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(calib_mfma_kernel, grid, dim3(kCalWaves * 64), 0, stream, seed, out, iters); break;
+    case 1: hipLaunchKernelGGL(calib_exp_kernel, grid, dim3(kCalWaves * 64), 0, stream, seed, out, iters); break;
+    case 2: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 16, 8>), grid, dim3(8 * 64), 0, stream, seed, out, iters); break;
+    case 3: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 8, 8>), grid, dim3(8 * 64), 0, stream, seed, out, iters); break;
+    case 4: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 8, 4>), grid, dim3(4 * 64), 0, stream, seed, out, iters); break;
+    default: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 0, 8>), grid, dim3(8 * 64), 0, stream, seed, out, iters); break;
+  }
   return hipGetLastError();
 }
 
 int64_t calib_ops_per_workgroup(int kind, int iters) {
-  // MFMA: FLOPs; exp: exponentials
-  return kind == 0 ? (int64_t)kCalWaves * iters * kChains * 32768 : (int64_t)kCalWaves * 64 * iters * 16;
+  // MFMA kinds: FLOPs; exp: exponentials
+  if (kind == 0) return (int64_t)kCalWaves * iters * kChains * 32768;
+  if (kind == 1) return (int64_t)kCalWaves * 64 * iters * 16;
+  return (int64_t)kMix[kind - 2].waves * iters * 16 * 32768;
 }
 
 }  // namespace attn

@@ -249,12 +249,17 @@ int64_t attn_decode_workspace_floats(int64_t B, int64_t H, int64_t Nq, int64_t N
  * a dense loop of independent 32x32x16 bf16 MFMAs, kind 1 a dense loop of v_exp_f32
  * (exponentials; "8.3 FlashAttention-3", section 1, names the exponential unit as the
  * softmax's bottleneck next to the matrix units), each in `workgroups` workgroups of 512
- * threads (the attention kernels' launch shape) for `iters` iterations. seed: device
- * memory of 4 uint32 values (operands, so that nothing folds); out: device memory of
- * workgroups * 512 floats, overwritten with one value per thread. attn_calibrate_ops
- * gives the operations (FLOPs for kind 0, exponentials for kind 1) of one workgroup, so
- * that rate = ops * workgroups / elapsed time. kind outside {0, 1}, workgroups or iters
- * < 1, or a NULL pointer is ATTN_ERR_INVALID_ARG (attn_calibrate_ops returns -1). */
+ * threads (the attention kernels' launch shape) for `iters` iterations. Kinds 2-5 price
+ * the work the attention kernels put between their MFMAs: after every MFMA one fp32 FMA,
+ * one exponential and one add (independent of the MFMAs), and a 16-byte LDS read feeding
+ * the next MFMA after every MFMA (2), after every second MFMA (3), after every second
+ * MFMA with one wave per SIMD instead of two (4: workgroups of 256 threads), or no LDS
+ * read (5). seed: device memory of 4 uint32 values (operands, so that nothing folds);
+ * out: device memory of workgroups * 512 floats, overwritten with one value per thread.
+ * attn_calibrate_ops gives the operations (FLOPs, or exponentials for kind 1) of one
+ * workgroup, so that rate = ops * workgroups / elapsed time. kind outside [0, 5],
+ * workgroups or iters < 1, or a NULL pointer is ATTN_ERR_INVALID_ARG (attn_calibrate_ops
+ * returns -1). */
 attn_status_t attn_calibrate(int kind, const uint32_t* seed, float* out, int64_t workgroups, int iters,
                              void* stream);
 int64_t attn_calibrate_ops(int kind, int iters);
