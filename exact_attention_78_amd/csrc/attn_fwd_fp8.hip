@@ -58,9 +58,20 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
 }
 
 // 16-byte chunk c (of D/16 per row of D bytes) of tile row r lives at chunk c ^ swz(r); K
-// and V tiles use the same swizzle. It depends on row bits 1..3 (d = 128) or 1..2 (d = 64).
+// and V tiles use the same swizzle, a function of row bits 1..3 only (row offsets that are
+// multiples of 16 keep it). d = 128: two 128-byte rows share a 256-byte line of the 64
+// LDS banks, so a 16-byte bank group is (r & 1) * 8 + (c ^ swz(r)) (mod 16). The K reads
+// (one 16-byte chunk per lane from 16 consecutive rows) need swz to take 8 distinct values
+// on the even rows and on the odd rows of 16; the V^T transpose reads (32 lanes: rows
+// {0,1,2,3,8,9,10,11} + 4h, chunks c and c^1) need swz >> 1 to differ between the rows
+// {0,2,8,10} (and {1,3,9,11}, {4,6,12,14}, {5,7,13,15}). Swapping bit 1 of the row to the
+// top does both: swz = 4 * r[1] + r[3:2]. (Using r[3:1] directly put rows 0 and 2, 8 and
+// 10 on one bank group for the V^T reads: 2-way conflicts, 33% of LDS cycles.)
 template <int D>
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & (D / 16 - 1); }
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  return (r >> 1) & (D / 16 - 1);
+}
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
 
