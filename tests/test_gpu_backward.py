@@ -12,7 +12,15 @@ for fp16) before fp32 accumulation, and the result is rounded once more; with th
 forward's O gate (2e-2 absolute on values of order one) as the model, the bound here is
 max|dX - dX_ref| <= 2e-2 * max(1, max|dX_ref|) per gradient tensor, the same budget
 scaled by the gradient's magnitude (which grows with the number of rows that attend to
-a key). The test prints the measured errors, which sit well inside it.
+a key), and, for dV row by row (a key's row), the same budget scaled by that row's
+largest gradient with a floor of 0.1, so that keys with small gradients are held to
+their own scale rather than the tensor's largest. dQ and dK keep the per-tensor bound
+only: both are products with dS = P * (dP - rowsum(P * dP)), which cancels on query rows
+whose probability sits on a few keys (causal row 0: exactly), so their rows can be far
+smaller than the terms they sum and carry errors of those terms' size (measured against
+a per-row bound: dQ up to 2.5x on causal rows and 64x with keys scaled x8, dK up to
+5.7x with keys scaled x8). dV = P^T dO has no such difference inside it. The test prints
+the measured errors and, for every gradient, the worst row's share of its per-row bound.
 """
 
 import sys
@@ -27,6 +35,7 @@ from oracle.attention import attention_backward
 pytestmark = pytest.mark.gpu
 
 G_TOL = 2e-2
+ROW_FLOOR = 0.1                  # per-row bound: 2e-2 * max(0.1, max over the row of |dX_ref|)
 
 FWD = {"bf16": attn_fwd_bf16, "f16": attn_fwd_f16}
 BWD = {"bf16": attn_bwd_bf16, "f16": attn_bwd_f16}
@@ -61,10 +70,17 @@ def compare(got, ref, label, heads=None):
             idx = tuple(np.array(heads).T)
             x, r = x[idx], r[idx]
         assert np.isfinite(x).all(), name
-        e = np.abs(x - r).max()
+        err = np.abs(x - r)
+        e = err.max()
         bound = G_TOL * max(1.0, np.abs(r).max())
-        errs.append(f"{name} {e:.2e} (bound {bound:.2e})")
+        # per row (a query row of dQ, a key row of dK and dV): the same budget scaled by
+        # that row's largest gradient, with a floor of 0.1
+        row_bound = G_TOL * np.maximum(ROW_FLOOR, np.abs(r).max(axis=-1, keepdims=True))
+        ratio = (err / row_bound).max()
+        errs.append(f"{name} {e:.2e} (bound {bound:.2e}; worst row at {ratio:.2f} of its bound)")
         assert e <= bound, (name, e, bound)
+        if name == "dV":
+            assert ratio <= 1.0, (name, ratio)
     say(f"  {label}: " + ", ".join(errs))
 
 
