@@ -81,15 +81,25 @@ def read_counters(key="hbm_bytes_per_launch"):
 
 
 def time_launches(torch, fn, steps, warmup, reps=1, between=None):
-    """Run fn() `warmup` times untimed, then `steps` timed launches (each a group of `reps`
-    back-to-back calls) with one HIP event pair per launch on the current stream (the
-    stream the library launches on). `between`, if given, runs untimed before each timed
-    launch (e.g. a cache flush). Returns per-call milliseconds: mean over the whole timed
-    region, and median / min / std over the launches."""
+    """Run fn() `warmup` times untimed, then time `steps` launches (each a group of `reps`
+    back-to-back calls) with HIP events on the current stream (the stream the library
+    launches on). `between`, if given, runs untimed before each timed launch (e.g. a cache
+    flush; every launch then has its own event pair). Returns per-call milliseconds: the
+    mean over the timed calls, and median / min / std over the launches."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     if between is None:
+        # the mean from one event pair around all calls (an event recorded between two
+        # calls adds a gap of a few microseconds); then the same number of launches again,
+        # one pair each, for the spread
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps * reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        total = e0.elapsed_time(e1) / (steps * reps)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         ev[0].record()
         for i in range(steps):
@@ -98,7 +108,6 @@ def time_launches(torch, fn, steps, warmup, reps=1, between=None):
             ev[i + 1].record()
         torch.cuda.synchronize()
         per = [ev[i].elapsed_time(ev[i + 1]) / reps for i in range(steps)]
-        total = ev[0].elapsed_time(ev[steps]) / (steps * reps)
     else:
         per = []
         for _ in range(steps):
@@ -411,12 +420,23 @@ def main():
         extra["forward"] = forward_legs(torch, ea, inputs, w, gq, gk, gv, o, lse, legs_steps, legs_warm,
                                         extra["calibration"])
 
-    # the headline: W untimed steps, then exactly K timed steps, one event pair per launch
+    # the headline: W untimed steps, then exactly K timed steps between one pair of HIP
+    # events (events recorded between the calls would add a gap of several microseconds
+    # to each); then K more calls, each between its own pair of events, for the per-call
+    # median, min and std
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
-    t = time_launches(torch, step, args.steps, args.warmup)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
     torch.cuda.synchronize()
-    ms = t["mean_ms"]
+    ms = e0.elapsed_time(e1) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
+    t = time_launches(torch, step, args.steps, 0)
+    t["mean_ms"] = ms
 
     out = {
         "metric": "attention fwd TFLOP/s (bf16, causal, d=128, N=8k) and % of MFMA peak",
@@ -434,7 +454,8 @@ def main():
         "config": {"workload": "bf16 causal attention forward, B=2 H=16 N=8192 d=128", "B": w.B, "H": w.H,
                    "N": w.N, "d": w.d, "causal": True, "flop_per_step": flops},
         "pct_of_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
-        "launch_us": us(t),
+        "launch_us": {**us(t), "what": "mean: the K timed calls (one event pair around them); median, min, std: "
+                                        "K more calls, one event pair each (the pairs add a few microseconds per call)"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": read_counters()},
     }
