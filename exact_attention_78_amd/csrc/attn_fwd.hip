@@ -201,7 +201,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
     // Running max M (log2 units; raised only when a tile's max exceeds it by more than
     // kTau, so that probabilities stay below 2^kTau), this lane's partial row sum of the
-    // rounded probabilities, and a pending O rescale factor.
+    // fp32 probabilities (before their rounding to 16 bits), and a pending O rescale factor.
     float M = -INFINITY, l_part = 0.f, alpha_pend = 1.f;
     // Scores of tile u that lie above the diagonal or past the end of the sequence -> -inf.
     auto mask_tile = [&](int u, f32x16 (&S)[NKB]) __attribute__((always_inline)) {
