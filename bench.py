@@ -360,7 +360,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-extra", action="store_true", help="headline only: skip every other leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--only", choices=["fp8", "backward", "decode"],
+    ap.add_argument("--only", choices=["calibration", "fp8", "backward", "decode"],
                     help="run only this leg (for profiler runs) and print its JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 1 GiB x 4 (HBM counter calibration) and exit")
@@ -386,6 +386,9 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": 2 * (1 << 30), "launches": 4}))
         return
 
+    if args.only == "calibration":
+        print(json.dumps({"calibration": calibration_leg(torch, ea)}))
+        return
     if args.only in ("fp8", "decode"):
         fn = fp8_leg if args.only == "fp8" else decode_leg
         print(json.dumps({args.only: fn(torch, ea, inputs, args.steps, args.warmup)}))
