@@ -30,6 +30,8 @@
 // Causal: query tiles of dq stop at the diagonal and key tiles of dkdv start at it;
 // waves skip blocks that are wholly masked for them, and only blocks crossing the
 // diagonal or the end of the sequence apply a mask.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "tile_lds.h"
@@ -119,37 +121,38 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
   auto kbuf = [&](int slot) __attribute__((always_inline)) { return lds + slot * TB; };
   auto vbuf = [&](int slot) __attribute__((always_inline)) { return lds + (2 + slot) * TB; };
 
-  load_rows<D, kBN, W>(Kh, 0, N, kbuf(0), wave, lane);
-  load_rows<D, kBN, W>(Vh, 0, N, vbuf(0), wave, lane);
-  wait_vmcnt<0>();
-  barrier_lds();
-  for (int t = 0; t < T; ++t) {
-    const int slot = t & 1;
+  // Step t: prefetch K/V tile t + 1 into the other slot, process tile t from slot SLOT
+  // (compile-time, so every LDS read takes an immediate offset), then wait for the
+  // prefetch. Only tiles crossing the diagonal or the end of the sequence mask scores,
+  // in one block of their own ahead of the exponentials.
+  auto step = [&](auto slot_c, int t) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_c)::value;
     if (t + 1 < T) {
-      load_rows<D, kBN, W>(Kh, (t + 1) * kBN, N, kbuf(slot ^ 1), wave, lane);
-      load_rows<D, kBN, W>(Vh, (t + 1) * kBN, N, vbuf(slot ^ 1), wave, lane);
+      load_rows<D, kBN, W>(Kh, (t + 1) * kBN, N, kbuf(SLOT ^ 1), wave, lane);
+      load_rows<D, kBN, W>(Vh, (t + 1) * kBN, N, vbuf(SLOT ^ 1), wave, lane);
     }
     if (!CAUSAL || t * kBN <= q0 + 31) {            // else: every key of the tile lies past this wave's rows
-      const uint8_t* kt = kbuf(slot);
-      const uint8_t* vt = vbuf(slot);
+      const uint8_t* kt = kbuf(SLOT);
+      const uint8_t* vt = vbuf(SLOT);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        const int key0 = t * kBN + kb * 32;
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) s = mfma32(Tag{}, row_frag<D>(kt, ta, kb * 32, st), qreg[st], s);
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) dp = mfma32(Tag{}, row_frag<D>(vt, ta, kb * 32, st), doreg[st], dp);
-        const int key0 = t * kBN + kb * 32;
-        const bool edge = (CAUSAL && key0 + 31 > q0) || key0 + 32 > N;
+        if ((CAUSAL && key0 + 31 > q0) || key0 + 32 > N) {
+          // keys past this lane's row (causal) or past the sequence
+          const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - key0 - half * 4;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((r / 4) * 8 + (r % 4) > lim) s[r] = -INFINITY;
+        }
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = s[r];
-          if (edge) {
-            const int key = key0 + (r / 4) * 8 + half * 4 + (r % 4);
-            if ((CAUSAL && key > qrow) || key >= N) x = -INFINITY;
-          }
-          const float p = fast_exp2(__builtin_fmaf(x, c, -lse2));
+          const float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
           ds[r] = p * (dp[r] - delta);
         }
         u32x4 pb[2];
@@ -157,11 +160,21 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(Tag{}, tr_frag<D>(kt, ta, kb * 32 + h * 16, db), pb[h], acc[db]);
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = mfma32(Tag{}, tr_frag<D>(kt, ta, kb * 32 + h * 16, db), pb[h], acc[db]);
       }
     }
     wait_vmcnt<0>();
     barrier_lds();
+  };
+
+  load_rows<D, kBN, W>(Kh, 0, N, kbuf(0), wave, lane);
+  load_rows<D, kBN, W>(Vh, 0, N, vbuf(0), wave, lane);
+  wait_vmcnt<0>();
+  barrier_lds();
+  for (int t = 0; t < T; t += 2) {
+    step(IC<0>{}, t);
+    if (t + 1 < T) step(IC<1>{}, t + 1);
   }
   if (qrow < N) store_rows<Tag, D>(dQ + head_off + (int64_t)qrow * D, acc, half, scale);
 }
@@ -222,26 +235,23 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
   };
   static_assert(2 * kBQ <= W * 64, "one thread per fetched value");
 
-  load_rows<D, BNK, W>(K + head_off, nt * BNK, N, kt, wave, lane);
-  load_rows<D, BNK, W>(V + head_off, nt * BNK, N, vt, wave, lane);
-  load_rows<D, kBQ, W>(Qh, u0 * kBQ, N, qbuf(0), wave, lane);      // u0 < n_qtiles: the tile's first key is < N
-  load_rows<D, kBQ, W>(dOh, u0 * kBQ, N, gbuf(0), wave, lane);
-  if (tid < 2 * kBQ) lsd[0][tid / kBQ][tid % kBQ] = fetch_ld(u0);
-  wait_vmcnt<0>();
-  barrier_lds();
-  for (int u = u0; u < n_qtiles; ++u) {
-    const int slot = (u - u0) & 1;
+  const int qr = qh * 32;                           // this wave's 32 queries start at row qr of each tile
+  // Step u: prefetch Q/dO tile u + 1 (and its LSE / Delta) into the other slot, process
+  // tile u from slot SLOT (compile-time, so the tile reads take immediate offsets), then
+  // wait for the prefetch. Only blocks crossing the diagonal or the end of the sequence
+  // mask scores, in one block of their own ahead of the exponentials.
+  auto step = [&](auto slot_c, int u) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_c)::value;
     float pf = 0.f;
     if (u + 1 < n_qtiles) {
-      load_rows<D, kBQ, W>(Qh, (u + 1) * kBQ, N, qbuf(slot ^ 1), wave, lane);
-      load_rows<D, kBQ, W>(dOh, (u + 1) * kBQ, N, gbuf(slot ^ 1), wave, lane);
+      load_rows<D, kBQ, W>(Qh, (u + 1) * kBQ, N, qbuf(SLOT ^ 1), wave, lane);
+      load_rows<D, kBQ, W>(dOh, (u + 1) * kBQ, N, gbuf(SLOT ^ 1), wave, lane);
       if (tid < 2 * kBQ) pf = fetch_ld(u + 1);
     }
-    const int qr = qh * 32;                         // this wave's 32 queries start at row qr of the tile
     const int qb0 = u * kBQ + qr;
     if (!CAUSAL || qb0 + 31 >= k0) {                // else: every query of the block precedes this wave's keys
-      const uint8_t* qt = qbuf(slot);
-      const uint8_t* gt = gbuf(slot);
+      const uint8_t* qt = qbuf(SLOT);
+      const uint8_t* gt = gbuf(SLOT);
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st)
@@ -249,22 +259,26 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
       for (int st = 0; st < NSTEP; ++st)
         dp = mfma32(Tag{}, row_frag<D>(gt, ta, qr, st), row_frag<D>(vt, ta, kg * 32, st), dp);
-      const bool edge = (CAUSAL && qb0 < k0 + 31) || qb0 + 32 > N;
+      if ((CAUSAL && qb0 < k0 + 31) || qb0 + 32 > N) {
+        // queries before this lane's key (causal) or past the sequence: element r is
+        // query qb0 + 8 * (r / 4) + 4 * half + r % 4
+        const int lo = (CAUSAL ? krow : 0) - qb0 - half * 4, hi = N - 1 - qb0 - half * 4;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o = (r / 4) * 8 + (r % 4);
+          if (o < lo || o > hi) s[r] = -INFINITY;
+        }
+      }
       float p[16], ds[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qi = qr + g * 8 + half * 4;       // this lane's queries qi .. qi + 3 of the tile
-        const f32x4 l4 = *(const f32x4*)&lsd[slot][0][qi];
-        const f32x4 d4 = *(const f32x4*)&lsd[slot][1][qi];
+        const f32x4 l4 = *(const f32x4*)&lsd[SLOT][0][qi];
+        const f32x4 d4 = *(const f32x4*)&lsd[SLOT][1][qi];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = g * 4 + e;
-          float x = s[r];
-          if (edge) {
-            const int q = u * kBQ + qi + e;
-            if ((CAUSAL && q < krow) || q >= N) x = -INFINITY;
-          }
-          p[r] = fast_exp2(__builtin_fmaf(x, c, -l4[e]));
+          p[r] = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
           ds[r] = p[r] * (dp[r] - d4[e]);
         }
       }
@@ -279,9 +293,21 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
           acck[db] = mfma32(Tag{}, tr_frag<D>(qt, ta, qr + h * 16, db), sb[h], acck[db]);
         }
     }
-    if (u + 1 < n_qtiles && tid < 2 * kBQ) lsd[slot ^ 1][tid / kBQ][tid % kBQ] = pf;
+    if (u + 1 < n_qtiles && tid < 2 * kBQ) lsd[SLOT ^ 1][tid / kBQ][tid % kBQ] = pf;
     wait_vmcnt<0>();
     barrier_lds();
+  };
+
+  load_rows<D, BNK, W>(K + head_off, nt * BNK, N, kt, wave, lane);
+  load_rows<D, BNK, W>(V + head_off, nt * BNK, N, vt, wave, lane);
+  load_rows<D, kBQ, W>(Qh, u0 * kBQ, N, qbuf(0), wave, lane);      // u0 < n_qtiles: the tile's first key is < N
+  load_rows<D, kBQ, W>(dOh, u0 * kBQ, N, gbuf(0), wave, lane);
+  if (tid < 2 * kBQ) lsd[0][tid / kBQ][tid % kBQ] = fetch_ld(u0);
+  wait_vmcnt<0>();
+  barrier_lds();
+  for (int u = u0; u < n_qtiles; u += 2) {
+    step(IC<0>{}, u);
+    if (u + 1 < n_qtiles) step(IC<1>{}, u + 1);
   }
   // The two query halves of a key group hold partial sums of the same dK and dV rows.
   // Half 1 hands over its dK part and half 0 its dV part through LDS (the tiles are no
