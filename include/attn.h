@@ -213,10 +213,10 @@ attn_status_t attn_bwd_f16(const void* q, const void* k, const void* v, const vo
  * query rows, k and v [B, H, Nk, d], no mask (every query row sees all Nk keys), in bf16;
  * writes O bf16 [B, H, Nq, d] and LSE fp32 [B, H, Nq] with the same definitions as
  * attn_fwd_bf16. The FlashAttention-2 digest (discussion points) asks whether decoding
- * needs its own kernel; here the keys are split into chunks, each chunk's partial O and
- * LSE go to `workspace` (caller-owned device memory of attn_decode_workspace_floats(...)
- * fp32 values, overwritten, nothing of use afterwards), and a second kernel merges them
- * through the LSEs. Two kernels are enqueued on `stream`. Nq outside [1, 32] is
+ * needs its own kernel; here each head's keys are split (split s of n takes the 32-key
+ * tiles s, s + n, ...), each split's partial O and LSE go to `workspace` (caller-owned
+ * device memory of attn_decode_workspace_floats(...) fp32 values, overwritten, nothing of
+ * use afterwards), and a second kernel merges them through the LSEs. Two kernels are enqueued on `stream`. Nq outside [1, 32] is
  * ATTN_ERR_INVALID_ARG; d as for the other entry points. */
 attn_status_t attn_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
                                int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
@@ -229,12 +229,12 @@ attn_status_t attn_decode_f16(const void* q, const void* k, const void* v, void*
 
 /* attn_decode_bf16 for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and
- * results, with the per-chunk partials in a static device array of the library (64 MiB,
+ * results, with the per-split partials in a static device array of the library (64 MiB,
  * 2^24 floats, per GPU, held until the process ends) instead of a caller workspace. The
  * call allocates and frees nothing; the first call on a device looks up that device's
  * copy of the array. Sizes whose attn_decode_workspace_floats(...) exceeds 2^24 return
  * ATTN_ERR_SCRATCH_TOO_SMALL before anything is enqueued (at Nq = 32, d = 128 that is up
- * to 4064 (head, key chunk) pairs: any B*H <= 2016 at any Nk). Every call on one GPU shares that GPU's
+ * to 4064 (head, key split) pairs: any B*H <= 2016 at any Nk). Every call on one GPU shares that GPU's
  * array: calls that overlap in time on one GPU (two streams, two threads) race and give
  * undefined results; calls enqueued on one stream do not overlap. */
 attn_status_t attn_decode_bf16_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
