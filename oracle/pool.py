@@ -2,8 +2,10 @@
 
 This module holds no arithmetic of its own. Heads and query rows of exact attention are
 independent (each output row depends only on its own query row and the head's K and V),
-so a call is split into units of (b, h, chunk of query rows) and every unit is handed,
-unchanged, to ``attention.attention_forward`` on a worker thread. NumPy releases the
+so a forward call is split into units of (b, h, chunk of query rows) and every unit is
+handed, unchanged, to ``attention.attention_forward`` on a worker thread; a backward call
+(whose dK and dV sum over all query rows of a head) into units of one head, each handed
+to ``attention.attention_backward``. NumPy releases the
 interpreter lock inside its array kernels, so the units run in parallel; each worker
 keeps BLAS to one thread so that the workers do not oversubscribe the cores.
 """
@@ -15,7 +17,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .attention import _as_f64, attention_forward
+from .attention import _as_f64, attention_backward, attention_forward
 
 
 def host_cores() -> int:
@@ -52,3 +54,28 @@ def forward_pooled(q, k, v, causal: bool, scale: float, rows=None, heads=None, w
     with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers or host_cores()) as ex:
         list(ex.map(run, units))
     return O, LSE
+
+
+def backward_pooled(q, k, v, dout, causal: bool, scale: float, heads=None, workers=None, row_chunk: int = 1024):
+    """``attention_backward`` with the same arguments and result, one head per unit on
+    ``workers`` threads (default: every core of the affinity set).
+
+    Returns (dQ, dK, dV) exactly as ``attention_backward`` would: fp64 [B, H, N, d], NaN
+    for heads not requested.
+    """
+    from threadpoolctl import threadpool_limits
+
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    heads = [(b, h) for b in range(q.shape[0]) for h in range(q.shape[1])] if heads is None else list(heads)
+    out = [np.full(q.shape, np.nan) for _ in range(3)]
+
+    def run(unit):
+        b, h = unit
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        grads = attention_backward(q[sl], k[sl], v[sl], dout[sl], causal, scale, row_chunk=row_chunk)
+        for o, g in zip(out, grads):
+            o[b, h] = g[0, 0]
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers or host_cores()) as ex:
+        list(ex.map(run, heads))
+    return tuple(out)

@@ -31,6 +31,7 @@ import torch
 
 from exact_attention_78_amd import attn_bwd_bf16, attn_bwd_f16, attn_fwd_bf16, attn_fwd_f16, bwd, inputs
 from oracle.attention import attention_backward
+from oracle.pool import backward_pooled
 
 pytestmark = pytest.mark.gpu
 
@@ -108,19 +109,16 @@ def test_large_scores(causal):
     compare(got, ref, f"x8 keys causal={causal}")
 
 
-@pytest.mark.parametrize("name", ["C3", "H"])
-def test_full_size_sampled_heads(name):
-    # full-size launch (every head computed on the device); the oracle differentiates
-    # two heads completely
+@pytest.mark.parametrize("name,causal", [("H", True), ("C3", True), ("C3", False)])
+def test_full_size_every_head(name, causal):
+    # full-size launch, every head of every gradient against the oracle (one head per
+    # worker thread on the host's cores)
     w = inputs.WORKLOADS[name]
-    say(f"case bwd full size {name} B{w.B} H{w.H} N{w.N} d{w.d} causal")
+    say(f"case bwd full size {name} B{w.B} H{w.H} N{w.N} d{w.d} causal={causal}")
     cpu = make(w.wid, w.B, w.H, w.N, w.d, "bf16")
-    got = run_device(cpu, "bf16", True)
-    heads = [(0, 0), (w.B - 1, w.H - 1)]
-    ref = attention_backward(*cpu, True, w.scale, heads=heads, row_chunk=1024)
-    compare(got, ref, f"{name} sampled heads", heads=heads)
-    for x in got:
-        assert np.isfinite(x).all()
+    got = run_device(cpu, "bf16", causal)
+    ref = backward_pooled(*cpu, causal, w.scale)
+    compare(got, ref, f"{name} every head causal={causal}")
 
 
 def test_dispatch_stream_and_determinism():

@@ -7,8 +7,8 @@ import numpy as np
 import pytest
 
 from exact_attention_78_amd.flops import counted_flops, counted_flops_backward
-from oracle.attention import attention_forward
-from oracle.pool import forward_pooled, host_cores
+from oracle.attention import attention_backward, attention_forward
+from oracle.pool import backward_pooled, forward_pooled, host_cores
 
 
 def _terms(N, d, causal):
@@ -59,3 +59,19 @@ def test_pooled_oracle_matches_the_oracle(causal):
 
 
 
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_pooled_backward_matches_the_oracle(causal):
+    # one head per unit: the same gradients in the same places, NaN for heads left out
+    rng = np.random.default_rng(5)
+    B, H, N, d = 2, 2, 50, 8
+    q, k, v, g = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    ref = attention_backward(q, k, v, g, causal, 0.3, row_chunk=7)
+    got = backward_pooled(q, k, v, g, causal, 0.3, workers=3, row_chunk=7)
+    for x, r in zip(got, ref):
+        np.testing.assert_allclose(x, r, rtol=0, atol=1e-13)
+    part = backward_pooled(q, k, v, g, causal, 0.3, heads=[(1, 0)], workers=2)
+    for x, r in zip(part, ref):
+        np.testing.assert_allclose(x[1, 0], r[1, 0], rtol=0, atol=1e-12)
+        assert np.isnan(x[0]).all() and np.isnan(x[1, 1]).all()
