@@ -138,7 +138,8 @@ def rate(work, t, scale=1e12):
 
 def calibration_leg(torch, ea):
     """Dense MFMA and exp2 loops (one 8-wave workgroup per CU, the attention kernels'
-    launch shape), and an 8192^3 bf16 GEMM through torch.matmul (hipBLASLt)."""
+    launch shape), an 8192^3 bf16 GEMM through torch.matmul (hipBLASLt), and a streaming
+    read loop over 1 GiB."""
     res = {}
     wg = torch.cuda.get_device_properties(0).multi_processor_count
     for kind, iters, unit, scale in (("mfma", 4000, "TFLOP/s", 1e12), ("exp", 8000, "Gexp/s", 1e9)):
@@ -166,6 +167,15 @@ def calibration_leg(torch, ea):
                              "frac_of_published_peak": rate(2.0 * n ** 3, t) / PEAK_BF16_TFLOPS,
                              "library": "torch.matmul (hipBLASLt)"}
     del a, b, c
+    # what streaming reads attain (the HBM-bound kernels' attainable rate beside the
+    # published 8 TB/s): the read loop sweeping 1 GiB once, 2048 workgroups of 256 threads
+    wgr, itr = 2048, 128
+    buf = torch.zeros(wgr * 256 * itr * 4, dtype=torch.int32, device="cuda")
+    out, nbytes = ea.attn_calibrate("read", wgr, itr, seed=buf)
+    t = time_launches(torch, lambda: ea.attn_calibrate("read", wgr, itr, seed=buf, out=out), 10, 5)
+    res["read_loop"] = {"value": rate(nbytes, t, 1e9), "unit": "GB/s", "us": t["mean_ms"] * 1e3, "bytes": nbytes,
+                        "frac_of_published_hbm": rate(nbytes, t, 1e9) / PEAK_HBM_GBS}
+    del buf, out
     return res
 
 
@@ -420,6 +430,7 @@ def main():
         extra["backward"] = backward_leg(torch, ea, inputs, w, (gq, gk, gv), o, lse, legs_steps, legs_warm)
         extra["fp8"] = fp8_leg(torch, ea, inputs, legs_steps, legs_warm)
         extra["decode"] = decode_leg(torch, ea, inputs, legs_steps, 4 * legs_warm)
+        extra["decode"]["frac_of_read_loop"] = extra["decode"]["gbs"] / extra["calibration"]["read_loop"]["value"]
         extra["forward"] = forward_legs(torch, ea, inputs, w, gq, gk, gv, o, lse, legs_steps, legs_warm,
                                         extra["calibration"])
 

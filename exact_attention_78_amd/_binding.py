@@ -171,16 +171,22 @@ def attn_fwd_variant(q, k, v, causal=False, scale=None, sched="default", passes=
 # attn_calibrate kinds (see attn.h): the dense loops, and MFMA loops with the kernels' mix
 # of work between MFMAs (one fma, exp and add each; LDS reads per MFMA; waves per SIMD)
 CALIBRATION_KINDS = {"mfma": 0, "exp": 1, "mix_lds1_2w": 2, "mix_lds0.5_2w": 3, "mix_lds0.5_1w": 4,
-                     "mix_nolds_2w": 5}
+                     "mix_nolds_2w": 5, "read": 6}
 
 
 def attn_calibrate(kind, workgroups, iters, seed=None, out=None):
-    """Launch a calibration loop (kind "mfma" or "exp") on the current stream; returns the
-    output tensor and the operations it performs (FLOPs or exponentials)."""
+    """Launch a calibration loop (a key of CALIBRATION_KINDS) on the current stream; returns
+    the output tensor and the operations it performs (FLOPs, exponentials for "exp", bytes
+    read for "read"). For "read", ``seed`` is the buffer the loop streams through
+    (workgroups * 256 * iters 16-byte elements; zeros of that size by default)."""
     k = CALIBRATION_KINDS[kind]
     dev = torch.device("cuda", torch.cuda.current_device())
-    seed = torch.tensor([0x3F803F80, 0x3F003F00, 0x3F403F40, 0x3E803E80], dtype=torch.int64).to(torch.int32).to(dev) \
-        if seed is None else seed
+    if seed is None:
+        seed = torch.zeros(workgroups * 256 * iters * 4, dtype=torch.int32, device=dev) if kind == "read" else \
+            torch.tensor([0x3F803F80, 0x3F003F00, 0x3F403F40, 0x3E803E80], dtype=torch.int64).to(torch.int32).to(dev)
+    need = workgroups * 256 * iters * 16 if kind == "read" else 16
+    _require(seed.is_cuda and seed.is_contiguous() and seed.numel() * seed.element_size() >= need,
+             f"seed: a contiguous GPU buffer of at least {need} bytes")
     out = torch.empty(workgroups * 512, dtype=torch.float32, device=dev) if out is None else out
     _require(out.numel() >= workgroups * 512 and out.dtype == torch.float32, "out: workgroups * 512 fp32 values")
     st = library().attn_calibrate(k, seed.data_ptr(), out.data_ptr(), workgroups, iters,

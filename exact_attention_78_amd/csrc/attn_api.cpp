@@ -336,14 +336,17 @@ attn_status_t attn_decode_f16(const void* q, const void* k, const void* v, void*
 
 attn_status_t attn_calibrate(int kind, const uint32_t* seed, float* out, int64_t workgroups, int iters,
                              void* stream) {
-  if (kind < 0 || kind > 5 || !seed || !out || workgroups < 1 || workgroups > INT32_MAX || iters < 1)
+  if (kind < 0 || kind > 6 || !seed || !out || workgroups < 1 || workgroups > INT32_MAX || iters < 1)
     return ATTN_ERR_INVALID_ARG;
+  // kind 6 reads workgroups * 256 * iters 16-byte elements from seed: the count must fit
+  // the kernel's int64 indexing
+  if (kind == 6 && workgroups * 256 > INT64_MAX / 16 / iters) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(seed) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
   return from_hip(attn::launch_calib(kind, seed, out, workgroups, iters, (hipStream_t)stream));
 }
 
 int64_t attn_calibrate_ops(int kind, int iters) {
-  if (kind < 0 || kind > 5 || iters < 1) return -1;
+  if (kind < 0 || kind > 6 || iters < 1) return -1;
   return attn::calib_ops_per_workgroup(kind, iters);
 }
 

@@ -1,5 +1,6 @@
-// Calibration kernels: what the matrix cores and the transcendental unit of this part
-// sustain when nothing else competes, at the clock the chip runs under that load.
+// Calibration kernels: what the matrix cores, the transcendental unit and the memory
+// system of this part sustain when nothing else competes, at the clock the chip runs
+// under that load.
 //
 // The forward kernels are judged against the published dense MFMA peak (256 CUs x
 // 2.4 GHz x 4096 bf16 FLOP per clock); under full MFMA load the engine clock drops below
@@ -105,6 +106,24 @@ __global__ __launch_bounds__(WV * 64, 1) void calib_mix_kernel(const uint32_t* _
   out[(int64_t)blockIdx.x * 512 + threadIdx.x] = sum;
 }
 
+// Streaming reads (kind 6): what the memory system delivers to a kernel that only reads,
+// the attainable rate of the HBM-bound kernels beside the published 8 TB/s. Each of the
+// grid's threads loads one 16-byte element per iteration; iteration i of the grid covers
+// the consecutive elements [i * G, (i + 1) * G) (G = threads of the grid), so the whole
+// grid sweeps the buffer once, front to back.
+constexpr int kReadThreads = 256;
+__global__ __launch_bounds__(kReadThreads) void calib_read_kernel(const u32x4* __restrict__ src, float* out,
+                                                                   int iters) {
+  const int64_t stride = (int64_t)gridDim.x * kReadThreads;
+  int64_t i = (int64_t)blockIdx.x * kReadThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; ++it, i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  out[(int64_t)blockIdx.x * kReadThreads + threadIdx.x] = (float)acc;
+}
+
 // kinds 2..5 of attn_calibrate: the mixes above
 struct Mix {
   int waves;
@@ -122,7 +141,10 @@ hipError_t launch_calib(int kind, const uint32_t* seed, float* out, int64_t work
     case 2: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 16, 8>), grid, dim3(8 * 64), 0, stream, seed, out, iters); break;
     case 3: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 8, 8>), grid, dim3(8 * 64), 0, stream, seed, out, iters); break;
     case 4: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 8, 4>), grid, dim3(4 * 64), 0, stream, seed, out, iters); break;
-    default: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 0, 8>), grid, dim3(8 * 64), 0, stream, seed, out, iters); break;
+    case 5: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 0, 8>), grid, dim3(8 * 64), 0, stream, seed, out, iters); break;
+    default:
+      hipLaunchKernelGGL(calib_read_kernel, grid, dim3(kReadThreads), 0, stream, (const u32x4*)seed, out, iters);
+      break;
   }
   return hipGetLastError();
 }
@@ -131,6 +153,7 @@ int64_t calib_ops_per_workgroup(int kind, int iters) {
   // MFMA kinds: FLOPs; exp: exponentials
   if (kind == 0) return (int64_t)kCalWaves * iters * kChains * 32768;
   if (kind == 1) return (int64_t)kCalWaves * 64 * iters * 16;
+  if (kind == 6) return (int64_t)kReadThreads * iters * 16;   // bytes read
   return (int64_t)kMix[kind - 2].waves * iters * 16 * 32768;
 }
 

@@ -256,10 +256,13 @@ int64_t attn_decode_workspace_floats(int64_t B, int64_t H, int64_t Nq, int64_t N
  * MFMA with one wave per SIMD instead of two (4: workgroups of 256 threads), or no LDS
  * read (5). seed: device memory of 4 uint32 values (operands, so that nothing folds);
  * out: device memory of workgroups * 512 floats, overwritten with one value per thread.
- * attn_calibrate_ops gives the operations (FLOPs, or exponentials for kind 1) of one
- * workgroup, so that rate = ops * workgroups / elapsed time. kind outside [0, 5],
- * workgroups or iters < 1, or a NULL pointer is ATTN_ERR_INVALID_ARG (attn_calibrate_ops
- * returns -1). */
+ * Kind 6 streams reads, the attainable rate of the HBM-bound kernels: workgroups of 256
+ * threads each load one 16-byte element per iteration, the grid sweeping seed once front
+ * to back, so seed must hold workgroups * 256 * iters 16-byte elements (only read); out
+ * gets workgroups * 256 values. attn_calibrate_ops gives the operations (FLOPs,
+ * exponentials for kind 1, bytes read for kind 6) of one workgroup, so that rate = ops *
+ * workgroups / elapsed time. kind outside [0, 6], workgroups or iters < 1, or a NULL
+ * pointer is ATTN_ERR_INVALID_ARG (attn_calibrate_ops returns -1). */
 attn_status_t attn_calibrate(int kind, const uint32_t* seed, float* out, int64_t workgroups, int iters,
                              void* stream);
 int64_t attn_calibrate_ops(int kind, int iters);
