@@ -9,7 +9,8 @@ one batch of seeded synthetic inputs that are already resident in HBM.
 
 Prints ONE JSON line. Besides the headline it reports, from the same run:
   calibration  what a dense MFMA loop and a dense exp2 loop sustain at the loaded clock,
-               and a large bf16 GEMM through torch (hipBLASLt)
+               MFMA loops with the kernels' VALU/LDS work between MFMAs, a large bf16
+               GEMM through torch (hipBLASLt), and a streaming-read loop over 1 GiB
   forward      the headline call's per-launch statistics (median, min, std over the
                timed launches), the exact (running-max) pass alone on the same inputs,
                the same call on inputs whose query tiles all need the exact pass, the

@@ -29,10 +29,10 @@
 //   step's MFMAs, LDS reads and VALU work are written in the order they are issued.
 //   K and V tiles sit in two 4-slot LDS rings (128 KiB at d = 128), filled by direct
 //   global->LDS loads (global_load_lds_dwordx4) two or three steps ahead of their use.
-//   A call of at least ~1e11 FLOPs is two launches of this kernel: a fast pass that keeps
-//   the first tile's row max as the softmax reference for every tile, and an exact pass
-//   that redoes, with a per-tile running max, the query tiles whose probabilities
-//   outgrew that reference. Smaller calls launch the exact pass alone, on every tile.
+//   A call of at least ~1e11 FLOPs runs a fast pass that keeps the first tile's row max
+//   as the softmax reference for every tile; a workgroup whose probabilities outgrew that
+//   reference redoes its query tile at once with the exact pass (a per-tile running
+//   max). Smaller calls run the exact pass alone, on every tile.
 #include <type_traits>
 
 #include "device_common.h"
@@ -47,12 +47,13 @@ constexpr int kKD = 4;         // S^T MFMAs by which a K fragment read runs ahea
 constexpr int kVD = 2;         // P.V MFMAs by which a V fragment read runs ahead
 constexpr int kTail = 1;       // last MFMAs of a step that carry no exponentials (they cover the step's last sums and packing)
 constexpr float kTau = 8.0f;   // lazy-rescale threshold for the running max, in log2 units
-// Two launches per call. The fast pass computes no per-tile row max: every tile uses the
-// max of the first tile, which softmax allows (the result does not depend on the
-// reference value) as long as the probabilities stay representable. A row whose
-// probabilities relative to it reach the guard (a partial row sum above it, or not
-// finite) marks its wave's LSE with NaN; the exact pass then redoes, with a per-tile max,
-// every query tile that carries a mark and leaves the others untouched. The guard, 2^8
+// The fast pass computes no per-tile row max: every tile uses the max of the first tile,
+// which softmax allows (the result does not depend on the reference value) as long as
+// the probabilities stay representable. A row whose probabilities relative to it reach
+// the guard (a partial row sum above it, or not finite) marks its query tile, and the
+// workgroup then redoes that tile with the exact pass, a per-tile max, before it leaves
+// (one launch per call: a second launch over all tiles, most of which would leave at
+// once, cost ~1-4% more, measured). The guard, 2^8
 // on each lane's partial sum of a tile (32 probabilities), keeps every probability of the
 // fast pass within the range the exact pass allows (P <= 2^kTau against its running
 // max), so rounding P to 16 bits costs the fast pass no more accuracy than the exact
@@ -82,7 +83,6 @@ template <typename Tag, int D, bool CAUSAL, int W, bool FAST, bool PERSIST>
 __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_mtiles, int total_wg, float c /* scale*log2 e */,
-    int check_marks /* exact pass: redo marked tiles only (1) or every tile (0) */,
     int order /* TileOrder of a plain grid */, int persist /* PERSIST: 1 fixed stride, 2 queue */,
     int* __restrict__ queue /* persist 2: 8 tile counters, then 8 exit counts */) {
   constexpr int BM = W * 32;                        // query rows per workgroup
@@ -98,12 +98,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   // immediate offset of ds_read (< 64 KiB) with no address add; the K reads need one add
   // per head-dim step.
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];
-  __shared__ int marked;                            // exact pass: this tile carries a mark
+  __shared__ int marked;                            // fast pass: some wave of the tile is marked
   __shared__ int stop[2];                           // fast pass: some wave is marked (by step parity)
 
-  // One query tile (batch*head, m-tile) per workgroup, in both passes; in the exact pass
-  // the workgroups of unmarked tiles leave at once.
-  auto tile = [&](const int bh, const int mt) __attribute__((always_inline)) {
+  // One query tile (batch*head, m-tile), by the fast pass (FASTP) or the exact pass.
+  auto tile = [&](auto fast_c, const int bh, const int mt) __attribute__((always_inline)) {
+    constexpr bool FASTP = decltype(fast_c)::value;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -116,19 +116,11 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
 
     const int q0 = mt * BM + wave * 32;               // this wave's 32 rows; one per lane (and lane^32)
     const int qrow = q0 + l32;
-    if (!FAST && check_marks) {
-      // Exact pass after a fast pass: only query tiles that it marked (a NaN LSE) are redone.
-      if (tid == 0) marked = 0;
-      __syncthreads();
-      const bool mine = half == 0 && qrow < N && __builtin_isnan(LSE[(int64_t)bh * N + qrow]);
-      if (__builtin_amdgcn_ballot_w64(mine) != 0 && lane == 0) marked = 1;
-      __syncthreads();
-      if (marked == 0) return;
-    }
-    if constexpr (FAST) {
+    if constexpr (FASTP) {
       if (tid == 0) {                                   // read only after the prologue's barriers
         stop[0] = 0;
         stop[1] = 0;
+        marked = 0;
       }
     }
     u32x4 qreg[NSTEP];                                // Q^T as the B operand, resident
@@ -280,7 +272,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       // Causal: once the tile's first key lies past this wave's last row, this and every
       // later tile are fully masked for the wave; it only keeps up its loads and barriers.
       if (!CAUSAL || t * kBN <= q0 + 31) {
-        if constexpr (!FAST) {
+        if constexpr (!FASTP) {
           if (pend) rescale_o();
         }
         mask_tile(t + 1, S_soft);
@@ -290,7 +282,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
         // (exact pass) the row max over the first five S^T MFMAs, then the exponentials,
         // one or two per MFMA; (fast pass) the exponentials from the second MFMA on.
         constexpr int NQ = NKB * NSTEP, NP = NDB * NKB * 2, KD = kKD, VD = kVD;
-        constexpr int NMAX = FAST ? 1 : 5;                 // MFMAs before the first exponential
+        constexpr int NMAX = FASTP ? 1 : 5;                 // MFMAs before the first exponential
         constexpr int NSLOT = NQ + NP - NMAX - kTail;      // MFMAs that carry exponentials
         u32x4 kf[NQ], vf[NP];
         auto kread = [&](int i) __attribute__((always_inline)) {   // i = s * NKB + kb
@@ -323,7 +315,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
           if (i < NMAX - 1) {
             max_pairs(m4, S_soft, 4 + i * 8, min(4 + (i + 1) * 8, NKB * 16));
           } else if (i == NMAX - 1) {
-            if constexpr (!FAST) pend = max_final(m4);
+            if constexpr (!FASTP) pend = max_final(m4);
             args(S_soft, lo(0), lo(1));
           } else {
             exps_slot(i - NMAX);
@@ -339,9 +331,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
         if constexpr (kTail == 0) finish(S_soft, P_new, lsum, lo(NSLOT - 1), NKB * 16);
         const float lt = lsum[0] + lsum[1];
         l_part += lt;
-        if constexpr (FAST) ovf |= !(lt <= kGuard);
+        if constexpr (FASTP) ovf |= !(lt <= kGuard);
       }
-      if constexpr (FAST) {
+      if constexpr (FASTP) {
         // a marked wave dooms the whole query tile to the exact pass: say so to the others
         if (__builtin_amdgcn_ballot_w64(ovf) != 0 && lane == 0) stop[t & 1] = 1;
       }
@@ -385,7 +377,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       // was last written in step t+3 (or t+1) before its barrier and is next written in
       // step t+5, after the barrier of step t+4, so every wave reads the same value here
       // and all leave the loop together.
-      if constexpr (FAST) {
+      if constexpr (FASTP) {
         if (stop[1] != 0) t_end = t + 4;
       }
     }
@@ -393,6 +385,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     if (pend) rescale_o();
 
     const float l_tot = add_halves(l_part);
+    if constexpr (FASTP) {
+      if (__builtin_amdgcn_ballot_w64(ovf) != 0 && lane == 0) marked = 1;   // redo the tile exactly
+    }
     if (qrow >= N) return;
     const float inv = 1.0f / l_tot;
     uint16_t* Orow = O + head_off + (int64_t)qrow * D;
@@ -406,11 +401,19 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
                    pack2(Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
         *(u32x2*)(Orow + d) = w;
       }
-    float lse = (M + __builtin_log2f(l_tot)) * kLn2;
-    if constexpr (FAST) {
-      if (__builtin_amdgcn_ballot_w64(ovf) != 0) lse = __builtin_nanf("");   // mark: redo in the exact pass
-    }
+    const float lse = (M + __builtin_log2f(l_tot)) * kLn2;   // (a marked tile's O and LSE are rewritten)
     if (half == 0) LSE[(int64_t)bh * N + qrow] = lse;
+  };
+  // A tile that the fast pass marked is redone at once by the exact pass, in the same
+  // workgroup (after the barrier no wave reads the LDS rings any more).
+  auto run_tile = [&](const int bh, const int mt) __attribute__((always_inline)) {
+    if constexpr (FAST) {
+      tile(std::true_type{}, bh, mt);
+      __syncthreads();
+      if (marked != 0) tile(std::false_type{}, bh, mt);
+    } else {
+      tile(std::false_type{}, bh, mt);
+    }
   };
   // The query tiles of this workgroup. A plain grid has one workgroup per tile, picked by
   // the tile order from the workgroup id. A persistent grid has one workgroup per CU and
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   if constexpr (!PERSIST) {
     int bh, mt;
     query_tile_ordered(order, blockIdx.x, total_wg, n_mtiles, CAUSAL, bh, mt);
-    tile(bh, mt);
+    run_tile(bh, mt);
     return;
   }
   __shared__ int ticket;
@@ -441,7 +444,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     if (wl < 0 || wl >= total_wg) break;   // every workgroup reaches this: the tickets only grow
     int bh, mt;
     query_tile_ordered(kOrderXcdPairs, (int)wl, total_wg, n_mtiles, CAUSAL, bh, mt);
-    tile(bh, mt);
+    run_tile(bh, mt);
   }
   if (persist == 2 && threadIdx.x == 0) {
     // Every workgroup of queue xq has drawn its last (failing) ticket before counting its
@@ -469,8 +472,8 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
   constexpr int BM = W * 32;
   const int n_mtiles = (int)((N + BM - 1) / BM);
   const int64_t total = BH * n_mtiles;
-  // Below ~1e11 counted FLOPs (~0.1 ms of work) the fast pass saves less than the exact
-  // pass's launch costs, so such calls run the exact pass alone, on every tile.
+  // Below ~1e11 counted FLOPs (~0.1 ms of work) the fast pass saves too little to matter,
+  // so such calls run the exact pass alone, on every tile.
   const double flops = 4.0 * (double)BH * (double)N * (double)N * D / (CAUSAL ? 2 : 1);
   const bool two_pass = var.passes == kPassesTwo || (var.passes == kPassesAuto && flops >= kTwoPassFlops);
   const int persist = var.sched >= kSchedPersistentStride ? var.sched - kSchedPersistentStride + 1 : 0;
@@ -479,17 +482,17 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
   auto run = [&](auto FASTC, auto PERSISTC) {
     hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, decltype(FASTC)::value, decltype(PERSISTC)::value>),
                        dim3(grid), dim3(W * 64), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, (uint16_t*)o, lse, (int)N, n_mtiles, (int)total, scale * kLog2e,
-                       decltype(FASTC)::value ? 1 : (two_pass ? 1 : 0), order, persist, var.queue);
+                       (const uint16_t*)v, (uint16_t*)o, lse, (int)N, n_mtiles, (int)total, scale * kLog2e, order,
+                       persist, var.queue);
   };
   using T1 = std::true_type;
   using F0 = std::false_type;
   if (persist) {
     if (two_pass) run(T1{}, T1{});
-    run(F0{}, T1{});
+    else run(F0{}, T1{});
   } else {
     if (two_pass) run(T1{}, F0{});
-    run(F0{}, F0{});
+    else run(F0{}, F0{});
   }
   return hipGetLastError();
 }

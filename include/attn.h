@@ -62,12 +62,12 @@ typedef enum {
 #define ATTN_ABI_VERSION 2
 
 /* bf16 Q/K/V in, bf16 O out (round to nearest even), fp32 LSE out. P is rounded to
- * bf16 before the P.V contraction; both contractions accumulate in fp32. A call of at
- * least 1e11 counted FLOPs (4*B*H*N^2*d, halved for causal) enqueues two kernels on
- * `stream` (a pass that uses the first key tile's row max as the softmax reference, then
- * a pass that redoes with a per-tile max any query tile whose probabilities outgrew it);
- * a smaller call enqueues the second kernel alone, on every tile. O and LSE are complete
- * when the call's kernels have run. */
+ * bf16 before the P.V contraction; both contractions accumulate in fp32. The call
+ * enqueues one kernel on `stream`. At least 1e11 counted FLOPs (4*B*H*N^2*d, halved for
+ * causal): a pass that uses the first key tile's row max as the softmax reference, whose
+ * workgroups redo with a per-tile max any query tile whose probabilities outgrew it; a
+ * smaller call runs the per-tile-max pass alone, on every tile. O and LSE are complete
+ * when the kernel has run. */
 attn_status_t attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                             void* stream);
@@ -96,8 +96,8 @@ attn_status_t attn_fwd_bf16(const void* q, const void* k, const void* v, void* o
  * passes: ATTN_PASSES_AUTO as attn_fwd_bf16 (two passes at >= 1e11 counted FLOPs);
  *   ATTN_PASSES_EXACT the running-max pass alone, on every tile (the online softmax of the
  *   FlashAttention-2 digest, glossary: a per-tile max and a rescaled running sum);
- *   ATTN_PASSES_TWO the first-tile-reference pass, then the running-max pass on the query
- *   tiles it marked, at any size.
+ *   ATTN_PASSES_TWO the first-tile-reference pass, its marked query tiles redone by the
+ *   running-max pass in the same launch, at any size.
  * dtype: ATTN_DTYPE_BF16 or ATTN_DTYPE_F16 (q, k, v, o of that type).
  * queue: ATTN_SCHED_PERSISTENT_QUEUE only (else ignored, may be NULL): caller-owned device
  *   memory of 16 int32 values, all zero before the first call; every call leaves them zero
@@ -216,8 +216,9 @@ attn_status_t attn_bwd_f16(const void* q, const void* k, const void* v, const vo
  * needs its own kernel; here each head's keys are split (split s of n takes the 32-key
  * tiles s, s + n, ...), each split's partial O and LSE go to `workspace` (caller-owned
  * device memory of attn_decode_workspace_floats(...) fp32 values, overwritten, nothing of
- * use afterwards), and a second kernel merges them through the LSEs. Two kernels are enqueued on `stream`. Nq outside [1, 32] is
- * ATTN_ERR_INVALID_ARG; d as for the other entry points. */
+ * use afterwards), and a second kernel merges them through the LSEs. Two kernels are
+ * enqueued on `stream`. Nq outside [1, 32] is ATTN_ERR_INVALID_ARG; d as for the other
+ * entry points. */
 attn_status_t attn_decode_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* workspace,
                                int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                                void* stream);

@@ -119,7 +119,8 @@ def sample_rows(N, n_random=96, seed=0):
                                                ("C4", True, "bf16"), ("H", True, "bf16"), ("H", True, "f16")])
 def test_full_size_every_row(name, causal, dtype):
     # The named workloads on every head and every row. H in bf16 is the benchmarked call
-    # in the launch configuration the benchmark times (fast pass, then exact pass).
+    # in the launch configuration the benchmark times (the fast pass, redoing marked tiles
+    # with the exact pass in the same launch).
     w = inputs.WORKLOADS[name]
     say(f"case {name} causal={causal} dtype={dtype}: every head, every row")
     cpu, gpu = make(w.wid, w.B, w.H, w.N, w.d, dtype)
@@ -232,7 +233,8 @@ def test_scores_jumping_past_the_first_tile_max(factor, causal, dtype):
     # tile's max would then overflow fp16 (x8) or any 16-bit type (x30). At N = 700 the
     # call runs the exact pass alone (per-tile max); at B2 H16 N4096 d128 and B2 H16 N8192
     # d64 (above the two-pass threshold of 1e11 FLOPs) the fast pass must mark those rows
-    # and the exact pass redo their query tiles, checked on sampled rows of two heads.
+    # and its workgroups redo their query tiles with the exact pass, checked on sampled
+    # rows of two heads.
     say(f"case jumping scores x{factor} causal={causal} dtype={dtype}")
     for B, H, N, d in ((1, 2, 700, 128), (2, 16, 4096, 128), (2, 16, 8192, 64)):
         q, k, v = inputs.draw_qkv(12, B, H, N, d)
