@@ -7,11 +7,11 @@
 //   P = exp(scale * Q K^T - LSE)        recomputed per tile from the stored LSE
 //   dV = P^T dO,   dP = dO V^T,   Delta_i = dO_i . O_i  (= sum_j P_ij dP_ij)
 //   dS = P * (dP - Delta),   dQ = scale * dS K,   dK = scale * dS^T Q
-// Three launches per call:
-//   prep  Delta_i and LSE_i * log2(e) of every row into the caller's workspace (reads O
-//         and dO once).
-//   dq    one workgroup per (batch*head, 256-row query tile), 8 waves x 32 rows; K and V
-//         tiles of 64 keys stream through LDS (double-buffered direct loads). Per 32-key
+// Two launches per call:
+//   dq    one workgroup per (batch*head, 256-row query tile), 8 waves x 32 rows. First
+//         Delta_i = dO_i . O_i and LSE_i * log2(e) of its rows (O is read here only),
+//         also written to the caller's workspace for dkdv; then K and V tiles of 64
+//         keys stream through LDS (double-buffered direct loads). Per 32-key
 //         block: S^T = K Q^T and dP^T = V dO^T (A = K / V rows read from LDS, B = Q^T and
 //         dO^T kept in VGPRs), then P and dS in fp32 with one query row per lane (its LSE
 //         and Delta are scalars), then dQ^T += K^T dS^T (A = K^T by LDS transpose reads,
@@ -44,48 +44,18 @@ constexpr int kBN = 64;     // dq: keys per K/V tile
 constexpr int kKG = 4;      // dkdv: key groups of 32 keys per workgroup
 constexpr int kWk = 8;      // dkdv: waves per workgroup (a key group x a query half of each tile)
 constexpr int kBQ = 64;     // dkdv: queries per Q/dO tile (two 32-query blocks)
-constexpr int kPrepThreads = 256;
 
 __device__ __forceinline__ float to_f32(Bf16Tag, uint32_t bits16) { return __builtin_bit_cast(float, bits16 << 16); }
 __device__ __forceinline__ float to_f32(F16Tag, uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-// Delta_i = sum_d dO_id * O_id (fp32) and LSE_i * log2(e), D/16 lanes per row.
-template <typename Tag, int D>
-__global__ __launch_bounds__(kPrepThreads) void attn_bwd_prep_kernel(const uint16_t* __restrict__ O,
-                                                                     const uint16_t* __restrict__ dO,
-                                                                     const float* __restrict__ LSE,
-                                                                     float* __restrict__ ws, int64_t rows) {
-  constexpr int LPR = D / 16;
-  const int64_t row = (int64_t)blockIdx.x * (kPrepThreads / LPR) + threadIdx.x / LPR;
-  const int seg = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const u32x4 o = *(const u32x4*)(O + row * D + seg * 16 + i * 8);
-      const u32x4 g = *(const u32x4*)(dO + row * D + seg * 16 + i * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = __builtin_fmaf(to_f32(Tag{}, o[e] & 0xFFFFu), to_f32(Tag{}, g[e] & 0xFFFFu), acc);
-        acc = __builtin_fmaf(to_f32(Tag{}, o[e] >> 16), to_f32(Tag{}, g[e] >> 16), acc);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off /= 2) acc += __shfl_xor(acc, off);
-  if (row < rows && seg == 0) {
-    ws[row] = acc;
-    ws[rows + row] = LSE[row] * kLog2e;
-  }
-}
-
 template <typename Tag, int D, bool CAUSAL>
 __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dQ, int N, int n_mtiles,
-    int total_wg, int64_t rows, float c /* scale*log2 e */, float scale) {
+    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ ws, uint16_t* __restrict__ dQ, int N, int n_mtiles, int total_wg, int64_t rows,
+    float c /* scale*log2 e */, float scale) {
   constexpr int W = kWq, BM = W * 32, NSTEP = D / 16, NKB = kBN / 32, NDB = D / 32;
   constexpr int TB = kBN * D * 2;                   // bytes per K (or V) tile
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TB];   // K slots 0, 1; V slots 0, 1
@@ -103,11 +73,26 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
 
   const int q0 = mt * BM + wave * 32;
   const int qrow = q0 + l32;
-  u32x4 qreg[NSTEP], doreg[NSTEP];
+  u32x4 qreg[NSTEP], doreg[NSTEP], oreg[NSTEP];
   load_row_operand<D>(Q + head_off, qrow, N, half, qreg);
   load_row_operand<D>(dO + head_off, qrow, N, half, doreg);
-  const float delta = qrow < N ? ws[(int64_t)bh * N + qrow] : 0.f;
-  const float lse2 = qrow < N ? ws[rows + (int64_t)bh * N + qrow] : 0.f;
+  load_row_operand<D>(O + head_off, qrow, N, half, oreg);
+  // Delta = dO . O of this lane's row (each half of the wave holds half of the row) and
+  // LSE in log2 units; published in the workspace for the dK/dV kernel, which runs next.
+  float dpart = 0.f;
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dpart = __builtin_fmaf(to_f32(Tag{}, oreg[st][e] & 0xFFFFu), to_f32(Tag{}, doreg[st][e] & 0xFFFFu), dpart);
+      dpart = __builtin_fmaf(to_f32(Tag{}, oreg[st][e] >> 16), to_f32(Tag{}, doreg[st][e] >> 16), dpart);
+    }
+  const float delta = add_halves(dpart);
+  const float lse2 = qrow < N ? LSE[(int64_t)bh * N + qrow] * kLog2e : 0.f;
+  if (qrow < N && half == 0) {
+    ws[(int64_t)bh * N + qrow] = delta;
+    ws[rows + (int64_t)bh * N + qrow] = lse2;
+  }
 
   const int n_ktiles = (N + kBN - 1) / kBN;
   const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * BM + kBN - 1) / kBN) : n_ktiles;
@@ -349,15 +334,12 @@ template <typename Tag, int D, bool CAUSAL>
 hipError_t launch_one(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                       void* dq, void* dk, void* dv, float* ws, int64_t BH, int64_t N, float scale, hipStream_t stream) {
   const int64_t rows = BH * N;
-  constexpr int rows_per_prep = kPrepThreads / (D / 16);
-  hipLaunchKernelGGL((attn_bwd_prep_kernel<Tag, D>), dim3((unsigned)((rows + rows_per_prep - 1) / rows_per_prep)),
-                     dim3(kPrepThreads), 0, stream, (const uint16_t*)o, (const uint16_t*)dout, lse, ws, rows);
   const float c = scale * kLog2e;
   const int n_mtiles = (int)((N + kWq * 32 - 1) / (kWq * 32));
   const int64_t total_q = BH * n_mtiles;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag, D, CAUSAL>), dim3((unsigned)total_q), dim3(kWq * 64), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws,
-                     (uint16_t*)dq, (int)N, n_mtiles, (int)total_q, rows, c, scale);
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
+                     (const uint16_t*)o, lse, ws, (uint16_t*)dq, (int)N, n_mtiles, (int)total_q, rows, c, scale);
   const int n_ntiles = (int)((N + kKG * 32 - 1) / (kKG * 32));
   const int64_t total_k = BH * n_ntiles;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)total_k), dim3(kWk * 64), 0, stream,
@@ -394,8 +376,7 @@ hipError_t launch_bwd_f16(const void* q, const void* k, const void* v, const voi
 int64_t max_workgroups_bwd(int64_t BH, int64_t N) {
   const int64_t a = BH * ((N + kWq * 32 - 1) / (kWq * 32));
   const int64_t b = BH * ((N + kKG * 32 - 1) / (kKG * 32));
-  const int64_t p = (BH * N + 15) / 16;              // prep: at least 16 rows per workgroup
-  return a > b ? (a > p ? a : p) : (b > p ? b : p);
+  return a > b ? a : b;
 }
 
 }  // namespace attn

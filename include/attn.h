@@ -195,8 +195,8 @@ attn_status_t attn_fwd_fp8_rotq(const void* q, const float* signs, const uint8_t
  * O = softmax(scale * q k^T [+ causal mask]) v. workspace is caller-owned device memory
  * of 2 * B * H * N floats; the call overwrites it (per row: dout . o, then lse * log2 e)
  * and it holds nothing of use afterwards. The products use bf16 operands (P and dS
- * rounded to bf16) with fp32 accumulation. The call enqueues three kernels on `stream`;
- * dq, dk and dv are complete when the last has run. Outputs must not overlap each other,
+ * rounded to bf16) with fp32 accumulation. The call enqueues two kernels on `stream`;
+ * dq, dk and dv are complete when the second has run. Outputs must not overlap each other,
  * the inputs or the workspace. */
 attn_status_t attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                             const void* dout, void* dq, void* dk, void* dv, float* workspace,
