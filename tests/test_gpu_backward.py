@@ -121,6 +121,18 @@ def test_full_size_every_head(name, causal):
     compare(got, ref, f"{name} every head causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_full_size_d64_every_head(causal):
+    # the d = 64 instantiations of both gradient kernels at full size: B2 H16 N8192 d64,
+    # every head of every gradient against the oracle
+    B, H, N, d = 2, 16, 8192, 64
+    say(f"case bwd full size B{B} H{H} N{N} d{d} causal={causal}")
+    cpu = make(73, B, H, N, d, "bf16")
+    got = run_device(cpu, "bf16", causal)
+    ref = backward_pooled(*cpu, causal, inputs.softmax_scale(d))
+    compare(got, ref, f"d64 every head causal={causal}")
+
+
 def test_dispatch_stream_and_determinism():
     cpu = make(72, 1, 2, 300, 64, "f16")
     tq, tk, tv, tg = (t.cuda() for t in cpu)
