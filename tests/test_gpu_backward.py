@@ -109,16 +109,17 @@ def test_large_scores(causal):
     compare(got, ref, f"x8 keys causal={causal}")
 
 
-@pytest.mark.parametrize("name,causal", [("H", True), ("C3", True), ("C3", False)])
-def test_full_size_every_head(name, causal):
+@pytest.mark.parametrize("name,causal,dtype", [("H", True, "bf16"), ("H", True, "f16"), ("C3", True, "bf16"),
+                                               ("C3", False, "bf16")])
+def test_full_size_every_head(name, causal, dtype):
     # full-size launch, every head of every gradient against the oracle (one head per
     # worker thread on the host's cores)
     w = inputs.WORKLOADS[name]
-    say(f"case bwd full size {name} B{w.B} H{w.H} N{w.N} d{w.d} causal={causal}")
-    cpu = make(w.wid, w.B, w.H, w.N, w.d, "bf16")
-    got = run_device(cpu, "bf16", causal)
+    say(f"case bwd full size {name} B{w.B} H{w.H} N{w.N} d{w.d} causal={causal} {dtype}")
+    cpu = make(w.wid, w.B, w.H, w.N, w.d, dtype)
+    got = run_device(cpu, dtype, causal)
     ref = backward_pooled(*cpu, causal, w.scale)
-    compare(got, ref, f"{name} every head causal={causal}")
+    compare(got, ref, f"{name} {dtype} every head causal={causal}")
 
 
 @pytest.mark.parametrize("causal", [True, False])
