@@ -63,11 +63,9 @@ typedef enum {
 
 /* bf16 Q/K/V in, bf16 O out (round to nearest even), fp32 LSE out. P is rounded to
  * bf16 before the P.V contraction; both contractions accumulate in fp32. The call
- * enqueues one kernel on `stream`. At least 1e11 counted FLOPs (4*B*H*N^2*d, halved for
- * causal): a pass that uses the first key tile's row max as the softmax reference, whose
- * workgroups redo with a per-tile max any query tile whose probabilities outgrew it; a
- * smaller call runs the per-tile-max pass alone, on every tile. O and LSE are complete
- * when the kernel has run. */
+ * enqueues one kernel on `stream`: a pass that uses the first key tile's row max as the
+ * softmax reference, whose workgroups redo with a per-tile max any query tile whose
+ * probabilities outgrew it. O and LSE are complete when the kernel has run. */
 attn_status_t attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                             void* stream);
@@ -93,7 +91,7 @@ attn_status_t attn_fwd_bf16(const void* q, const void* k, const void* v, void* o
  *                                 tiles of the default order one at a time from a counter
  *                                 in `queue` (dynamic: a workgroup that finishes early
  *                                 takes the next tile)
- * passes: ATTN_PASSES_AUTO as attn_fwd_bf16 (two passes at >= 1e11 counted FLOPs);
+ * passes: ATTN_PASSES_AUTO as attn_fwd_bf16 (the same as ATTN_PASSES_TWO);
  *   ATTN_PASSES_EXACT the running-max pass alone, on every tile (the online softmax of the
  *   FlashAttention-2 digest, glossary: a per-tile max and a rescaled running sum);
  *   ATTN_PASSES_TWO the first-tile-reference pass, its marked query tiles redone by the

@@ -130,9 +130,9 @@ def test_full_size_every_row(name, causal, dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [True, False])
 def test_d64_two_pass_every_row(causal, dtype):
-    # Head dim 64 above the two-pass threshold (B2 H16 N8192 d64: 2.7e11 FLOPs causal,
-    # 5.5e11 non-causal), so the first-tile-reference pass and the exact pass both run in
-    # their d = 64 instantiations; every head, every row.
+    # Head dim 64 at full size (B2 H16 N8192 d64: 2.7e11 FLOPs causal, 5.5e11 non-causal)
+    # through the default call (the first-tile-reference pass) in its d = 64
+    # instantiation; every head, every row.
     B, H, N, d = 2, 16, 8192, 64
     say(f"case d64 two-pass B{B} H{H} N{N} causal={causal} dtype={dtype}: every head, every row")
     cpu, gpu = make(14, B, H, N, d, dtype)
@@ -230,11 +230,10 @@ def test_large_key_shift_is_stable(causal):
 def test_scores_jumping_past_the_first_tile_max(factor, causal, dtype):
     # Keys from 300 on are scaled up: their scores exceed the first tile's row max by about
     # 25 (x8) or far more than 64 (x30) in log2 units. Probabilities against the first
-    # tile's max would then overflow fp16 (x8) or any 16-bit type (x30). At N = 700 the
-    # call runs the exact pass alone (per-tile max); at B2 H16 N4096 d128 and B2 H16 N8192
-    # d64 (above the two-pass threshold of 1e11 FLOPs) the fast pass must mark those rows
-    # and its workgroups redo their query tiles with the exact pass, checked on sampled
-    # rows of two heads.
+    # tile's max would then overflow fp16 (x8) or any 16-bit type (x30). The fast pass
+    # must mark those rows and its workgroups redo their query tiles with the exact pass:
+    # at N = 700 on every row, at B2 H16 N4096 d128 and B2 H16 N8192 d64 on sampled rows
+    # of two heads.
     say(f"case jumping scores x{factor} causal={causal} dtype={dtype}")
     for B, H, N, d in ((1, 2, 700, 128), (2, 16, 4096, 128), (2, 16, 8192, 64)):
         q, k, v = inputs.draw_qkv(12, B, H, N, d)

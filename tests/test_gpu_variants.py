@@ -80,7 +80,7 @@ def test_every_schedule_small(shape, causal):
 @pytest.mark.parametrize("name,causal", [("H", True), ("C4", True), ("C3", False)])
 def test_every_schedule_full_size(name, causal):
     # The benchmarked shapes under every schedule (both passes, as the default call runs
-    # them above 1e11 FLOPs), against one oracle result; the queue schedule runs twice in
+    # them), against one oracle result; the queue schedule runs twice in
     # a row on one queue array.
     w = inputs.WORKLOADS[name]
     say(f"case schedules {name} causal={causal}")
