@@ -77,22 +77,7 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
   load_row_operand<D>(Q + head_off, qrow, N, half, qreg);
   load_row_operand<D>(dO + head_off, qrow, N, half, doreg);
   load_row_operand<D>(O + head_off, qrow, N, half, oreg);
-  // Delta = dO . O of this lane's row (each half of the wave holds half of the row) and
-  // LSE in log2 units; published in the workspace for the dK/dV kernel, which runs next.
-  float dpart = 0.f;
-#pragma unroll
-  for (int st = 0; st < NSTEP; ++st)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dpart = __builtin_fmaf(to_f32(Tag{}, oreg[st][e] & 0xFFFFu), to_f32(Tag{}, doreg[st][e] & 0xFFFFu), dpart);
-      dpart = __builtin_fmaf(to_f32(Tag{}, oreg[st][e] >> 16), to_f32(Tag{}, doreg[st][e] >> 16), dpart);
-    }
-  const float delta = add_halves(dpart);
-  const float lse2 = qrow < N ? LSE[(int64_t)bh * N + qrow] * kLog2e : 0.f;
-  if (qrow < N && half == 0) {
-    ws[(int64_t)bh * N + qrow] = delta;
-    ws[rows + (int64_t)bh * N + qrow] = lse2;
-  }
+  float delta, lse2;                                // this lane's row: dO . O and LSE * log2(e), set below
 
   const int n_ktiles = (N + kBN - 1) / kBN;
   const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * BM + kBN - 1) / kBN) : n_ktiles;
@@ -155,6 +140,23 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
 
   load_rows<D, kBN, W>(Kh, 0, N, kbuf(0), wave, lane);
   load_rows<D, kBN, W>(Vh, 0, N, vbuf(0), wave, lane);
+  // Delta = dO . O of this lane's row (each half of the wave holds half of the row) and
+  // LSE in log2 units, while the first K/V tile loads; published in the workspace for the
+  // dK/dV kernel, which runs next.
+  lse2 = qrow < N ? LSE[(int64_t)bh * N + qrow] * kLog2e : 0.f;
+  float dpart = 0.f;
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dpart = __builtin_fmaf(to_f32(Tag{}, oreg[st][e] & 0xFFFFu), to_f32(Tag{}, doreg[st][e] & 0xFFFFu), dpart);
+      dpart = __builtin_fmaf(to_f32(Tag{}, oreg[st][e] >> 16), to_f32(Tag{}, doreg[st][e] >> 16), dpart);
+    }
+  delta = add_halves(dpart);
+  if (qrow < N && half == 0) {
+    ws[(int64_t)bh * N + qrow] = delta;
+    ws[rows + (int64_t)bh * N + qrow] = lse2;
+  }
   wait_vmcnt<0>();
   barrier_lds();
   for (int t = 0; t < T; t += 2) {
