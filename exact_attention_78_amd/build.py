@@ -30,12 +30,13 @@ COMMON = [
 ]
 
 
-# Per-source flags. The attention kernels are written in issue order (their main loops
-# interleave MFMAs, LDS reads and softmax VALU work by hand), so the machine scheduler
-# is switched off for those files.
+# Per-source flags. The 16-bit forward kernel is written in issue order (its main loop
+# interleaves MFMAs, LDS reads and softmax VALU work by hand), so the machine scheduler
+# is switched off for that file (with it on, the headline is 1.6% slower). The fp8
+# kernel is written in the same order but gains from the scheduler (4% faster with both
+# scheduling passes on than with either or both off), so it keeps the default.
 FILE_FLAGS = {
     "attn_fwd.hip": ["-mllvm", "-enable-misched=0", "-mllvm", "-enable-post-misched=0"],
-    "attn_fwd_fp8.hip": ["-mllvm", "-enable-misched=0", "-mllvm", "-enable-post-misched=0"],
 }
 
 

@@ -7,7 +7,8 @@
 // K/V tiles, one final rescale, O and LSE written; split-Q waves of 32 rows, 8 waves per
 // workgroup; causal tiles above the diagonal skipped, masks only on diagonal / tail
 // tiles; step t issues P.V of tile t, the softmax of tile t+1 and S^T of tile t+2, with
-// MFMAs, LDS reads and VALU work written in issue order).
+// MFMAs, LDS reads and VALU work written in the intended issue order, which the machine
+// scheduler then refines: unlike the 16-bit kernel, this one is 4% faster with it).
 //
 // Per tile of 64 keys (inside one 128-row scale block of K and V):
 //   S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 on the raw codes (two per 32 keys);
@@ -414,10 +415,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
       const float ct = cq * sk_next;
       const bool uchg = weight(sv_next, w_soft);
       const float lw = __builtin_amdgcn_logf(w_soft);     // log2 w
-      // Main block in issue order: NQ S^T MFMAs (K fragments one MFMA ahead) and NDB P.V
-      // MFMAs (V^T fragments one MFMA ahead); the row max runs beside the first two S^T
-      // MFMAs, the exponentials beside the others (d = 128: 4 + 4, six slots; d = 64: 2 + 2,
-      // two slots).
+      // Main block in intended issue order: NQ S^T MFMAs (K fragments one MFMA ahead) and
+      // NDB P.V MFMAs (V^T fragments one MFMA ahead); the row max runs beside the first two
+      // S^T MFMAs, the exponentials beside the others (d = 128: 4 + 4, six slots; d = 64:
+      // 2 + 2, two slots).
       constexpr int NQ = NKB * NM;
       i32x8 kf[NQ], vf[NDB];
       auto kread = [&](int i) __attribute__((always_inline)) { kf[i] = kfrag(kbuf(KRD), i % NKB, i / NKB); };
