@@ -61,10 +61,16 @@ __device__ __forceinline__ uint32_t pack2(F16Tag, float a, float b) {
 __device__ __forceinline__ void permlane32_swap_pair(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
-// IEEE-754 2019 maximum (NaN-propagating): one v_maximum3_f32, with no canonicalising
-// v_max of each input as fmaxf needs.
+// IEEE-754 2019 maximum (NaN-propagating) of three values: one v_maximum3_f32, with no
+// canonicalising v_max of each input as fmaxf needs. Written as the instruction itself:
+// from nested two-input maxima the compiler re-balances a chain of these into pairs
+// (v_maximum3 with a repeated operand) and a tree over them, 24 instructions for the 32
+// scores of a tile where 16 do. (Its inputs here are MFMA results of an earlier step or
+// VALU results, far outside the MFMA-to-VALU read hazard window.)
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-  return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+  float r;
+  asm("v_maximum3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 __device__ __forceinline__ float max_halves(float x) {
   float a = x, b = x;
@@ -164,6 +170,12 @@ __device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
 // and barrier_lds(). (The s_nop separates the M0 write from the instruction that reads it.)
 __device__ __forceinline__ void dma_load16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(gptr), "{m0}"(lds_base) : "memory");
+}
+
+// The 4-byte form (global_load_lds_dword): lane i's 4 bytes land at lds_base + 4*i (lanes
+// with exec clear write nothing).
+__device__ __forceinline__ void dma_load4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(gptr), "{m0}"(lds_base) : "memory");
 }
 
 // Workgroup barrier for LDS hand-over only: LDS reads of this wave are complete, then
