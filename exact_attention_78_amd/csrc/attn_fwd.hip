@@ -99,9 +99,21 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];
   __shared__ int marked;                            // fast pass: some wave of the tile is marked
   __shared__ int stop[2];                           // fast pass: some wave is marked (by step parity)
+  __shared__ int ticket[2];                         // persistent grids: current and next ticket
+  u32x4 qreg[NSTEP];                                // Q^T as the B operand, resident (persistent grids:
+                                                    // the next tile's rows arrive while a tile ends)
 
   // One query tile (batch*head, m-tile), by the fast pass (FASTP) or the exact pass.
-  auto tile = [&](auto fast_c, const int bh, const int mt) __attribute__((always_inline)) {
+  // Persistent grids (fast pass): pf_in says that the previous tile of this workgroup has
+  // already loaded this tile's Q rows (into qreg) and its first K / V tiles (into the
+  // rings). draw >= 0: this tile draws the workgroup's next ticket into ticket[draw], as
+  // late as it can, so that the queue still hands tiles out in the order the workgroups
+  // finish them: the fast pass, when its own tile count is a multiple of 4 (the ring slots
+  // then line up), draws it four steps before its end and loads the next tile's Q and first
+  // K / V tiles during its last four steps; otherwise a tile draws it after its loop.
+  // Returns whether it loaded the next tile's data.
+  auto tile = [&](auto fast_c, const int bh, const int mt, const bool pf_in, const int draw)
+                  __attribute__((always_inline)) -> bool {
     constexpr bool FASTP = decltype(fast_c)::value;
 
     const int tid = threadIdx.x;
@@ -122,13 +134,49 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
         marked = 0;
       }
     }
-    u32x4 qreg[NSTEP];                                // Q^T as the B operand, resident
+    auto load_q = [&](const uint16_t* Qb, int row) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s)
-      qreg[s] = qrow < N ? *(const u32x4*)(Qh + (int64_t)qrow * D + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
+      for (int s = 0; s < NSTEP; ++s)
+        qreg[s] = row < N ? *(const u32x4*)(Qb + (int64_t)row * D + s * 16 + half * 8) : u32x4{0, 0, 0, 0};
+    };
+    if (!(PERSIST && FASTP && pf_in)) load_q(Qh, qrow);
 
     const int n_ktiles = (N + kBN - 1) / kBN;
-    const int T = CAUSAL ? min(n_ktiles, ((mt + 1) * BM + kBN - 1) / kBN) : n_ktiles;
+    auto tiles_of = [&](int m) __attribute__((always_inline)) {
+      return CAUSAL ? min(n_ktiles, ((m + 1) * BM + kBN - 1) / kBN) : n_ktiles;
+    };
+    const int T = tiles_of(mt);
+    // the next tile (persistent fast pass): cap, this tile runs its last four steps apart
+    // (they can load the next tile's first data); pfo, it does load it (the next ticket is
+    // valid); the next tile's head offset, m-tile and tile count, looked up from its ticket
+    // after the main loop, so that nothing of it stays live through the loop
+    const bool cap = PERSIST && FASTP && draw >= 0 && T % 4 == 0;
+    bool pfo = false;
+    int64_t nhead_off = 0;
+    int nmt = 0, nT = 1;
+    auto next_tile = [&]() __attribute__((always_inline)) -> bool {
+      const int64_t wl = (int64_t)ticket[draw] * 8 + blockIdx.x % 8;
+      if (wl < 0 || wl >= total_wg) return false;
+      int nbh;
+      query_tile_ordered(kOrderXcdPairs, (int)wl, total_wg, n_mtiles, CAUSAL, nbh, nmt);
+      nhead_off = (int64_t)nbh * N * D;
+      nT = tiles_of(nmt);
+      return true;
+    };
+    // the next ticket (persistent grids): from the XCD's queue or the fixed stride; thread
+    // 0 writes it to LDS for the other waves (after a wait for loads that covers it)
+    int tnext = 0;
+    bool drawn = false;
+    auto draw_ticket = [&]() __attribute__((always_inline)) {
+      if (tid == 0) tnext = persist == 2 ? atomicAdd(queue + blockIdx.x % 8, 1) : ticket[draw ^ 1] + gridDim.x / 8;
+      drawn = true;
+    };
+    auto publish = [&]() __attribute__((always_inline)) {
+      if (tid == 0) ticket[draw] = tnext;
+    };
+    if constexpr (PERSIST && FASTP) {
+      if (cap && T < 8) draw_ticket();          // no main loop: drawn before the prologue's loads
+    }
 
     uint32_t kaddr[NSTEP];
 #pragma unroll
@@ -264,10 +312,18 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     //   K(t+2) in K slot (t+2)%4, V(t) in V slot t%4; loads: K(t+4) -> K slot t%4,
     //   V(t+3) -> V slot (t+3)%4. Past the last tile the loads are clamped (never read),
     //   and the scores of tile T (if computed) are fully masked, so P(T) = 0 adds nothing.
+    // K(t+4) and V(t+3) of a step; past the last tile, the next tile's first tiles when
+    // this tile loads them (pfo), else the last tile again (never read)
+    auto kv_loads = [&](int t, auto KLD, auto VLD, auto ROUTEc) __attribute__((always_inline)) {
+      if (decltype(ROUTEc)::value && pfo && t + 4 >= T) load_tile(K + nhead_off, ld_koff, ld_kch, min(t + 4 - T, nT - 1), kbuf(KLD));
+      else load_tile(Kh, ld_koff, ld_kch, min(t + 4, T - 1), kbuf(KLD));
+      if (decltype(ROUTEc)::value && pfo && t + 3 >= T) load_tile(V + nhead_off, ld_voff, ld_vch, min(t + 3 - T, nT - 1), vbuf(VLD));
+      else load_tile(Vh, ld_voff, ld_vch, min(t + 3, T - 1), vbuf(VLD));
+    };
     auto step = [&](int t, f32x16 (&S_soft)[NKB], f32x16 (&S_new)[NKB], const u32x4 (&P_use)[NKB][2],
-                    u32x4 (&P_new)[NKB][2], auto KRD, auto VRD, auto KLD, auto VLD) __attribute__((always_inline)) {
-      load_tile(Kh, ld_koff, ld_kch, min(t + 4, T - 1), kbuf(KLD));
-      load_tile(Vh, ld_voff, ld_vch, min(t + 3, T - 1), vbuf(VLD));
+                    u32x4 (&P_new)[NKB][2], auto KRD, auto VRD, auto KLD, auto VLD, auto ROUTEc)
+                    __attribute__((always_inline)) {
+      kv_loads(t, KLD, VLD, ROUTEc);
       // Causal: once the tile's first key lies past this wave's last row, this and every
       // later tile are fully masked for the wave; it only keeps up its loads and barriers.
       if (!CAUSAL || t * kBN <= q0 + 31) {
@@ -340,16 +396,80 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       barrier_lds();
     };
 
-    // Prologue: K tiles 0..3 and V tiles 0..2; S(0), softmax of tile 0, S(1).
-    load_tile(Kh, ld_koff, ld_kch, 0, kbuf(IC<0>{}));
-    load_tile(Kh, ld_koff, ld_kch, min(1, T - 1), kbuf(IC<1>{}));
-    load_tile(Kh, ld_koff, ld_kch, min(2, T - 1), kbuf(IC<2>{}));
-    load_tile(Kh, ld_koff, ld_kch, min(3, T - 1), kbuf(IC<3>{}));
-    load_tile(Vh, ld_voff, ld_vch, 0, vbuf(IC<0>{}));
-    load_tile(Vh, ld_voff, ld_vch, min(1, T - 1), vbuf(IC<1>{}));
-    load_tile(Vh, ld_voff, ld_vch, min(2, T - 1), vbuf(IC<2>{}));
+    // The last two steps of a tile that loads its successor (pfo: T a multiple of 4, fast
+    // pass), with no S^T MFMAs (the tiles T and T+1 they would compute do not exist), so
+    // that qreg is free: DRAIN 1 (t = T-2) loads the next tile's Q rows into qreg and runs
+    // the softmax of tile T-1 beside the P.V MFMAs of tile T-2; DRAIN 2 (t = T-1) runs the
+    // P.V MFMAs of tile T-1. Neither waits for loads: nothing reads the rings again before
+    // the next tile's prologue, which waits for all of them.
+    auto drain = [&](auto DRc, int t, f32x16 (&S_soft)[NKB], const u32x4 (&P_use)[NKB][2], u32x4 (&P_new)[NKB][2],
+                     auto VRD, auto KLD, auto VLD) __attribute__((always_inline)) {
+      constexpr int DR = decltype(DRc)::value;
+      if constexpr (DR == 1) {
+        if (pfo) load_q(Q + nhead_off, nmt * BM + wave * 32 + l32);
+      }
+      kv_loads(t, KLD, VLD, std::true_type{});
+      if (!CAUSAL || t * kBN <= q0 + 31) {
+        constexpr int NP = NDB * NKB * 2, VD = kVD;
+        constexpr int NSL = NP - kTail;                  // P.V MFMAs that carry exponentials
+        u32x4 vf[NP];
+        auto vread = [&](int i) __attribute__((always_inline)) {   // i = (kb * 2 + h) * NDB + db
+          const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
+          const uint8_t* base = vbuf(VRD) + (kb * 32 + h * 16) * ROW + vaddr[db];
+          const u32x2 v1 = lds_read_tr16((const uint16_t*)base);
+          const u32x2 v2 = lds_read_tr16((const uint16_t*)(base + 8 * ROW));
+          vf[i] = u32x4{v1[0], v1[1], v2[0], v2[1]};
+        };
+        float lsum[2] = {0.f, 0.f};
+        auto lo = [&](int slot) __attribute__((always_inline)) { return min(slot * (NKB * 16) / NSL, NKB * 16); };
+        if constexpr (DR == 1) {
+          mask_tile(t + 1, S_soft);
+          args(S_soft, lo(0), lo(1));
+        }
+#pragma unroll
+        for (int i = 0; i < VD; ++i) vread(i);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          if (i + VD < NP) vread(i + VD);
+          const int db = i % NDB, kb = i / (2 * NDB), h = (i / NDB) % 2;
+          oacc[db] = mfma32(Tag{}, vf[i], P_use[kb][h], oacc[db]);
+          if constexpr (DR == 1) {
+            if (i < NSL) {
+              if (i + 1 < NSL) args(S_soft, lo(i + 1), lo(i + 2));
+              exps(S_soft, lo(i), lo(i + 1));
+              if (i > 0) finish(S_soft, P_new, lsum, lo(i - 1), lo(i));
+            }
+          }
+        }
+        if constexpr (DR == 1) {
+          finish(S_soft, P_new, lsum, lo(NSL - 1), NKB * 16);
+          const float lt = lsum[0] + lsum[1];
+          l_part += lt;
+          ovf |= !(lt <= kGuard);
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(ovf) != 0 && lane == 0) stop[t & 1] = 1;
+      barrier_lds();
+    };
+
+    // Prologue: K tiles 0..3 and V tiles 0..2 (unless the previous tile loaded them); S(0),
+    // softmax of tile 0, S(1).
+    if (!(PERSIST && FASTP && pf_in)) {
+      load_tile(Kh, ld_koff, ld_kch, 0, kbuf(IC<0>{}));
+      load_tile(Kh, ld_koff, ld_kch, min(1, T - 1), kbuf(IC<1>{}));
+      load_tile(Kh, ld_koff, ld_kch, min(2, T - 1), kbuf(IC<2>{}));
+      load_tile(Kh, ld_koff, ld_kch, min(3, T - 1), kbuf(IC<3>{}));
+      load_tile(Vh, ld_voff, ld_vch, 0, vbuf(IC<0>{}));
+      load_tile(Vh, ld_voff, ld_vch, min(1, T - 1), vbuf(IC<1>{}));
+      load_tile(Vh, ld_voff, ld_vch, min(2, T - 1), vbuf(IC<2>{}));
+    }
     wait_vmcnt<0>();
+    if constexpr (PERSIST && FASTP) {
+      if (drawn) publish();
+    }
     barrier_lds();
+    // the next tile of this workgroup (persistent fast pass): its head's K and V, its tile
+    // count and whether this tile loads its first tiles
     qk(IC<0>{}, Sa);
     {
       mask_tile(0, Sa);
@@ -367,11 +487,26 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     barrier_lds();                 // K slots 0 and 1 are refilled from step 0 on
 
     int t_end = T;
-    for (int t = 0; t < t_end; t += 4) {
-      step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{});
-      if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{});
-      if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{});
-      if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{});
+    const int t_main = cap ? T - 4 : T;                // cap: the last four steps follow the loop
+    for (int t = 0; t < min(t_end, t_main); t += 4) {
+      using F0 = std::false_type;
+      step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{}, F0{});
+      if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{}, F0{});
+      if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{}, F0{});
+      if (t + 3 < T) {
+        // cap: step T-5 draws the next ticket, published before the last four steps
+        const bool dr = PERSIST && FASTP && cap && t + 4 == t_main;
+        if constexpr (PERSIST && FASTP) {
+          if (dr) draw_ticket();
+        }
+        step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{}, F0{});
+        if constexpr (PERSIST && FASTP) {
+          if (dr) {
+            publish();
+            barrier_lds();
+          }
+        }
+      }
       // Fast pass: once some wave is marked, the tile is left to the exact pass. stop[1]
       // was last written in step t+3 (or t+1) before its barrier and is next written in
       // step t+5, after the barrier of step t+4, so every wave reads the same value here
@@ -380,14 +515,34 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
         if (stop[1] != 0) t_end = t + 4;
       }
     }
-    wait_vmcnt<0>();               // no load may still target this workgroup's LDS when it exits
+    bool pf_out = false;
+    if constexpr (PERSIST && FASTP) {
+      if (cap && t_end == T) {     // not stopped: the last four steps, which load the next tile
+        pfo = next_tile();
+        const int t = T - 4;
+        step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{}, std::true_type{});
+        step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{}, std::true_type{});
+        drain(IC<1>{}, t + 2, Sb, Pa, Pb, IC<2>{}, IC<2>{}, IC<1>{});
+        drain(IC<2>{}, t + 3, Sa, Pb, Pa, IC<3>{}, IC<3>{}, IC<2>{});
+        pf_out = pfo;
+      }
+    }
+    if constexpr (PERSIST) {
+      if (draw >= 0 && !drawn) {   // not drawn yet: now (published by the barrier after the tile)
+        draw_ticket();
+        publish();
+      }
+    }
+    // no load may still target this workgroup's LDS when it exits, or when the exact pass
+    // redoes the tile (the next tile's loads, when this tile issued them, are left in flight)
+    if (!pf_out) wait_vmcnt<0>();
     if (pend) rescale_o();
 
     const float l_tot = add_halves(l_part);
     if constexpr (FASTP) {
       if (__builtin_amdgcn_ballot_w64(ovf) != 0 && lane == 0) marked = 1;   // redo the tile exactly
     }
-    if (qrow >= N) return;
+    if (qrow >= N) return pf_out;
     const float inv = 1.0f / l_tot;
     uint16_t* Orow = O + head_off + (int64_t)qrow * D;
 #pragma unroll
@@ -402,16 +557,28 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       }
     const float lse = (M + __builtin_log2f(l_tot)) * kLn2;   // (a marked tile's O and LSE are rewritten)
     if (half == 0) LSE[(int64_t)bh * N + qrow] = lse;
+    return pf_out;
   };
   // A tile that the fast pass marked is redone at once by the exact pass, in the same
   // workgroup (after the barrier no wave reads the LDS rings any more).
-  auto run_tile = [&](const int bh, const int mt) __attribute__((always_inline)) {
+  // Returns whether the next tile's first loads were issued (persistent fast pass).
+  auto run_tile = [&](const int bh, const int mt, const bool pf_in, const int draw) __attribute__((always_inline)) -> bool {
     if constexpr (FAST) {
-      tile(std::true_type{}, bh, mt);
-      __syncthreads();
-      if (marked != 0) tile(std::false_type{}, bh, mt);
+      bool pf = tile(std::true_type{}, bh, mt, pf_in, draw);
+      // The flag is in LDS: an LDS-only barrier publishes it. (__syncthreads() would also
+      // wait for this wave's O and LSE stores to complete, several microseconds under load,
+      // before the workgroup can leave.) A redo first drains those stores, since it
+      // rewrites the same rows, and any loads of the next tile, since it refills the rings;
+      // the next tile then loads its own.
+      barrier_lds();
+      if (marked != 0) {
+        wait_vmcnt<0>();
+        tile(std::false_type{}, bh, mt, false, -1);
+        pf = false;
+      }
+      return pf;
     } else {
-      tile(std::false_type{}, bh, mt);
+      return tile(std::false_type{}, bh, mt, false, draw);
     }
   };
   // The query tiles of this workgroup. A plain grid has one workgroup per tile, picked by
@@ -421,29 +588,28 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   // that order (longest first when causal). Its workgroups take either every P-th of them
   // (P workgroups per queue: a fixed stride, as a persistent kernel that walks its share
   // in a loop does), or the next one from the queue's counter, an atomic in caller memory.
+  // A workgroup's next ticket is drawn during its current tile, so that the fast pass can
+  // load the next tile's Q rows and first K / V tiles in the current tile's last steps.
   // (The plain grid is a separate instantiation without the loop, so that the compiler
   // keeps the one-tile kernel's code as it is.)
   if constexpr (!PERSIST) {
     int bh, mt;
     query_tile_ordered(order, blockIdx.x, total_wg, n_mtiles, CAUSAL, bh, mt);
-    run_tile(bh, mt);
+    run_tile(bh, mt, false, -1);
     return;
   }
-  __shared__ int ticket;
   const int xq = blockIdx.x % 8, per_q = gridDim.x / 8;
-  for (int it = 0;; ++it) {
-    int tk = blockIdx.x / 8 + it * per_q;
-    __syncthreads();               // every wave is done with the previous tile's LDS flags and ticket
-    if (persist == 2) {
-      if (threadIdx.x == 0) ticket = atomicAdd(queue + xq, 1);
-      __syncthreads();
-      tk = ticket;
-    }
-    const int64_t wl = (int64_t)tk * 8 + xq;
+  if (threadIdx.x == 0) ticket[0] = persist == 2 ? atomicAdd(queue + xq, 1) : blockIdx.x / 8;
+  __syncthreads();
+  bool pf = false;
+  for (int par = 0;; par ^= 1) {
+    // ticket[par] was published by the previous tile's prologue barrier (or the one above)
+    const int64_t wl = (int64_t)ticket[par] * 8 + xq;
     if (wl < 0 || wl >= total_wg) break;   // every workgroup reaches this: the tickets only grow
     int bh, mt;
     query_tile_ordered(kOrderXcdPairs, (int)wl, total_wg, n_mtiles, CAUSAL, bh, mt);
-    run_tile(bh, mt);
+    pf = run_tile(bh, mt, pf, par ^ 1);
+    barrier_lds();                 // every wave has read this tile's flags before the next resets them
   }
   if (persist == 2 && threadIdx.x == 0) {
     // Every workgroup of queue xq has drawn its last (failing) ticket before counting its
