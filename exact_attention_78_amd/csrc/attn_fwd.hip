@@ -150,7 +150,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     // (they can load the next tile's first data); pfo, it does load it (the next ticket is
     // valid); the next tile's head offset, m-tile and tile count, looked up from its ticket
     // after the main loop, so that nothing of it stays live through the loop
-    const bool cap = PERSIST && FASTP && draw >= 0 && T % 4 == 0;
+    const bool cap = FASTP && (!PERSIST || draw >= 0) && T % 4 == 0;
     bool pfo = false;
     int64_t nhead_off = 0;
     int nmt = 0, nT = 1;
@@ -516,9 +516,9 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       }
     }
     bool pf_out = false;
-    if constexpr (PERSIST && FASTP) {
-      if (cap && t_end == T) {     // not stopped: the last four steps, which load the next tile
-        pfo = next_tile();
+    if constexpr (FASTP) {
+      if (cap && t_end == T) {     // not stopped: the last four steps (persistent: they load the next tile)
+        if constexpr (PERSIST) pfo = next_tile();
         const int t = T - 4;
         step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{}, std::true_type{});
         step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{}, std::true_type{});
