@@ -126,7 +126,7 @@ def attn_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None):
 
 # attn_sched_t / attn_passes_t / attn_dtype_t of attn.h
 SCHEDULES = {"default": 0, "xcd_all_heads": 1, "xcd_head": 2, "xcd_natural": 3, "linear_longest": 4,
-             "linear_natural": 5, "persistent_stride": 6, "persistent_queue": 7}
+             "linear_natural": 5, "persistent_stride": 6, "persistent_queue": 7, "persistent_snake": 8}
 PASSES = {"auto": 0, "exact": 1, "two": 2}
 
 

@@ -145,7 +145,7 @@ attn_status_t attn_fwd_variant(const void* q, const void* k, const void* v, void
                                int64_t H, int64_t N, int64_t d, int causal, float scale, int dtype, int sched,
                                int passes, int32_t* queue, void* stream) {
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_INVALID_ARG;
-  if (sched < ATTN_SCHED_DEFAULT || sched > ATTN_SCHED_PERSISTENT_QUEUE) return ATTN_ERR_INVALID_ARG;
+  if (sched < ATTN_SCHED_DEFAULT || sched > ATTN_SCHED_PERSISTENT_SNAKE) return ATTN_ERR_INVALID_ARG;
   if (passes < ATTN_PASSES_AUTO || passes > ATTN_PASSES_TWO) return ATTN_ERR_INVALID_ARG;
   attn_status_t st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, 2, attn::max_workgroups_fwd16);
   if (st != ATTN_OK) return st;

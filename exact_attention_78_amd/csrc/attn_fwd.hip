@@ -100,6 +100,18 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
   __shared__ int marked;                            // fast pass: some wave of the tile is marked
   __shared__ int stop[2];                           // fast pass: some wave is marked (by step parity)
   __shared__ int ticket[2];                         // persistent grids: current and next ticket
+  // Static persistent orders, ticket = index into the XCD's tiles (default order, longest
+  // first when causal): the fixed stride (persist 1) takes every P-th tile (P workgroups per
+  // XCD); the snake (persist 3) deals them round by round, forward in even rounds and
+  // backward in odd ones, so that the workgroup with the longest tile of one round gets the
+  // shortest of the next (with tile lengths that fall evenly, every workgroup gets the same
+  // total, as a queue that hands the next tile to whoever finishes first would do).
+  auto next_static = [&](int tk) __attribute__((always_inline)) -> int {
+    const int P = gridDim.x / 8, j = blockIdx.x / 8;
+    if (persist == 1) return tk + P;
+    const int r = tk / P + 1;
+    return r * P + (r % 2 == 0 ? j : P - 1 - j);
+  };
   u32x4 qreg[NSTEP];                                // Q^T as the B operand, resident (persistent grids:
                                                     // the next tile's rows arrive while a tile ends)
 
@@ -163,12 +175,12 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
       nT = tiles_of(nmt);
       return true;
     };
-    // the next ticket (persistent grids): from the XCD's queue or the fixed stride; thread
+    // the next ticket (persistent grids): from the XCD's queue, the fixed stride or the snake; thread
     // 0 writes it to LDS for the other waves (after a wait for loads that covers it)
     int tnext = 0;
     bool drawn = false;
     auto draw_ticket = [&]() __attribute__((always_inline)) {
-      if (tid == 0) tnext = persist == 2 ? atomicAdd(queue + blockIdx.x % 8, 1) : ticket[draw ^ 1] + gridDim.x / 8;
+      if (tid == 0) tnext = persist == 2 ? atomicAdd(queue + blockIdx.x % 8, 1) : next_static(ticket[draw ^ 1]);
       drawn = true;
     };
     auto publish = [&]() __attribute__((always_inline)) {
@@ -599,7 +611,7 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     return;
   }
   const int xq = blockIdx.x % 8, per_q = gridDim.x / 8;
-  if (threadIdx.x == 0) ticket[0] = persist == 2 ? atomicAdd(queue + xq, 1) : blockIdx.x / 8;
+  if (threadIdx.x == 0) ticket[0] = persist == 2 ? atomicAdd(queue + xq, 1) : blockIdx.x / 8;   // round 0 of both static orders
   __syncthreads();
   bool pf = false;
   for (int par = 0;; par ^= 1) {
@@ -641,8 +653,12 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
   // asked for: on inputs that mark no tile it was 0.6-6.6% faster than the exact pass at
   // every size measured, from 4.6e7 to 5.5e11 counted FLOPs.
   const bool two_pass = var.passes != kPassesExact;
-  const int persist = var.sched >= kSchedPersistentStride ? var.sched - kSchedPersistentStride + 1 : 0;
-  const int order = persist ? 0 : var.sched;
+  // The plain entry points run one workgroup per tile in the default order: the persistent
+  // grids, with their tiles loading their successors' first data, were within +-2% of it on
+  // H, C3 and C4, faster on some boxes and slower on others.
+  const int sched = var.sched != kSchedAuto ? var.sched : 0;
+  const int persist = sched >= kSchedPersistentStride ? sched - kSchedPersistentStride + 1 : 0;
+  const int order = persist ? 0 : sched;
   const unsigned grid = persist ? (unsigned)persistent_workgroups() : (unsigned)total;
   auto run = [&](auto FASTC, auto PERSISTC) {
     hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, W, decltype(FASTC)::value, decltype(PERSISTC)::value>),

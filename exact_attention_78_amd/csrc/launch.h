@@ -9,10 +9,11 @@ namespace attn {
 
 // Launch variants of the 16-bit forward pass: tile order or persistent grid (sched), and
 // which passes run. The values match attn_sched_t and attn_passes_t of attn.h.
-enum : int { kSchedPersistentStride = 6, kSchedPersistentQueue = 7 };
+enum : int { kSchedAuto = -1, kSchedPersistentStride = 6, kSchedPersistentQueue = 7, kSchedPersistentSnake = 8 };
 enum : int { kPassesAuto = 0, kPassesExact = 1, kPassesTwo = 2 };
 struct FwdVariant {
-  int sched = 0;             // 0..5: TileOrder of a plain grid; 6, 7: persistent grids
+  int sched = kSchedAuto;    // 0..5: TileOrder of a plain grid; 6..8: persistent grids; auto (the
+                             // plain entry points): the plain grid in the default order
   int passes = kPassesAuto;
   int* queue = nullptr;      // kSchedPersistentQueue: 16 ints of caller memory, zero between calls
 };

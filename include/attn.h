@@ -91,6 +91,13 @@ attn_status_t attn_fwd_bf16(const void* q, const void* k, const void* v, void* o
  *                                 tiles of the default order one at a time from a counter
  *                                 in `queue` (dynamic: a workgroup that finishes early
  *                                 takes the next tile)
+ *   ATTN_SCHED_PERSISTENT_SNAKE  one workgroup per CU; the workgroups of XCD x take XCD x's
+ *                                 tiles of the default order round by round, forward in
+ *                                 even rounds and backward in odd ones (static: the longest
+ *                                 tile of one round pairs with the shortest of the next)
+ * In the persistent grids a workgroup's tile loads the next tile's Q rows and first K / V
+ * tiles during its last steps (when its tile count is a multiple of 4). attn_fwd_bf16 and
+ * attn_fwd_f16 run ATTN_SCHED_DEFAULT.
  * passes: ATTN_PASSES_AUTO as attn_fwd_bf16 (the same as ATTN_PASSES_TWO);
  *   ATTN_PASSES_EXACT the running-max pass alone, on every tile (the online softmax of the
  *   FlashAttention-2 digest, glossary: a per-tile max and a rescaled running sum);
@@ -110,7 +117,8 @@ typedef enum {
   ATTN_SCHED_LINEAR_LONGEST = 4,
   ATTN_SCHED_LINEAR_NATURAL = 5,
   ATTN_SCHED_PERSISTENT_STRIDE = 6,
-  ATTN_SCHED_PERSISTENT_QUEUE = 7
+  ATTN_SCHED_PERSISTENT_QUEUE = 7,
+  ATTN_SCHED_PERSISTENT_SNAKE = 8
 } attn_sched_t;
 
 typedef enum { ATTN_PASSES_AUTO = 0, ATTN_PASSES_EXACT = 1, ATTN_PASSES_TWO = 2 } attn_passes_t;

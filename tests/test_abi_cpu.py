@@ -84,7 +84,7 @@ def test_fwd_validation(lib, fn, defect, expect):
 @no_gpu_only
 @pytest.mark.parametrize("defect,expect", [
     (dict(q=None), INVALID), (dict(N=0), INVALID), (dict(d=96), UNSUPPORTED), (dict(scale=0.0), INVALID),
-    (dict(o=A[0]), INVALID), (dict(dtype=2), INVALID), (dict(dtype=-1), INVALID), (dict(sched=8), INVALID),
+    (dict(o=A[0]), INVALID), (dict(dtype=2), INVALID), (dict(dtype=-1), INVALID), (dict(sched=9), INVALID),
     (dict(sched=-1), INVALID), (dict(passes=3), INVALID), (dict(passes=-1), INVALID),
     (dict(sched=7, queue=None), INVALID), (dict(sched=7, queue=A[5] + 4), INVALID),
     (dict(sched=7, queue=A[3] + 64), INVALID), (dict(sched=7, queue=A[4]), INVALID),
