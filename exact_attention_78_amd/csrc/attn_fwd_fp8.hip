@@ -400,8 +400,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   // K(t+2) in K slot (t+2)%4, V(t) in V slot t%4; loads K(t+4) -> K slot t%4 and
   // V(t+3) -> V slot (t+3)%4 (clamped past the last tile, never read; the scores of tile
   // T, if computed, are fully masked).
+  // DR (drain steps, T a multiple of 4): 1 at t = T-2, whose S^T MFMAs would compute the
+  // nonexistent tile T (skipped; the softmax of tile T-1 runs as usual); 2 at t = T-1, which
+  // runs only the P.V MFMAs of tile T-1 (no tile T+1 to compute, no tile T to take the
+  // softmax of).
   auto step = [&](int t, f32x16 (&S_soft)[NKB], f32x16 (&S_new)[NKB], const int (&P_use)[8], int (&P_new)[8],
-                  auto KRD, auto VRD, auto KLD, auto VLD) __attribute__((always_inline)) {
+                  auto KRD, auto VRD, auto KLD, auto VLD, auto DRc) __attribute__((always_inline)) {
+    constexpr int DR = decltype(DRc)::value;
     load_tile(Kh, min(t + 4, T - 1), kbuf(KLD));
     load_tile(Vh, min(t + 3, T - 1), vbuf(VLD));
     static_assert(kScaleRows == 2 * kBN, "a V scale block spans two tiles");
@@ -411,6 +416,27 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
       l_rnd = __builtin_fmaf(lacc[0], w_lacc, l_rnd);    // tile t-1's rounded codes
       w_lacc = w_soft;                                    // tile t, whose codes lacc sums next
       if (pend) rescale();
+      if constexpr (DR == 2) {
+        i32x8 vf[NDB];
+        auto vread = [&](int db) __attribute__((always_inline)) {
+          int av[8];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const i32x2 x = lds_read_tr8(vbuf(VRD) + ((m / 2) * 32 + (m % 2) * 16) * ROW + vaddr[db]);
+            av[2 * m] = x[0];
+            av[2 * m + 1] = x[1];
+          }
+          vf[db] = i32x8{av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]};
+        };
+        vread(0);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          if (db + 1 < NDB) vread(db + 1);
+          const i32x8 pb = {P_use[0], P_use[1], P_use[2], P_use[3], P_use[4], P_use[5], P_use[6], P_use[7]};
+          oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
+          if (db == NDB - 1) lacc = mfma_fp8(ones, pb, f32x16{});
+        }
+      } else {
       mask_tile(t + 1, S_soft);
       const float ct = cq * sk_next;
       const bool uchg = weight(sv_next, w_soft);
@@ -445,13 +471,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
         exps(S_soft, lo(slot), lo(slot + 1));
         if (slot > 0) finish(S_soft, P_new, lsum, lo(slot - 1), lo(slot));
       };
-      kread(0);
+      if constexpr (DR == 0) kread(0);
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {              // i = m * NKB + kb
-        if (i + 1 < NQ) kread(i + 1);
-        else vread(0);
+        if (i + 1 < NQ) {
+          if constexpr (DR == 0) kread(i + 1);
+        } else {
+          vread(0);
+        }
         const int kb = i % NKB, m = i / NKB;
-        S_new[kb] = mfma_fp8(kf[i], qreg[m], m == 0 ? f32x16{} : S_new[kb]);
+        if constexpr (DR == 0) S_new[kb] = mfma_fp8(kf[i], qreg[m], m == 0 ? f32x16{} : S_new[kb]);
         if (i == 0) {
           max_pairs(m4, S_soft, 4, 18);
         } else if (i == 1) {
@@ -477,6 +506,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
       l_part = __builtin_fmaf(lsum[0] + lsum[1], w_soft, l_part);
       sk_next = tile_sk(t + 2);
       sv_next = tile_sv(t + 2);
+      }
     }
     wait_vmcnt<2>();         // K(t+3) and V(t+1), issued a step earlier, have landed
     barrier_lds();
@@ -530,11 +560,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   qk(IC<1>{}, Sb);
   barrier_lds();                 // K slots 0 and 1 are refilled from step 0 on
 
-  for (int t = 0; t < T; t += 4) {
-    step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{});
-    if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{});
-    if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{});
-    if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{});
+  // Causal, T a multiple of 4: the last four steps follow the loop, the last two as drain
+  // steps (the non-causal kernel keeps one loop: a second copy of the step costs it its
+  // spill-free register allocation)
+  const bool peel = CAUSAL && T % 4 == 0;
+  const int t_main = peel ? T - 4 : T;
+  for (int t = 0; t < t_main; t += 4) {
+    step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{}, IC<0>{});
+    if (t + 1 < T) step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{});
+    if (t + 2 < T) step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{}, IC<0>{});
+    if (t + 3 < T) step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{}, IC<0>{});
+  }
+  if (CAUSAL && peel) {
+    const int t = T - 4;
+    step(t, Sb, Sa, Pa, Pb, IC<2>{}, IC<0>{}, IC<0>{}, IC<3>{}, IC<0>{});
+    step(t + 1, Sa, Sb, Pb, Pa, IC<3>{}, IC<1>{}, IC<1>{}, IC<0>{}, IC<0>{});
+    step(t + 2, Sb, Sa, Pa, Pb, IC<0>{}, IC<2>{}, IC<2>{}, IC<1>{}, IC<1>{});
+    step(t + 3, Sa, Sb, Pb, Pa, IC<1>{}, IC<3>{}, IC<3>{}, IC<2>{}, IC<2>{});
   }
   wait_vmcnt<0>();               // no load may still target this workgroup's LDS when it exits
   l_rnd = __builtin_fmaf(lacc[0], w_lacc, l_rnd);       // the last tile's rounded codes
