@@ -9,26 +9,32 @@
 //   dS = P * (dP - Delta),   dQ = scale * dS K,   dK = scale * dS^T Q
 // Two launches per call:
 //   dq    one workgroup per (batch*head, 256-row query tile), 8 waves x 32 rows. First
-//         Delta_i = dO_i . O_i and LSE_i * log2(e) of its rows (O is read here only),
-//         also written to the caller's workspace for dkdv; then K and V tiles of 64
-//         keys stream through LDS (double-buffered direct loads). Per 32-key
+//         Delta_i = dO_i . O_i and LSE_i of its rows (O is read here only), also written
+//         to the caller's workspace for dkdv (as -Delta_i and -LSE_i / scale); then K and
+//         V tiles of 64 keys stream through LDS (double-buffered direct loads). Per 32-key
 //         block: S^T = K Q^T and dP^T = V dO^T (A = K / V rows read from LDS, B = Q^T and
 //         dO^T kept in VGPRs), then P and dS in fp32 with one query row per lane (its LSE
 //         and Delta are scalars), then dQ^T += K^T dS^T (A = K^T by LDS transpose reads,
 //         B = dS rounded to 16 bits).
 //   dkdv  one workgroup per (batch*head, 128-key tile), 8 waves: 4 key groups of 32 keys
-//         x 2 halves of each 64-query tile. The tile's K and V stay in LDS, Q and dO tiles
-//         stream through it. Per wave and tile: S = Q K^T and dP = dO V^T on its 32
-//         queries (A = Q / dO rows, B = K^T / V^T as rows of K / V: one key per lane), P
-//         and dS in fp32 with the 16 per-query LSE and Delta values of each lane read from
-//         LDS, then dV^T += dO^T P and dK^T += Q^T dS (A = dO^T / Q^T by LDS transpose
-//         reads, B = P / dS rounded to 16 bits). The two halves of a key group add their
-//         partial dK / dV once, through LDS, at the end. Two waves per SIMD keep each
-//         wave within 256 VGPRs, so MFMA results stay in VGPRs (no AGPR copies).
+//         x 2 halves of each 64-query tile. Each lane keeps its key's K and V rows in
+//         registers (the B operands of S and dP); Q and dO tiles stream through a 3-slot
+//         LDS ring. Per wave and tile: S = Q K^T and dP = dO V^T on its 32 queries, with
+//         accumulators that start at -LSE / scale and -Delta of each query, so that the
+//         MFMAs give the exponent and the factor of dS directly: P = 2^(scale log2 e * s),
+//         dS = P * dp. The two waves of a key group split the gradients: the first
+//         accumulates dV^T += dO^T P, the second dK^T += Q^T dS, each over all 64 queries
+//         (A = dO^T / Q^T by LDS transpose reads, B = P / dS rounded to 16 bits); each
+//         hands the other the 16-bit P or dS of its own 32 queries through LDS. These
+//         contractions run one tile behind S and dP (tile u - 1 in the step of tile u),
+//         so the softmax of a tile and the contraction of the one before sit in the same
+//         step. Two waves per SIMD keep each wave within 256 VGPRs, so MFMA results stay
+//         in VGPRs (no AGPR copies).
 // The two gradient kernels each recompute S and dP, so that every gradient stays in
 // registers until its one store: no fp32 partial sums or atomics in memory.
-// Causal: query tiles of dq stop at the diagonal and key tiles of dkdv start at it;
-// waves skip blocks that are wholly masked for them, and only blocks crossing the
+// Causal: query tiles of dq stop at the diagonal and key tiles of dkdv start at it; a dq
+// wave skips key tiles that lie wholly past its rows (a dkdv wave computes its two fully
+// masked blocks: the other waves set the step's length), and only blocks crossing the
 // diagonal or the end of the sequence apply a mask.
 #include <type_traits>
 
@@ -143,7 +149,8 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
   // Delta = dO . O of this lane's row (each half of the wave holds half of the row) and
   // LSE in log2 units, while the first K/V tile loads; published in the workspace for the
   // dK/dV kernel, which runs next.
-  lse2 = qrow < N ? LSE[(int64_t)bh * N + qrow] * kLog2e : 0.f;
+  const float lse_raw = qrow < N ? LSE[(int64_t)bh * N + qrow] : 0.f;
+  lse2 = lse_raw * kLog2e;
   float dpart = 0.f;
 #pragma unroll
   for (int st = 0; st < NSTEP; ++st)
@@ -154,8 +161,8 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
     }
   delta = add_halves(dpart);
   if (qrow < N && half == 0) {
-    ws[(int64_t)bh * N + qrow] = delta;
-    ws[rows + (int64_t)bh * N + qrow] = lse2;
+    ws[(int64_t)bh * N + qrow] = -delta;
+    ws[rows + (int64_t)bh * N + qrow] = -(lse_raw / scale);
   }
   wait_vmcnt<0>();
   barrier_lds();
@@ -172,13 +179,12 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ ws, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int N, int n_ntiles, int total_wg, int64_t rows, float c, float scale) {
   constexpr int W = kWk, BNK = kKG * 32, NSTEP = D / 16, NDB = D / 32;
+  constexpr int NS = 3;                             // Q / dO ring slots
   constexpr int TB = kBQ * D * 2;                   // bytes per Q (or dO) tile
-  constexpr int TKV = BNK * D * 2;                  // bytes of the workgroup's K (or V)
-  constexpr int LDS_BYTES = 4 * TB + 2 * TKV;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];   // Q slots 0, 1; dO slots 0, 1; K; V
-  __shared__ __attribute__((aligned(16))) float lsd[2][2][kBQ];    // [slot][LSE*log2 e | Delta][query]
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * NS * TB];   // Q slots, then dO slots
+  __shared__ __attribute__((aligned(16))) float lsd[NS][2][kBQ];     // [slot][-LSE/scale | -Delta][query]
+  __shared__ __attribute__((aligned(16))) u32x4 xch[2][W][2][64];    // [tile parity][wave][block][lane]
   static_assert(W == 2 * kKG && kBQ == 64, "two waves (query halves) per key group");
-  static_assert(2 * kKG * NDB * 16 * 64 * 4 <= LDS_BYTES, "the final exchange fits the tiles' LDS");
 
   // causal: low key tiles see the most queries; the query-tile order, reversed, runs
   // them first
@@ -194,58 +200,120 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
   const int64_t head_off = (int64_t)bh * N * D;
   const uint16_t* Qh = Q + head_off;
   const uint16_t* dOh = dO + head_off;
-  const float* delta_h = ws + (int64_t)bh * N;
-  const float* lse2_h = ws + rows + (int64_t)bh * N;
+  const float* ndelta_h = ws + (int64_t)bh * N;     // -Delta
+  const float* nlsc_h = ws + rows + (int64_t)bh * N;  // -LSE / scale
 
   const int k0 = nt * BNK + kg * 32;
   const int krow = k0 + l32;
+  // K^T and V^T as the B operands of S = Q K^T and dP = dO V^T: this lane's key row,
+  // resident for the whole loop (zero past the end of the sequence: such a key's dK and dV
+  // are never stored)
+  u32x4 kreg[NSTEP], vreg[NSTEP];
+  load_row_operand<D>(K + head_off, krow, N, half, kreg);
+  load_row_operand<D>(V + head_off, krow, N, half, vreg);
 
   const int n_qtiles = (N + kBQ - 1) / kBQ;
   const int u0 = CAUSAL ? (nt * BNK) / kBQ : 0;
   TileAddr<D> ta;
   ta.init(lane);
+  RowPieces<D, kBQ, W> rp;
+  rp.init(wave, lane);
 
-  f32x16 acck[NDB], accv[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    acck[db] = f32x16{};
-    accv[db] = f32x16{};
-  }
-  auto qbuf = [&](int slot) __attribute__((always_inline)) { return lds + slot * TB; };
-  auto gbuf = [&](int slot) __attribute__((always_inline)) { return lds + (2 + slot) * TB; };
-  uint8_t* const kt = lds + 4 * TB;                 // rows: the workgroup's keys (past N: row N-1, never stored)
-  uint8_t* const vt = kt + TKV;
-  // the first 2 * kBQ threads fetch the LSE (log2 units) and Delta of a query tile
-  auto fetch_ld = [&](int u) __attribute__((always_inline)) -> float {
-    const int q = min(u * kBQ + (tid % kBQ), N - 1);
-    return tid < kBQ ? lse2_h[q] : delta_h[q];
-  };
-  static_assert(2 * kBQ <= W * 64, "one thread per fetched value");
-
-  const int qr = qh * 32;                           // this wave's 32 queries start at row qr of each tile
-  // Step u: prefetch Q/dO tile u + 1 (and its LSE / Delta) into the other slot, process
-  // tile u from slot SLOT (compile-time, so the tile reads take immediate offsets), then
-  // wait for the prefetch. Only blocks crossing the diagonal or the end of the sequence
-  // mask scores, in one block of their own ahead of the exponentials.
-  auto step = [&](auto slot_c, int u) __attribute__((always_inline)) {
-    constexpr int SLOT = decltype(slot_c)::value;
-    float pf = 0.f;
-    if (u + 1 < n_qtiles) {
-      load_rows<D, kBQ, W>(Qh, (u + 1) * kBQ, N, qbuf(SLOT ^ 1), wave, lane);
-      load_rows<D, kBQ, W>(dOh, (u + 1) * kBQ, N, gbuf(SLOT ^ 1), wave, lane);
-      if (tid < 2 * kBQ) pf = fetch_ld(u + 1);
+  auto qbuf = [&](auto SLOT) __attribute__((always_inline)) { return lds + decltype(SLOT)::value * TB; };
+  auto gbuf = [&](auto SLOT) __attribute__((always_inline)) { return lds + (NS + decltype(SLOT)::value) * TB; };
+  // -LSE / scale and -Delta of a query tile (the workspace holds them negated) by 4-byte
+  // direct loads into LDS, 32 values per wave (lanes 0..31 of waves 0..3): the initial
+  // values of the S and dP accumulators, so that the MFMAs produce S - LSE / scale and
+  // dP - Delta, i.e. P = 2^(c * s) and dS = P * dp with c = scale * log2 e
+  static_assert(2 * kBQ == 4 * 32 && W >= 4, "four waves fetch a tile's values");
+  auto load_ld = [&](int u, auto SLOT) __attribute__((always_inline)) {
+    if (wave < 4 && lane < 32) {
+      const float* base = wave / 2 ? ndelta_h : nlsc_h;
+      const uint32_t q = (uint32_t)min(u * kBQ + 32 * (wave % 2) + lane, N - 1);
+      dma_load4_s(base, q * 4, lds_u32((const uint8_t*)&lsd[decltype(SLOT)::value][wave / 2][32 * (wave % 2)]));
     }
-    const int qb0 = u * kBQ + qr;
-    if (!CAUSAL || qb0 + 31 >= k0) {                // else: every query of the block precedes this wave's keys
-      const uint8_t* qt = qbuf(SLOT);
-      const uint8_t* gt = gbuf(SLOT);
-      f32x16 s = f32x16{}, dp = f32x16{};
+  };
+  const int qr = qh * 32;                           // this wave's 32 queries start at row qr of each tile
+
+  // The two waves of a key group split the gradients: query half 0 accumulates dV^T +=
+  // dO^T P and half 1 dK^T += Q^T dS, each over all 64 queries of a tile. Each computes S,
+  // dP, P and dS of its own 32 queries, keeps the 16-bit operand of its own contraction and
+  // hands the other one to its partner through LDS (xch, by tile parity).
+  auto run = [&](auto ROLE) __attribute__((always_inline)) {
+    constexpr bool RV = decltype(ROLE)::value == 0;   // dV (else dK)
+    f32x16 acc[NDB];
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st)
-        s = mfma32(Tag{}, row_frag<D>(qt, ta, qr, st), row_frag<D>(kt, ta, kg * 32, st), s);
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    f32x16 s, dp;                                   // S and dP of the current tile (own 32 queries)
+    u32x4 keep[2];                                  // own P (dV) or dS (dK) of the previous tile, 16-bit
+    // The step is written in issue order, with scheduling fences, so that no phase's
+    // operand reads are hoisted into another (the registers would not hold them).
+    constexpr int NMV = 4 * NDB;                    // MFMAs of the contraction per tile
+    constexpr int EPM = 16 / NMV;                   // softmax elements beside each of them
+    static_assert(EPM * NMV == 16, "the 16 elements spread evenly over the MFMAs");
+    // MFMA i: 16-query block b = i / NDB of the tile, head-dim block db = i % NDB; A = dO^T
+    // (dV) or Q^T (dK) by transpose reads of the tile's slot, B = the block's P or dS (own
+    // blocks: this wave's half; the others: the partner's, from xch).
+    auto frag = [&](auto SLOT, int i) __attribute__((always_inline)) -> u32x4 {
+      return tr_frag<D>(RV ? gbuf(SLOT) : qbuf(SLOT), ta, (i / NDB) * 16, i % NDB);
+    };
+    auto mfma_i = [&](int i, const u32x4& a, const u32x4 (&other)[2]) __attribute__((always_inline)) {
+      const int b = i / NDB, db = i % NDB;
+      acc[db] = mfma32(Tag{}, a, b / 2 == decltype(ROLE)::value ? keep[b % 2] : other[b % 2], acc[db]);
+    };
+    auto read_other = [&](int u, u32x4 (&other)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int st = 0; st < NSTEP; ++st)
-        dp = mfma32(Tag{}, row_frag<D>(gt, ta, qr, st), row_frag<D>(vt, ta, kg * 32, st), dp);
+      for (int j = 0; j < 2; ++j) other[j] = xch[u & 1][wave ^ kKG][j][lane];
+    };
+    // the last tile's contraction alone (after the loop)
+    auto contract = [&](auto SLOT, int u) __attribute__((always_inline)) {
+      u32x4 other[2];
+      read_other(u, other);
+#pragma unroll
+      for (int i = 0; i < NMV; ++i) mfma_i(i, frag(SLOT, i), other);
+    };
+    // Step of tile u in slot CUR: loads of tile u + 1 into slot NXT (which held tile u - 2,
+    // last read a step earlier); phase A: S and dP of tile u (A = Q / dO rows, B = K^T / V^T
+    // in registers; accumulators from the offsets); the mask; phase C: the contraction of
+    // tile u - 1 (slot PRV; none in the first step), each MFMA followed by the softmax of
+    // one (d = 64: two) of the lane's 16 elements of tile u; then P and dS of tile u are
+    // packed, one kept, the other handed over. A wave whose queries all precede its keys
+    // (causal, the first two tiles) computes fully masked blocks (P = dS = 0): the step's
+    // length is set by the other waves.
+    auto step = [&](auto CUR, auto PRV, auto NXT, auto FIRST, int u) __attribute__((always_inline)) {
+      constexpr bool FST = decltype(FIRST)::value;
+      constexpr int SC = decltype(CUR)::value;
+      if (u + 1 < n_qtiles) {
+        rp.load(Qh, (u + 1) * kBQ, N, qbuf(NXT), wave);
+        rp.load(dOh, (u + 1) * kBQ, N, gbuf(NXT), wave);
+        load_ld(u + 1, NXT);
+      }
+      const uint8_t* qt = qbuf(CUR);
+      const uint8_t* gt = gbuf(CUR);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {                 // element 4g + e: query qr + 8g + 4 half + e
+        const f32x4 a = *(const f32x4*)&lsd[SC][0][qr + g * 8 + half * 4];
+        const f32x4 b = *(const f32x4*)&lsd[SC][1][qr + g * 8 + half * 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[g * 4 + e] = a[e];
+          dp[g * 4 + e] = b[e];
+        }
+      }
+      u32x4 fq[2], fg[2];
+      fq[0] = row_frag<D>(qt, ta, qr, 0);
+      fg[0] = row_frag<D>(gt, ta, qr, 0);
+#pragma unroll
+      for (int st = 0; st < NSTEP; ++st) {
+        if (st + 1 < NSTEP) {
+          fq[(st + 1) % 2] = row_frag<D>(qt, ta, qr, st + 1);
+          fg[(st + 1) % 2] = row_frag<D>(gt, ta, qr, st + 1);
+        }
+        s = mfma32(Tag{}, fq[st % 2], kreg[st], s);
+        dp = mfma32(Tag{}, fg[st % 2], vreg[st], dp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int qb0 = u * kBQ + qr;
       if ((CAUSAL && qb0 < k0 + 31) || qb0 + 32 > N) {
         // queries before this lane's key (causal) or past the sequence: element r is
         // query qb0 + 8 * (r / 4) + 4 * half + r % 4
@@ -256,80 +324,61 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
           if (o < lo || o > hi) s[r] = -INFINITY;
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
       float p[16], ds[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qi = qr + g * 8 + half * 4;       // this lane's queries qi .. qi + 3 of the tile
-        const f32x4 l4 = *(const f32x4*)&lsd[SLOT][0][qi];
-        const f32x4 d4 = *(const f32x4*)&lsd[SLOT][1][qi];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = g * 4 + e;
-          p[r] = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
-          ds[r] = p[r] * (dp[r] - d4[e]);
-        }
+      u32x4 fa[3], other[2];
+      if constexpr (!FST) {
+        read_other(u - 1, other);
+        fa[0] = frag(PRV, 0);
+        fa[1] = frag(PRV, 1);
       }
-      u32x4 pb[2], sb[2];
-      pack16<Tag>(p, pb);
-      pack16<Tag>(ds, sb);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          accv[db] = mfma32(Tag{}, tr_frag<D>(gt, ta, qr + h * 16, db), pb[h], accv[db]);
-          acck[db] = mfma32(Tag{}, tr_frag<D>(qt, ta, qr + h * 16, db), sb[h], acck[db]);
+      for (int i = 0; i < NMV; ++i) {
+        if constexpr (!FST) {
+          if (i + 2 < NMV) fa[(i + 2) % 3] = frag(PRV, i + 2);
+          mfma_i(i, fa[i % 3], other);
         }
-    }
-    if (u + 1 < n_qtiles && tid < 2 * kBQ) lsd[SLOT ^ 1][tid / kBQ][tid % kBQ] = pf;
+#pragma unroll
+        for (int r = i * EPM; r < (i + 1) * EPM; ++r) {
+          p[r] = fast_exp2(s[r] * c);
+          ds[r] = p[r] * dp[r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      u32x4 give[2];
+      pack16<Tag>(RV ? p : ds, keep);
+      pack16<Tag>(RV ? ds : p, give);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) xch[u & 1][wave][j][lane] = give[j];
+      wait_vmcnt<0>();
+      barrier_lds();
+    };
+
+    rp.load(Qh, u0 * kBQ, N, qbuf(IC<0>{}), wave);   // u0 < n_qtiles: the tile's first key is < N
+    rp.load(dOh, u0 * kBQ, N, gbuf(IC<0>{}), wave);
+    load_ld(u0, IC<0>{});
     wait_vmcnt<0>();
     barrier_lds();
+    using T1 = std::true_type;
+    using F0 = std::false_type;
+    step(IC<0>{}, IC<2>{}, IC<1>{}, T1{}, u0);
+    for (int u = u0 + 1; u < n_qtiles; u += 3) {   // tile u in slot (u - u0) mod 3
+      step(IC<1>{}, IC<0>{}, IC<2>{}, F0{}, u);
+      if (u + 1 < n_qtiles) step(IC<2>{}, IC<1>{}, IC<0>{}, F0{}, u + 1);
+      if (u + 2 < n_qtiles) step(IC<0>{}, IC<2>{}, IC<1>{}, F0{}, u + 2);
+    }
+    // the last tile's contraction, from its slot
+    const int ul = n_qtiles - 1, last = (ul - u0) % 3;
+    if (last == 0) contract(IC<0>{}, ul);
+    else if (last == 1) contract(IC<1>{}, ul);
+    else contract(IC<2>{}, ul);
+    if (krow < N) {
+      if constexpr (RV) store_rows<Tag, D>(dV + head_off + (int64_t)krow * D, acc, half, 1.f);
+      else store_rows<Tag, D>(dK + head_off + (int64_t)krow * D, acc, half, scale);
+    }
   };
-
-  load_rows<D, BNK, W>(K + head_off, nt * BNK, N, kt, wave, lane);
-  load_rows<D, BNK, W>(V + head_off, nt * BNK, N, vt, wave, lane);
-  load_rows<D, kBQ, W>(Qh, u0 * kBQ, N, qbuf(0), wave, lane);      // u0 < n_qtiles: the tile's first key is < N
-  load_rows<D, kBQ, W>(dOh, u0 * kBQ, N, gbuf(0), wave, lane);
-  if (tid < 2 * kBQ) lsd[0][tid / kBQ][tid % kBQ] = fetch_ld(u0);
-  wait_vmcnt<0>();
-  barrier_lds();
-  for (int u = u0; u < n_qtiles; u += 2) {
-    step(IC<0>{}, u);
-    if (u + 1 < n_qtiles) step(IC<1>{}, u + 1);
-  }
-  // The two query halves of a key group hold partial sums of the same dK and dV rows.
-  // Half 1 hands over its dK part and half 0 its dV part through LDS (the tiles are no
-  // longer read: the loop ended on a barrier); then half 0 stores dK and half 1 dV.
-  // Layout: [tensor][key group][16-byte piece i of the lane's accumulators][lane].
-  f32x4* xch = (f32x4*)lds;
-  auto piece = [&](int which, int g, int i) __attribute__((always_inline)) -> f32x4* {
-    return xch + ((which * kKG + g) * (NDB * 4) + i) * 64 + lane;
-  };
-  auto give = [&](const f32x16 (&a)[NDB], int which) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *piece(which, kg, db * 4 + q4) = f32x4{a[db][q4 * 4], a[db][q4 * 4 + 1], a[db][q4 * 4 + 2], a[db][q4 * 4 + 3]};
-  };
-  auto take = [&](f32x16 (&a)[NDB], int which) __attribute__((always_inline)) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 b = *piece(which, kg, db * 4 + q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[db][q4 * 4 + e] += b[e];
-      }
-  };
-  if (qh == 1) give(acck, 0);
-  else give(accv, 1);
-  barrier_lds();
-  if (qh == 0) take(acck, 0);
-  else take(accv, 1);
-  if (krow < N) {
-    if (qh == 0) store_rows<Tag, D>(dK + head_off + (int64_t)krow * D, acck, half, scale);
-    else store_rows<Tag, D>(dV + head_off + (int64_t)krow * D, accv, half, 1.f);
-  }
+  if (qh == 0) run(IC<0>{});
+  else run(IC<1>{});
 }
 
 template <typename Tag, int D, bool CAUSAL>

@@ -178,6 +178,16 @@ __device__ __forceinline__ void dma_load4(const void* gptr, uint32_t lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(gptr), "{m0}"(lds_base) : "memory");
 }
 
+// Both forms with a wave-uniform base address (an SGPR pair) and a 32-bit per-lane byte
+// offset from it: a loop then keeps one offset register per lane instead of a 64-bit
+// address.
+__device__ __forceinline__ void dma_load16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ void dma_load4_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_base) : "memory");
+}
+
 // Workgroup barrier for LDS hand-over only: LDS reads of this wave are complete, then
 // s_barrier. Unlike __syncthreads() it does not drain this wave's outstanding global
 // loads, so a load for a later tile can stay in flight across it.

@@ -79,6 +79,39 @@ __device__ __forceinline__ void load_rows(const uint16_t* src, int r0, int N, ui
   }
 }
 
+// load_rows with a wave-uniform base: each lane's byte offsets within the tile (row and
+// source chunk of its 1 KiB pieces) are set once, then a tile whose rows all lie before N
+// loads from base src + r0 * D; a tile that reaches past N re-reads row N-1 as load_rows
+// does.
+template <int D, int R, int W>
+struct RowPieces {
+  static constexpr int ROW = D * 2, TB = R * ROW, LPW = TB / 1024 / W;
+  static_assert(LPW >= 1 && LPW * 1024 * W == TB, "tile must split into whole 1 KiB loads per wave");
+  static_assert((ROW & (ROW - 1)) == 0, "row length a power of two");
+  uint32_t off[LPW];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int slot = (wave * LPW + i) * 1024 + lane * 16;
+      const int r = slot / ROW, phys = (slot % ROW) / 16;
+      off[i] = r * ROW + ((phys ^ BSwz<D>::f(r)) << 4);
+    }
+  }
+  __device__ __forceinline__ void load(const uint16_t* src, int r0, int N, uint8_t* dst, int wave) const {
+    if (r0 + R <= N) {
+      const uint16_t* base = src + (int64_t)r0 * D;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) dma_load16_s(base, off[i], lds_u32(dst) + (wave * LPW + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int row = min(r0 + (int)(off[i] / ROW), N - 1);
+        dma_load16((const uint8_t*)(src + (int64_t)row * D) + (off[i] % ROW), lds_u32(dst) + (wave * LPW + i) * 1024);
+      }
+    }
+  }
+};
+
 // B operand of the next contraction: 16 fp32 accumulator values -> two groups of 8
 // 16-bit values (accumulator rows 0..7 and 8..15).
 template <typename Tag>

@@ -199,7 +199,7 @@ attn_status_t attn_fwd_fp8_rotq(const void* q, const float* signs, const uint8_t
  * bf16 [B, H, N, d] except lse (fp32 [B, H, N]). Outputs (bf16 [B, H, N, d], round to
  * nearest even): dq, dk, dv, the gradients of sum(dout * O) with respect to q, k, v for
  * O = softmax(scale * q k^T [+ causal mask]) v. workspace is caller-owned device memory
- * of 2 * B * H * N floats; the call overwrites it (per row: dout . o, then lse * log2 e)
+ * of 2 * B * H * N floats; the call overwrites it (per row: -(dout . o), then -lse / scale)
  * and it holds nothing of use afterwards. The products use bf16 operands (P and dS
  * rounded to bf16) with fp32 accumulation. The call enqueues two kernels on `stream`;
  * dq, dk and dv are complete when the second has run. Outputs must not overlap each other,
