@@ -81,15 +81,22 @@ def read_counters(key="hbm_bytes_per_launch"):
         return None
 
 
-def time_launches(torch, fn, steps, warmup, reps=1, between=None):
-    """Run fn() `warmup` times untimed, then time `steps` launches (each a group of `reps`
-    back-to-back calls) with HIP events on the current stream (the stream the library
+def time_launches(torch, fn, steps, warmup, reps=1, between=None, warm_s=0.3):
+    """Run fn() `warmup` times untimed, and then on for at least `warm_s` seconds (in
+    synchronised batches of 8 calls, so that the launch queue stays short), so that the
+    clock has settled under this kernel's load; then time `steps` launches (each a group of
+    `reps` back-to-back calls) with HIP events on the current stream (the stream the library
     launches on). `between`, if given, runs untimed before each timed launch (e.g. a cache
     flush; every launch then has its own event pair). Returns per-call milliseconds: the
     mean over the timed calls, and median / min / std over the launches."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     if between is None:
         # the mean from one event pair around all calls (an event recorded between two
         # calls adds a gap of a few microseconds); then the same number of launches again,
@@ -450,7 +457,7 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     tflops = flops / (ms * 1e-3) / 1e12
-    t = time_launches(torch, step, args.steps, 0)
+    t = time_launches(torch, step, args.steps, 0, warm_s=0.0)
     t["mean_ms"] = ms
 
     out = {
