@@ -62,6 +62,64 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def sample_sclk(torch, fn, seconds=1.5, settle=0.5):
+    """Mean GFX clock of this process's GPU while fn() keeps it busy: amd-smi (a child
+    process) reads the clock of every GFX partition of the device whose PCI address
+    matches torch's device 0, repeatedly for `seconds`, after `settle` seconds of load
+    (the firmware's metrics refresh every few hundred milliseconds, so earlier readings
+    can still show the idle clock), while this thread enqueues fn() in synchronised
+    batches of 64 calls. Returns {"mhz": mean over samples and partitions, "min_mhz",
+    "max_mhz", "samples": n} or {"mhz": None, "why": ...}."""
+    import shutil
+    import subprocess
+    import threading
+
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe):
+        return {"mhz": None, "why": "amd-smi not found"}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}"
+        lst = json.loads(subprocess.run([exe, "list", "--json"], capture_output=True, text=True, timeout=60).stdout)
+        lst = lst if isinstance(lst, list) else lst.get("gpu_data", lst.get("gpus", []))
+        idx = [g["gpu"] for g in lst if str(g.get("bdf", "")).lower().startswith(bdf)]
+    except Exception as e:  # noqa: BLE001 - reported, not raised: the clock is context, not the metric
+        return {"mhz": None, "why": f"device lookup failed: {e!r}"}
+    if len(idx) != 1:
+        return {"mhz": None, "why": f"no unique amd-smi device with PCI address {bdf}"}
+    samples, errs = [], []
+
+    def sampler():
+        time.sleep(settle)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            try:
+                r = subprocess.run([exe, "metric", "-g", str(idx[0]), "--clock", "--json"], capture_output=True,
+                                   text=True, timeout=60)
+                d = json.loads(r.stdout)
+                g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+                vals = [float(v["clk"]["value"]) for k, v in g["clock"].items()
+                        if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+                if vals:
+                    samples.append(vals)
+            except Exception as e:  # noqa: BLE001
+                errs.append(repr(e))
+                return
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    while th.is_alive():
+        for _ in range(64):
+            fn()
+        torch.cuda.synchronize()
+    th.join()
+    if not samples:
+        return {"mhz": None, "why": errs[0] if errs else "no clock sample"}
+    flat = [x for v in samples for x in v]
+    return {"mhz": sum(flat) / len(flat), "min_mhz": min(flat), "max_mhz": max(flat), "samples": len(samples),
+            "amd_smi_gpu": idx[0]}
+
+
 def read_counters(key="hbm_bytes_per_launch"):
     """A figure of the committed rocprofv3 counter summary of the bf16 kernel (HBM bytes per
     launch by default), or None when the summary is missing or was taken on different
@@ -459,6 +517,9 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     t = time_launches(torch, step, args.steps, 0, warm_s=0.0)
     t["mean_ms"] = ms
+    # the clock the chip holds under this call, sampled after the timed region while the
+    # same call keeps running (outside the timed region: it does not enter `value`)
+    clk = sample_sclk(torch, step)
 
     out = {
         "metric": "attention fwd TFLOP/s (bf16, causal, d=128, N=8k) and % of MFMA peak",
@@ -476,6 +537,13 @@ def main():
         "config": {"workload": "bf16 causal attention forward, B=2 H=16 N=8192 d=128", "B": w.B, "H": w.H,
                    "N": w.N, "d": w.d, "causal": True, "flop_per_step": flops},
         "pct_of_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        # the published peak is at 2.4 GHz; at the sampled clock the matrix cores can do
+        # peak * sclk / 2.4 GHz
+        "sclk": {**clk, "source": "amd-smi metric --clock of this GPU, mean over its GFX partitions and over "
+                                  "1.5 s of samples taken after the timed region while the same call kept "
+                                  "running (after 0.5 s of it)",
+                 "pct_of_peak_at_measured_clock": (100.0 * tflops / (PEAK_BF16_TFLOPS * clk["mhz"] / 2400.0)
+                                                   if clk.get("mhz") else None)},
         "launch_us": {**us(t), "what": "mean: the K timed calls (one event pair around them); median, min, std: "
                                         "K more calls, one event pair each (the pairs add a few microseconds per call)"},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
