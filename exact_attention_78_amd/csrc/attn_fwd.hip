@@ -554,21 +554,44 @@ __global__ __launch_bounds__(W * 64, 1) void attn_fwd_kernel(
     if constexpr (FASTP) {
       if (__builtin_amdgcn_ballot_w64(ovf) != 0 && lane == 0) marked = 1;   // redo the tile exactly
     }
-    if (qrow >= N) return pf_out;
-    const float inv = 1.0f / l_tot;
-    uint16_t* Orow = O + head_off + (int64_t)qrow * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = db * 32 + g * 8 + half * 4;
-        const f32x16 a = oacc[db];
-        u32x2 w = {pack2(Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv),
+    const float inv = 1.0f / l_tot;                   // (rows past N are not stored)
+    // this lane's 4 consecutive head dims db * 32 + g * 8 + half * 4 .. + 3 of row qrow
+    auto o_piece = [&](int db, int g) __attribute__((always_inline)) -> u32x2 {
+      const f32x16 a = oacc[db];
+      return u32x2{pack2(Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv),
                    pack2(Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
-        *(u32x2*)(Orow + d) = w;
+    };
+    if constexpr (!PERSIST) {
+      // O through LDS, so that the stores write whole rows: stored from the accumulators,
+      // every instruction would put 16 bytes into each of 32 rows. Each wave stages its 32
+      // rows (row-major, 16-byte chunk c of row r at chunk c ^ (r mod chunks per row)) in
+      // its own 32 * ROW bytes, then stores 16 bytes per lane, 1 KiB of consecutive rows
+      // per instruction. Every wave has waited for its own loads above; after the barrier
+      // no load is in flight into the rings and no wave reads them any more.
+      barrier_lds();
+      constexpr int NCH = ROW / 16;                   // 16-byte chunks per row
+      uint8_t* stg = lds + wave * 32 * ROW;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(u32x2*)(stg + l32 * ROW + (((db * 4 + g) ^ (l32 % NCH)) << 4) + half * 8) = o_piece(db, g);
+      uint8_t* Ow = (uint8_t*)(O + head_off + (int64_t)q0 * D);   // the wave's 32 rows, contiguous
+#pragma unroll
+      for (int i = 0; i < 32 * ROW / 1024; ++i) {
+        const int off = i * 1024 + lane * 16, r = off / ROW, ch = (off % ROW) / 16;
+        const u32x4 x = *(const u32x4*)(stg + r * ROW + ((ch ^ (r % NCH)) << 4));
+        if (q0 + r < N) *(u32x4*)(Ow + off) = x;
       }
+    } else if (qrow < N) {
+      uint16_t* Orow = O + head_off + (int64_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *(u32x2*)(Orow + db * 32 + g * 8 + half * 4) = o_piece(db, g);
+    }
     const float lse = (M + __builtin_log2f(l_tot)) * kLn2;   // (a marked tile's O and LSE are rewritten)
-    if (half == 0) LSE[(int64_t)bh * N + qrow] = lse;
+    if (qrow < N && half == 0) LSE[(int64_t)bh * N + qrow] = lse;
     return pf_out;
   };
   // A tile that the fast pass marked is redone at once by the exact pass, in the same
