@@ -170,7 +170,9 @@ __global__ __launch_bounds__(kWq * 64, 1) void attn_bwd_dq_kernel(
     step(IC<0>{}, t);
     if (t + 1 < T) step(IC<1>{}, t + 1);
   }
-  if (qrow < N) store_rows<Tag, D>(dQ + head_off + (int64_t)qrow * D, acc, half, scale);
+  // the loop ended on a barrier with no load in flight: the K/V slots are free for staging
+  static_assert(W * 32 * D * 2 <= 4 * TB, "the staged rows fit the tiles' LDS");
+  store_rows_staged<Tag, D>(dQ + head_off + (int64_t)q0 * D, N - q0, acc, lane, scale, lds + wave * 32 * D * 2);
 }
 
 template <typename Tag, int D, bool CAUSAL>
@@ -372,10 +374,11 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
     if (last == 0) contract(IC<0>{}, ul);
     else if (last == 1) contract(IC<1>{}, ul);
     else contract(IC<2>{}, ul);
-    if (krow < N) {
-      if constexpr (RV) store_rows<Tag, D>(dV + head_off + (int64_t)krow * D, acc, half, 1.f);
-      else store_rows<Tag, D>(dK + head_off + (int64_t)krow * D, acc, half, scale);
-    }
+    barrier_lds();                                  // every wave has read the rings and xch
+    static_assert(W * 32 * D * 2 <= 2 * NS * TB, "the staged rows fit the rings");
+    uint8_t* stg = lds + wave * 32 * D * 2;
+    if constexpr (RV) store_rows_staged<Tag, D>(dV + head_off + (int64_t)k0 * D, N - k0, acc, lane, 1.f, stg);
+    else store_rows_staged<Tag, D>(dK + head_off + (int64_t)k0 * D, N - k0, acc, lane, scale, stg);
   };
   if (qh == 0) run(IC<0>{});
   else run(IC<1>{});

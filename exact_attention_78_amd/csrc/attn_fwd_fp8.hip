@@ -583,20 +583,33 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
   if (pend) rescale();
 
   const float l_tot = add_halves(l_part) * (1.f / (1 << (int)kPShift));   // sum of probabilities
-  if (qrow >= N) return;
-  const float inv = U / l_rnd;
-  uint16_t* Orow = O + head_off + (int64_t)qrow * D;
+  const float inv = U / l_rnd;                       // (rows past N are not stored)
+  // O (bf16) through LDS, so that the stores write whole rows: each wave stages its 32 rows
+  // (row-major, 16-byte chunk c of row r at chunk c ^ (r mod chunks per row)) in its own
+  // 32 * OROW bytes of the rings, then stores 16 bytes per lane, 1 KiB of consecutive rows
+  // per instruction. Every wave has waited for its own loads above; after the barrier no
+  // load is in flight into the rings and no wave reads them any more.
+  constexpr int OROW = D * 2, NCH = OROW / 16;
+  static_assert(kWaves * 32 * OROW <= 2 * NS * TB, "the staged rows fit the rings");
+  barrier_lds();
+  uint8_t* stg = lds + wave * 32 * OROW;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int d = db * 32 + g * 8 + half * 4;
       const f32x16 a = oacc[db];
-      u32x2 w = {pack2(Bf16Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv),
-                 pack2(Bf16Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
-      *(u32x2*)(Orow + d) = w;
+      *(u32x2*)(stg + l32 * OROW + (((db * 4 + g) ^ (l32 % NCH)) << 4) + half * 8) =
+          u32x2{pack2(Bf16Tag{}, a[g * 4 + 0] * inv, a[g * 4 + 1] * inv),
+                pack2(Bf16Tag{}, a[g * 4 + 2] * inv, a[g * 4 + 3] * inv)};
     }
-  if (half == 0) LSE[(int64_t)bh * N + qrow] = (M + __builtin_log2f(l_tot)) * kLn2;
+  uint8_t* Ow = (uint8_t*)(O + head_off + (int64_t)q0 * D);   // the wave's 32 rows, contiguous
+#pragma unroll
+  for (int i = 0; i < 32 * OROW / 1024; ++i) {
+    const int off = i * 1024 + lane * 16, r = off / OROW, ch = (off % OROW) / 16;
+    const u32x4 x = *(const u32x4*)(stg + r * OROW + ((ch ^ (r % NCH)) << 4));
+    if (q0 + r < N) *(u32x4*)(Ow + off) = x;
+  }
+  if (qrow < N && half == 0) LSE[(int64_t)bh * N + qrow] = (M + __builtin_log2f(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool FUSEQ>

@@ -1,7 +1,8 @@
 // LDS tiles of 16-bit rows shared by the backward and decode kernels: one chunk swizzle
 // that serves both row reads and transpose reads, the per-lane addresses of both read
-// patterns for 32x32x16 MFMA operands, direct global->LDS tile loads, and packing of
-// fp32 accumulators into the 16-bit B operand of the next contraction.
+// patterns for 32x32x16 MFMA operands, direct global->LDS tile loads, packing of fp32
+// accumulators into the 16-bit B operand of the next contraction, and row stores through
+// LDS.
 #pragma once
 
 #include "device_common.h"
@@ -122,20 +123,32 @@ __device__ __forceinline__ void pack16(const float (&x)[16], u32x4 (&p)[2]) {
                  pack2(Tag{}, x[h * 8 + 4], x[h * 8 + 5]), pack2(Tag{}, x[h * 8 + 6], x[h * 8 + 7])};
 }
 
-// Store 32 x D accumulators (lane: one row of the result; head dims 8 * (r / 4) + 4 * half
-// + r % 4 of each block) times `mul` as 16-bit values.
+// Store 32 x D accumulators (lane pair l32, l32 + 32: one row of the result; head dims
+// 8 * (r / 4) + 4 * half + r % 4 of each block) times `mul` as 16-bit values, through LDS
+// so that the stores write whole rows: the wave's 32 rows are staged in stg (32 * D * 2
+// bytes, 16-byte chunk c of row r at chunk c ^ (r mod chunks per row)), then written with
+// 16-byte stores, 1 KiB of consecutive rows per instruction, to dst0 (the first of the 32
+// rows, which are contiguous); rows from nvalid on are not written. The caller makes stg
+// free for this wave (a barrier).
 template <typename Tag, int D>
-__device__ __forceinline__ void store_rows(uint16_t* dst_row, const f32x16 (&acc)[D / 32], int half, float mul) {
+__device__ __forceinline__ void store_rows_staged(uint16_t* dst0, int nvalid, const f32x16 (&acc)[D / 32], int lane,
+                                                  float mul, uint8_t* stg) {
+  constexpr int ROW = D * 2, NCH = ROW / 16;
+  const int half = lane / 32, l32 = lane % 32;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int d = db * 32 + g * 8 + half * 4;
       const f32x16 a = acc[db];
-      u32x2 w = {pack2(Tag{}, a[g * 4 + 0] * mul, a[g * 4 + 1] * mul),
-                 pack2(Tag{}, a[g * 4 + 2] * mul, a[g * 4 + 3] * mul)};
-      *(u32x2*)(dst_row + d) = w;
+      *(u32x2*)(stg + l32 * ROW + (((db * 4 + g) ^ (l32 % NCH)) << 4) + half * 8) =
+          u32x2{pack2(Tag{}, a[g * 4 + 0] * mul, a[g * 4 + 1] * mul), pack2(Tag{}, a[g * 4 + 2] * mul, a[g * 4 + 3] * mul)};
     }
+#pragma unroll
+  for (int i = 0; i < 32 * ROW / 1024; ++i) {
+    const int off = i * 1024 + lane * 16, r = off / ROW, ch = (off % ROW) / 16;
+    const u32x4 x = *(const u32x4*)(stg + r * ROW + ((ch ^ (r % NCH)) << 4));
+    if (r < nvalid) *(u32x4*)((uint8_t*)dst0 + off) = x;
+  }
 }
 
 // B-operand fragments of one row (this lane's) of a [N, D] tensor: head-dim step s holds
