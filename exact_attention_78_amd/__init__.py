@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     queue_workspace,
     attn_quant_fp8,
     attn_quant_fp8_kv,
+    attn_quant_fp8_qkv,
     bwd,
     fwd,
     library,

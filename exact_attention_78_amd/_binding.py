@@ -32,6 +32,7 @@ SIGNATURES = {
     "attn_fwd_fp8": [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_quant_fp8": [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P],
     "attn_quant_fp8_kv": [_P] * 7 + [_I64, _I64, _I64, _I64, _P],
+    "attn_quant_fp8_qkv": [_P] * 10 + [_I64, _I64, _I64, _I64, _P],
     "attn_fwd_fp8_rotq": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_bwd_bf16": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
     "attn_bwd_f16": [_P] * 10 + [_I64, _I64, _I64, _I64, _INT, _F32, _P],
@@ -379,6 +380,33 @@ def attn_quant_fp8_kv(k, v, signs, k8=None, v8=None, k_scale=None, v_scale=None)
                                          _stream(k))
     _check("attn_quant_fp8_kv", st)
     return outs[0], outs[2], outs[1], outs[3]
+
+
+def attn_quant_fp8_qkv(q, k, v, signs, q8=None, k8=None, v8=None, q_scale=None, k_scale=None, v_scale=None):
+    """Quantise Q and K (rotated with ``signs``) and V (unrotated) in one launch; returns
+    (q8, q_scale, k8, k_scale, v8, v_scale) as three attn_quant_fp8 calls would."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.bfloat16 and t.dim() == 4
+                 and t.is_contiguous() and t.shape == q.shape and t.device == q.device,
+                 f"{name} must be a contiguous bf16 [B, H, N, d] GPU tensor like q")
+    B, H, N, d = q.shape
+    nblk = (N + 127) // 128
+    _require(isinstance(signs, torch.Tensor) and signs.dtype == torch.float32 and signs.shape == (d,)
+             and signs.is_contiguous() and signs.device == q.device, "signs must be fp32 [d] on q's device")
+    outs = []
+    for name, t, shape, dt in (("q8", q8, (B, H, N, d), torch.uint8), ("k8", k8, (B, H, N, d), torch.uint8),
+                               ("v8", v8, (B, H, N, d), torch.uint8),
+                               ("q_scale", q_scale, (B, H, nblk), torch.float32),
+                               ("k_scale", k_scale, (B, H, nblk), torch.float32),
+                               ("v_scale", v_scale, (B, H, nblk), torch.float32)):
+        t = torch.empty(shape, dtype=dt, device=q.device) if t is None else t
+        _require(t.shape == shape and t.dtype == dt and t.is_contiguous() and t.device == q.device, f"bad {name}")
+        outs.append(t)
+    with torch.cuda.device(q.device):
+        st = library().attn_quant_fp8_qkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), signs.data_ptr(),
+                                          *(t.data_ptr() for t in outs), B, H, N, d, _stream(q))
+    _check("attn_quant_fp8_qkv", st)
+    return outs[0], outs[3], outs[1], outs[4], outs[2], outs[5]
 
 
 def attn_fwd_fp8_rotq(q, signs, k8, v8, k_scale, v_scale, causal=False, scale=None, out=None, lse=None,

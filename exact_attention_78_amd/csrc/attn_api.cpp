@@ -123,6 +123,42 @@ attn_status_t check_decode(const void* q, const void* k, const void* v, const vo
   return ATTN_OK;
 }
 
+// Shared by the one-launch quantisers: nt = 2 (K, V) or 3 (Q, K, V) bf16 inputs x[i] of one
+// shape, the signs, and their codes x8[i] and scales sc[i]; every pointer non-null and
+// 16-byte aligned, no output overlapping an input or another output.
+attn_status_t quant_multi(int nt, const void* const* x, const float* signs, uint8_t* const* x8, float* const* sc,
+                          int64_t B, int64_t H, int64_t N, int64_t d, void* stream) {
+  if (!signs || !aligned16(signs)) return ATTN_ERR_INVALID_ARG;
+  for (int i = 0; i < nt; ++i)
+    if (!x[i] || !x8[i] || !sc[i] || !aligned16(x[i]) || !aligned16(x8[i]) || !aligned16(sc[i]))
+      return ATTN_ERR_INVALID_ARG;
+  int64_t elems, rows;
+  attn_status_t st = check_shape(B, H, N, d, &elems, &rows);
+  if (st != ATTN_OK) return st;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (nt * attn::max_workgroups_quant(B * H, N) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  const int64_t nblk = (N + 127) / 128;
+  const uintptr_t sb = (uintptr_t)(B * H * nblk) * sizeof(float);
+  auto span = [](const void* p, uintptr_t n) { return Range{(uintptr_t)p, (uintptr_t)p + n}; };
+  Range ins[4], outs[6];
+  int ni = 0, no = 0;
+  ins[ni++] = span(signs, (uintptr_t)d * sizeof(float));
+  for (int i = 0; i < nt; ++i) {
+    ins[ni++] = span(x[i], (uintptr_t)elems * 2);
+    outs[no++] = span(x8[i], (uintptr_t)elems);
+    outs[no++] = span(sc[i], sb);
+  }
+  for (int i = 0; i < no; ++i) {
+    for (int j = 0; j < ni; ++j)
+      if (overlaps(outs[i], ins[j])) return ATTN_ERR_INVALID_ARG;
+    for (int j = i + 1; j < no; ++j)
+      if (overlaps(outs[i], outs[j])) return ATTN_ERR_INVALID_ARG;
+  }
+  const int o = nt == 3 ? 1 : 0;                    // index of K
+  return from_hip(attn::launch_quant_fp8_qkv(nt == 3 ? x[0] : nullptr, x[o], x[o + 1], nt == 3 ? x8[0] : nullptr,
+                                             x8[o], x8[o + 1], nt == 3 ? sc[0] : nullptr, sc[o], sc[o + 1], signs,
+                                             B * H, N, d, (hipStream_t)stream));
+}
 }  // namespace
 
 extern "C" {
@@ -228,29 +264,19 @@ attn_status_t attn_quant_fp8(const void* x, uint8_t* x8, float* scales, const fl
 attn_status_t attn_quant_fp8_kv(const void* k, const void* v, const float* signs, uint8_t* k8, uint8_t* v8,
                                 float* k_scale, float* v_scale, int64_t B, int64_t H, int64_t N, int64_t d,
                                 void* stream) {
-  if (!k || !v || !signs || !k8 || !v8 || !k_scale || !v_scale) return ATTN_ERR_INVALID_ARG;
-  int64_t elems, rows;
-  attn_status_t st = check_shape(B, H, N, d, &elems, &rows);
-  if (st != ATTN_OK) return st;
-  const void* ptrs[7] = {k, v, signs, k8, v8, k_scale, v_scale};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return ATTN_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if (2 * attn::max_workgroups_quant(B * H, N) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
-  const int64_t nblk = (N + 127) / 128;
-  const uintptr_t sb = (uintptr_t)(B * H * nblk) * sizeof(float);
-  auto span = [](const void* p, uintptr_t n) { return Range{(uintptr_t)p, (uintptr_t)p + n}; };
-  const Range ins[3] = {span(k, (uintptr_t)elems * 2), span(v, (uintptr_t)elems * 2),
-                        span(signs, (uintptr_t)d * sizeof(float))};
-  const Range outs[4] = {span(k8, (uintptr_t)elems), span(v8, (uintptr_t)elems), span(k_scale, sb),
-                         span(v_scale, sb)};
-  for (int i = 0; i < 4; ++i) {
-    for (const Range& r : ins)
-      if (overlaps(outs[i], r)) return ATTN_ERR_INVALID_ARG;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlaps(outs[i], outs[j])) return ATTN_ERR_INVALID_ARG;
-  }
-  return from_hip(attn::launch_quant_fp8_kv(k, v, k8, v8, k_scale, v_scale, signs, B * H, N, d, (hipStream_t)stream));
+  const void* x[2] = {k, v};
+  uint8_t* x8[2] = {k8, v8};
+  float* sc[2] = {k_scale, v_scale};
+  return quant_multi(2, x, signs, x8, sc, B, H, N, d, stream);
+}
+
+attn_status_t attn_quant_fp8_qkv(const void* q, const void* k, const void* v, const float* signs, uint8_t* q8,
+                                 uint8_t* k8, uint8_t* v8, float* q_scale, float* k_scale, float* v_scale, int64_t B,
+                                 int64_t H, int64_t N, int64_t d, void* stream) {
+  const void* x[3] = {q, k, v};
+  uint8_t* x8[3] = {q8, k8, v8};
+  float* sc[3] = {q_scale, k_scale, v_scale};
+  return quant_multi(3, x, signs, x8, sc, B, H, N, d, stream);
 }
 
 attn_status_t attn_fwd_fp8_rotq(const void* q, const float* signs, const uint8_t* k8, const uint8_t* v8,

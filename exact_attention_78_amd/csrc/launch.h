@@ -29,9 +29,10 @@ hipError_t launch_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v
                           float scale, hipStream_t stream);
 hipError_t launch_quant_fp8(const void* x, uint8_t* x8, float* scales, const float* signs, int64_t BH, int64_t N,
                             int64_t d, hipStream_t stream);
-hipError_t launch_quant_fp8_kv(const void* k, const void* v, uint8_t* k8, uint8_t* v8, float* k_scales,
-                               float* v_scales, const float* signs, int64_t BH, int64_t N, int64_t d,
-                               hipStream_t stream);
+// Q (rotated; skipped when q is null), K (rotated) and V (unrotated) in one launch.
+hipError_t launch_quant_fp8_qkv(const void* q, const void* k, const void* v, uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                                float* q_scales, float* k_scales, float* v_scales, const float* signs, int64_t BH,
+                                int64_t N, int64_t d, hipStream_t stream);
 hipError_t launch_fwd_fp8_rotq(const void* q, const float* signs, const uint8_t* k8, const uint8_t* v8,
                                const float* sk, const float* sv, void* o, float* lse, uint8_t* q8_out, float* sq_out,
                                int64_t BH, int64_t N, int64_t d, bool causal, float scale, hipStream_t stream);

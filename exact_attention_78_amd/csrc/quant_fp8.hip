@@ -167,20 +167,23 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __r
   quant_block<D, ROTATE>(X, X8, scales, signs, N, nblk, inv_sqrt_d, blockIdx.x, wave_max);
 }
 
-// K (rotated) and V (unrotated) of one attention call in one launch: the first BH * nblk
-// workgroups take K's blocks, the rest V's.
+// Q (rotated, when nq = 1), K (rotated) and V (unrotated) of one attention call in one
+// launch: in blocks of n_wg = BH * nblk workgroups, Q's blocks first (nq = 1), then K's,
+// then V's.
 template <int D>
-__global__ __launch_bounds__(kThreads) void quant_fp8_kv_kernel(const uint16_t* __restrict__ K,
-                                                                const uint16_t* __restrict__ V,
-                                                                uint8_t* __restrict__ K8, uint8_t* __restrict__ V8,
-                                                                float* __restrict__ sk, float* __restrict__ sv,
-                                                                const float* __restrict__ signs, int N, int nblk,
-                                                                int n_wg_k, float inv_sqrt_d) {
+__global__ __launch_bounds__(kThreads) void quant_fp8_qkv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint8_t* __restrict__ Q8, uint8_t* __restrict__ K8, uint8_t* __restrict__ V8, float* __restrict__ sq,
+    float* __restrict__ sk, float* __restrict__ sv, const float* __restrict__ signs, int N, int nblk, int n_wg, int nq,
+    float inv_sqrt_d) {
   __shared__ float wave_max[kThreads / 64];
-  if ((int)blockIdx.x < n_wg_k)
-    quant_block<D, true>(K, K8, sk, signs, N, nblk, inv_sqrt_d, blockIdx.x, wave_max);
+  const int wg = blockIdx.x, t = wg / n_wg + (nq ? 0 : 1);   // 0 Q (only when nq = 1), 1 K, 2 V
+  if (t == 0)
+    quant_block<D, true>(Q, Q8, sq, signs, N, nblk, inv_sqrt_d, wg % n_wg, wave_max);
+  else if (t == 1)
+    quant_block<D, true>(K, K8, sk, signs, N, nblk, inv_sqrt_d, wg % n_wg, wave_max);
   else
-    quant_block<D, false>(V, V8, sv, nullptr, N, nblk, inv_sqrt_d, blockIdx.x - n_wg_k, wave_max);
+    quant_block<D, false>(V, V8, sv, nullptr, N, nblk, inv_sqrt_d, wg % n_wg, wave_max);
 }
 
 template <int D>
@@ -199,24 +202,25 @@ hipError_t launch(const void* x, uint8_t* x8, float* sc, const float* signs, int
 }
 
 template <int D>
-hipError_t launch_kv(const void* k, const void* v, uint8_t* k8, uint8_t* v8, float* sk, float* sv, const float* signs,
-                     int64_t BH, int64_t N, hipStream_t stream) {
+hipError_t launch_qkv(const void* q, const void* k, const void* v, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* sq,
+                      float* sk, float* sv, const float* signs, int64_t BH, int64_t N, hipStream_t stream) {
   const int nblk = (int)((N + kRowsPerBlock - 1) / kRowsPerBlock);
   const float inv_sqrt_d = (float)(1.0 / __builtin_sqrt((double)D));
   const int64_t n_wg = BH * nblk;
-  hipLaunchKernelGGL((quant_fp8_kv_kernel<D>), dim3((unsigned)(2 * n_wg)), dim3(kThreads), 0, stream,
-                     (const uint16_t*)k, (const uint16_t*)v, k8, v8, sk, sv, signs, (int)N, nblk, (int)n_wg,
-                     inv_sqrt_d);
+  const int nq = q != nullptr ? 1 : 0;
+  hipLaunchKernelGGL((quant_fp8_qkv_kernel<D>), dim3((unsigned)((2 + nq) * n_wg)), dim3(kThreads), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, q8, k8, v8, sq, sk, sv, signs, (int)N,
+                     nblk, (int)n_wg, nq, inv_sqrt_d);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_quant_fp8_kv(const void* k, const void* v, uint8_t* k8, uint8_t* v8, float* k_scales,
-                               float* v_scales, const float* signs, int64_t BH, int64_t N, int64_t d,
-                               hipStream_t stream) {
-  return d == 128 ? launch_kv<128>(k, v, k8, v8, k_scales, v_scales, signs, BH, N, stream)
-                  : launch_kv<64>(k, v, k8, v8, k_scales, v_scales, signs, BH, N, stream);
+hipError_t launch_quant_fp8_qkv(const void* q, const void* k, const void* v, uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                                float* q_scales, float* k_scales, float* v_scales, const float* signs, int64_t BH,
+                                int64_t N, int64_t d, hipStream_t stream) {
+  return d == 128 ? launch_qkv<128>(q, k, v, q8, k8, v8, q_scales, k_scales, v_scales, signs, BH, N, stream)
+                  : launch_qkv<64>(q, k, v, q8, k8, v8, q_scales, k_scales, v_scales, signs, BH, N, stream);
 }
 
 hipError_t launch_quant_fp8(const void* x, uint8_t* x8, float* scales, const float* signs, int64_t BH, int64_t N,

@@ -175,6 +175,16 @@ attn_status_t attn_quant_fp8_kv(const void* k, const void* v, const float* signs
                                 float* k_scale, float* v_scale, int64_t B, int64_t H, int64_t N, int64_t d,
                                 void* stream);
 
+/* Q, K and V preparation of one fp8 attention call in a single launch ("8.3
+ * FlashAttention-3", sections 5.1 and 5.2, as attn_quant_fp8): q and k (bf16 [B, H, N, d])
+ * rotated with `signs` and quantised, v quantised unrotated, each exactly as
+ * attn_quant_fp8(q, signs), attn_quant_fp8(k, signs) and attn_quant_fp8(v, NULL) would (same
+ * codes and scales), with one launch's start and end instead of three. signs must not be
+ * NULL. Outputs must not overlap each other or the inputs. */
+attn_status_t attn_quant_fp8_qkv(const void* q, const void* k, const void* v, const float* signs, uint8_t* q8,
+                                 uint8_t* k8, uint8_t* v8, float* q_scale, float* k_scale, float* v_scale,
+                                 int64_t B, int64_t H, int64_t N, int64_t d, void* stream);
+
 /* fp8 attention with the preparation of Q fused into the attention kernel ("8.3
  * FlashAttention-3", section 5.2: the Hadamard rotation is folded into the preprocessing
  * the kernel already does, at almost no extra cost). q is bf16 [B, H, N, d] (d = 64, 128);

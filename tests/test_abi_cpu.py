@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported_and_bound(lib):
     names = header_functions()
     assert set(names) == {"attn_fwd_bf16", "attn_fwd_f16", "attn_fwd_f32", "attn_fwd_fp8", "attn_quant_fp8",
                           "attn_fwd_variant", "attn_calibrate", "attn_calibrate_ops", "attn_decode_bf16_noalloc",
-                          "attn_quant_fp8_kv", "attn_fwd_fp8_rotq",
+                          "attn_quant_fp8_kv", "attn_quant_fp8_qkv", "attn_fwd_fp8_rotq",
                           "attn_bwd_bf16", "attn_bwd_f16", "attn_decode_bf16", "attn_decode_f16",
                           "attn_decode_workspace_floats", "attn_status_string", "attn_abi_version"}
     for n in names:
@@ -121,6 +121,20 @@ def test_quant_kv_validation(lib, defect, expect):
     args = dict(k=A[0], v=A[1], signs=A[2], k8=A[3], v8=A[4], sk=A[5], sv=A[6], B=1, H=1, N=256, d=128)
     args.update(defect)
     assert lib.attn_quant_fp8_kv(*args.values(), None) == expect
+
+
+@no_gpu_only
+@pytest.mark.parametrize("defect,expect", [
+    (dict(q=None), INVALID), (dict(v=None), INVALID), (dict(signs=None), INVALID), (dict(q8=None), INVALID),
+    (dict(sv=None), INVALID), (dict(d=96), UNSUPPORTED), (dict(N=0), INVALID), (dict(q8=A[0]), INVALID),
+    (dict(k8=A[1]), INVALID), (dict(v8=A[4]), INVALID), (dict(sq=A[8]), INVALID), (dict(sk=A[7] + 4), INVALID),
+    (dict(signs=A[3] + 4), INVALID), (dict(sv=A[3]), INVALID),
+])
+def test_quant_qkv_validation(lib, defect, expect):
+    args = dict(q=A[0], k=A[1], v=A[2], signs=A[3], q8=A[4], k8=A[5], v8=A[6], sq=A[7], sk=A[8], sv=A[9], B=1, H=1,
+                N=256, d=128)
+    args.update(defect)
+    assert lib.attn_quant_fp8_qkv(*args.values(), None) == expect
 
 
 @no_gpu_only

@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_78_amd import attn_fwd_fp8, attn_fwd_fp8_rotq, attn_quant_fp8, attn_quant_fp8_kv, inputs
+from exact_attention_78_amd import (attn_fwd_fp8, attn_fwd_fp8_rotq, attn_quant_fp8, attn_quant_fp8_kv,
+                                   attn_quant_fp8_qkv, inputs)
 from oracle import fp8 as ofp8
 from oracle.attention import attention_forward
 from oracle.pool import forward_pooled
@@ -320,6 +321,36 @@ def test_quant_kv_one_launch_bit_exact(N, d):
     rv, rsv = ofp8.quantize_blocks(vx)
     for got, ref in ((k8, rk), (sk, rsk), (v8, rv), (sv, rsv)):
         np.testing.assert_array_equal(got.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("N", [300, 1000, 1])
+def test_quant_qkv_one_launch_bit_exact(N, d):
+    # Q and K rotated and V unrotated in one launch: the codes and scales of the oracle's
+    # quantiser for each
+    say(f"case quant qkv N={N} d={d}")
+    q, k, v, signs = inputs.draw_fp8_workload(31 + N % 5, 2, 3, N, d)
+    (tq, qx), (tk, kx), (tv, vx) = (bf16_activations(t) for t in (q, k, v))
+    outs = attn_quant_fp8_qkv(tq.cuda(), tk.cuda(), tv.cuda(), torch.from_numpy(signs).cuda())
+    torch.cuda.synchronize()
+    refs = (*ofp8.quantize_blocks(ofp8.rotate_f32(qx, signs)), *ofp8.quantize_blocks(ofp8.rotate_f32(kx, signs)),
+            *ofp8.quantize_blocks(vx))
+    for got, ref in zip(outs, refs):
+        np.testing.assert_array_equal(got.cpu().numpy(), ref)
+
+
+def test_quant_qkv_full_size_equals_three_launches():
+    # The fp8 workload's shape: one launch gives the bytes of the three single-tensor calls
+    w = inputs.WORKLOADS["C5"]
+    say("case quant qkv C5 vs three attn_quant_fp8 calls")
+    q, k, v, signs = inputs.draw_fp8_workload(w.wid, w.B, w.H, w.N, w.d)
+    tq, tk, tv = (inputs.to_torch(x, "bf16").cuda() for x in (q, k, v))
+    sg = torch.from_numpy(signs).cuda()
+    one = attn_quant_fp8_qkv(tq, tk, tv, sg)
+    three = (*attn_quant_fp8(tq, sg), *attn_quant_fp8(tk, sg), *attn_quant_fp8(tv, None))
+    torch.cuda.synchronize()
+    for a, b in zip(one, three):
+        assert torch.equal(a, b)
 
 
 def fused_case(wid, B, H, N, d, tweak=None):
