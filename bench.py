@@ -74,6 +74,9 @@ def sample_sclk(torch, fn, seconds=1.5, settle=0.5):
     import subprocess
     import threading
 
+    if any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        # a profiler's preloaded library would initialise the GPU in the child before amd-smi starts
+        return {"mhz": None, "why": "not sampled under rocprofv3"}
     exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
     if not os.path.exists(exe):
         return {"mhz": None, "why": "amd-smi not found"}
