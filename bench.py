@@ -245,6 +245,15 @@ def calibration_leg(torch, ea):
     res["read_loop"] = {"value": rate(nbytes, t, 1e9), "unit": "GB/s", "us": t["mean_ms"] * 1e3, "bytes": nbytes,
                         "frac_of_published_hbm": rate(nbytes, t, 1e9) / PEAK_HBM_GBS}
     del buf, out
+    # LDS read rate, one workgroup of 8 waves per CU: 16-byte reads and the 8-byte transpose
+    # reads that feed the attention kernels' V^T (and backward Q^T, dO^T) operands
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for kind, what in (("lds_b128", "ds_read_b128, 16 bytes per lane"),
+                       ("lds_tr_b64", "ds_read_b64_tr_b16, 8 bytes per lane")):
+        out, nb = ea.attn_calibrate(kind, cus, 2000)
+        t = time_launches(torch, lambda: ea.attn_calibrate(kind, cus, 2000, out=out), 5, 3)
+        res[f"{kind}_loop"] = {"value": rate(nb, t, 1e9), "unit": "GB/s", "bytes_per_cu_per_ns": rate(nb, t, 1e9) / cus,
+                               "what": what}
     return res
 
 

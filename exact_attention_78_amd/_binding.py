@@ -172,13 +172,13 @@ def attn_fwd_variant(q, k, v, causal=False, scale=None, sched="default", passes=
 # attn_calibrate kinds (see attn.h): the dense loops, and MFMA loops with the kernels' mix
 # of work between MFMAs (one fma, exp and add each; LDS reads per MFMA; waves per SIMD)
 CALIBRATION_KINDS = {"mfma": 0, "exp": 1, "mix_lds1_2w": 2, "mix_lds0.5_2w": 3, "mix_lds0.5_1w": 4,
-                     "mix_nolds_2w": 5, "read": 6}
+                     "mix_nolds_2w": 5, "read": 6, "lds_b128": 7, "lds_tr_b64": 8}
 
 
 def attn_calibrate(kind, workgroups, iters, seed=None, out=None):
     """Launch a calibration loop (a key of CALIBRATION_KINDS) on the current stream; returns
     the output tensor and the operations it performs (FLOPs, exponentials for "exp", bytes
-    read for "read"). For "read", ``seed`` is the buffer the loop streams through
+    read for "read" and the LDS kinds). For "read", ``seed`` is the buffer the loop streams through
     (workgroups * 256 * iters 16-byte elements; zeros of that size by default)."""
     k = CALIBRATION_KINDS[kind]
     dev = torch.device("cuda", torch.cuda.current_device())

@@ -362,7 +362,7 @@ attn_status_t attn_decode_f16(const void* q, const void* k, const void* v, void*
 
 attn_status_t attn_calibrate(int kind, const uint32_t* seed, float* out, int64_t workgroups, int iters,
                              void* stream) {
-  if (kind < 0 || kind > 6 || !seed || !out || workgroups < 1 || workgroups > INT32_MAX || iters < 1)
+  if (kind < 0 || kind > 8 || !seed || !out || workgroups < 1 || workgroups > INT32_MAX || iters < 1)
     return ATTN_ERR_INVALID_ARG;
   // kind 6 reads workgroups * 256 * iters 16-byte elements from seed: the count must fit
   // the kernel's int64 indexing
@@ -372,7 +372,7 @@ attn_status_t attn_calibrate(int kind, const uint32_t* seed, float* out, int64_t
 }
 
 int64_t attn_calibrate_ops(int kind, int iters) {
-  if (kind < 0 || kind > 6 || iters < 1) return -1;
+  if (kind < 0 || kind > 8 || iters < 1) return -1;
   return attn::calib_ops_per_workgroup(kind, iters);
 }
 

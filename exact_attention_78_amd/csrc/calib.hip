@@ -124,6 +124,38 @@ __global__ __launch_bounds__(kReadThreads) void calib_read_kernel(const u32x4* _
   out[(int64_t)blockIdx.x * kReadThreads + threadIdx.x] = (float)acc;
 }
 
+// LDS read rate (kinds 7, 8): 8 waves per workgroup (the 128 KiB of LDS keep one
+// workgroup per CU), each lane reading 16 bytes (ds_read_b128, TR
+// false) or 8 bytes (ds_read_b64_tr_b16, TR true: the transpose reads that give the
+// attention kernels their V^T and Q^T / dO^T operands) per instruction, 16 instructions per
+// iteration, from addresses that put the 64 lanes on distinct banks. The values are
+// XOR-accumulated, so that no read is dead, and the result is written as a small integer
+// (a finite float).
+template <bool TR>
+__global__ __launch_bounds__(kCalWaves * 64, 1) void calib_lds_kernel(const uint32_t* __restrict__ seed, float* out,
+                                                                     int iters) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[131072];
+  for (int i = threadIdx.x; i < 131072 / 4; i += kCalWaves * 64) ((uint32_t*)lds)[i] = seed[i % 4] + i;
+  __syncthreads();
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      // lane * 16 + 15 * 1024 + 7 * 16384 + 16 <= 131072: inside the array
+      const uint8_t* p = lds + lane * 16 + ((m + wave) % 16) * 1024 + (it & 7) * 16384;
+      if constexpr (TR) {
+        const u32x2 v = lds_read_tr16((const uint16_t*)p);
+        acc ^= v[0] ^ v[1];
+      } else {
+        const u32x4 v = *(const u32x4*)p;
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      }
+    }
+  }
+  out[(int64_t)blockIdx.x * 512 + threadIdx.x] = (float)(acc & 0xFFFFu);
+}
+
 // kinds 2..5 of attn_calibrate: the mixes above
 struct Mix {
   int waves;
@@ -142,6 +174,8 @@ hipError_t launch_calib(int kind, const uint32_t* seed, float* out, int64_t work
     case 3: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 8, 8>), grid, dim3(8 * 64), 0, stream, seed, out, iters); break;
     case 4: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 8, 4>), grid, dim3(4 * 64), 0, stream, seed, out, iters); break;
     case 5: hipLaunchKernelGGL((calib_mix_kernel<1, 1, 1, 0, 8>), grid, dim3(8 * 64), 0, stream, seed, out, iters); break;
+    case 7: hipLaunchKernelGGL(calib_lds_kernel<false>, grid, dim3(kCalWaves * 64), 0, stream, seed, out, iters); break;
+    case 8: hipLaunchKernelGGL(calib_lds_kernel<true>, grid, dim3(kCalWaves * 64), 0, stream, seed, out, iters); break;
     default:
       hipLaunchKernelGGL(calib_read_kernel, grid, dim3(kReadThreads), 0, stream, (const u32x4*)seed, out, iters);
       break;
@@ -154,6 +188,7 @@ int64_t calib_ops_per_workgroup(int kind, int iters) {
   if (kind == 0) return (int64_t)kCalWaves * iters * kChains * 32768;
   if (kind == 1) return (int64_t)kCalWaves * 64 * iters * 16;
   if (kind == 6) return (int64_t)kReadThreads * iters * 16;   // bytes read
+  if (kind == 7 || kind == 8) return (int64_t)kCalWaves * 64 * iters * 16 * (kind == 7 ? 16 : 8);   // LDS bytes read
   return (int64_t)kMix[kind - 2].waves * iters * 16 * 32768;
 }
 

@@ -276,10 +276,14 @@ int64_t attn_decode_workspace_floats(int64_t B, int64_t H, int64_t Nq, int64_t N
  * Kind 6 streams reads, the attainable rate of the HBM-bound kernels: workgroups of 256
  * threads each load one 16-byte element per iteration, the grid sweeping seed once front
  * to back, so seed must hold workgroups * 256 * iters 16-byte elements (only read); out
- * gets workgroups * 256 values. attn_calibrate_ops gives the operations (FLOPs,
- * exponentials for kind 1, bytes read for kind 6) of one workgroup, so that rate = ops *
- * workgroups / elapsed time. kind outside [0, 6], workgroups or iters < 1, or a NULL
- * pointer is ATTN_ERR_INVALID_ARG (attn_calibrate_ops returns -1). */
+ * gets workgroups * 256 values. Kinds 7 and 8 read LDS, the operand path of the
+ * attention kernels' MFMAs: 512-thread workgroups (one per CU) in which every lane reads
+ * 16 bytes (ds_read_b128, kind 7) or 8 bytes (the transpose read ds_read_b64_tr_b16, kind
+ * 8) per instruction, 16 instructions per iteration, from bank-disjoint addresses; seed and
+ * out as for kinds 0-5. attn_calibrate_ops gives the operations (FLOPs, exponentials for
+ * kind 1, bytes read for kinds 6-8) of one workgroup, so that rate = ops * workgroups /
+ * elapsed time. kind outside [0, 8], workgroups or iters < 1, or a NULL pointer is
+ * ATTN_ERR_INVALID_ARG (attn_calibrate_ops returns -1). */
 attn_status_t attn_calibrate(int kind, const uint32_t* seed, float* out, int64_t workgroups, int iters,
                              void* stream);
 int64_t attn_calibrate_ops(int kind, int iters);

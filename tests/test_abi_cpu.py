@@ -196,7 +196,7 @@ def test_decode_validation(lib, fn, defect, expect):
 
 
 @no_gpu_only
-@pytest.mark.parametrize("defect", [dict(kind=7), dict(kind=-1), dict(seed=None), dict(out=None), dict(wg=0),
+@pytest.mark.parametrize("defect", [dict(kind=9), dict(kind=-1), dict(seed=None), dict(out=None), dict(wg=0),
                                     dict(iters=0), dict(seed=A[0] + 4), dict(wg=1 << 33)])
 def test_calibrate_validation(lib, defect):
     args = dict(kind=0, seed=A[0], out=A[1], wg=256, iters=10)
@@ -211,7 +211,9 @@ def test_calibrate_ops(lib):
     assert lib.attn_calibrate_ops(2, 10) == 8 * 10 * 16 * 32768 and lib.attn_calibrate_ops(4, 10) == 4 * 10 * 16 * 32768
     # kind 6: 256 threads x iters x 16 bytes read
     assert lib.attn_calibrate_ops(6, 10) == 256 * 10 * 16
-    assert lib.attn_calibrate_ops(7, 10) == -1 and lib.attn_calibrate_ops(0, 0) == -1
+    # kinds 7, 8: 512 lanes x iters x 16 reads of 16 or 8 bytes
+    assert lib.attn_calibrate_ops(7, 10) == 512 * 10 * 16 * 16 and lib.attn_calibrate_ops(8, 10) == 512 * 10 * 16 * 8
+    assert lib.attn_calibrate_ops(9, 10) == -1 and lib.attn_calibrate_ops(0, 0) == -1
 
 
 @no_gpu_only
