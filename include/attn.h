@@ -59,7 +59,7 @@ typedef enum {
   ATTN_ERR_SCRATCH_TOO_SMALL = 4
 } attn_status_t;
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 /* bf16 Q/K/V in, bf16 O out (round to nearest even), fp32 LSE out. P is rounded to
  * bf16 before the P.V contraction; both contractions accumulate in fp32. The call
