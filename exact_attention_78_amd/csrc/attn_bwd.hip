@@ -248,8 +248,8 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
     f32x16 s, dp;                                   // S and dP of the current tile (own 32 queries)
     u32x4 keep[2];                                  // own P (dV) or dS (dK) of the previous tile, 16-bit
-    // The step is written in issue order, with scheduling fences, so that no phase's
-    // operand reads are hoisted into another (the registers would not hold them).
+    // Scheduling fences between the phases keep each phase's operand reads inside it (the
+    // registers would not hold them hoisted).
     constexpr int NMV = 4 * NDB;                    // MFMAs of the contraction per tile
     constexpr int EPM = 16 / NMV;                   // softmax elements beside each of them
     static_assert(EPM * NMV == 16, "the 16 elements spread evenly over the MFMAs");
@@ -277,9 +277,11 @@ __global__ __launch_bounds__(kWk * 64, 1) void attn_bwd_dkdv_kernel(
     // Step of tile u in slot CUR: loads of tile u + 1 into slot NXT (which held tile u - 2,
     // last read a step earlier); phase A: S and dP of tile u (A = Q / dO rows, B = K^T / V^T
     // in registers; accumulators from the offsets); the mask; phase C: the contraction of
-    // tile u - 1 (slot PRV; none in the first step), each MFMA followed by the softmax of
-    // one (d = 64: two) of the lane's 16 elements of tile u; then P and dS of tile u are
-    // packed, one kept, the other handed over. A wave whose queries all precede its keys
+    // tile u - 1 (slot PRV; none in the first step), written with the softmax of one (d =
+    // 64: two) of the lane's 16 elements of tile u after each MFMA (the compiler moves the
+    // exponentials after the last MFMA, next to the packing; pinned in place they ran no
+    // faster: the two waves of a SIMD overlap each other's softmax); then P and dS of tile u
+    // are packed, one kept, the other handed over. A wave whose queries all precede its keys
     // (causal, the first two tiles) computes fully masked blocks (P = dS = 0): the step's
     // length is set by the other waves.
     auto step = [&](auto CUR, auto PRV, auto NXT, auto FIRST, int u) __attribute__((always_inline)) {
