@@ -24,9 +24,11 @@
 //   P'' is never below P' = 2^kPShift * 2^(s - M), so probabilities down to 2^-15 of the
 //   max stay representable, and as the running max is raised by more than kTau only,
 //   P'' <= 1.5 * 2^(kPShift+kTau) = 384 stays below the E4M3 maximum (448).
-//   O is normalised by the sum of the *rounded* P'' codes times w: one more MFMA per tile,
-//   whose A operand is all ones (E4M3 1.0), sums the tile's codes exactly in fp32, and
-//   that sum times the tile's w is added to the denominator. Numerator and denominator
+//   O is normalised by the sum of the *rounded* P'' codes times w: one more MFMA per tile
+//   (the 16x16x128 form, half the cycles of the others) sums the tile's codes exactly in
+//   fp32, and that sum times the tile's w is added to the denominator. Its A operand is
+//   E4M3 1.0 in a pattern of lanes that makes each lane's output the sum for its own
+//   query row (see the construction of `ones`). Numerator and denominator
 //   then use the same weights, so a row dominated by one key returns that key's V row
 //   however P'' rounds. The LSE uses the sum of the unrounded fp32 probabilities.
 //   V^T is gathered with ds_read_b64_tr_b8 (8-bit LDS transpose reads) in the key order
@@ -50,6 +52,13 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // format 0 = E4M3 for both operands; E8M0 scale 127 = 2^0 (no block scaling in the MFMA)
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// The 16x16x128 form of the same instruction (half the cycles of the 32x32x64 form):
+// lane l holds A row l%16 and B column l%16 over the same block l/16 of k, and receives
+// C rows 4*(l/16) .. 4*(l/16)+3 of column l%16.
+__device__ __forceinline__ f32x4 mfma_fp8_16(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 // 8-bit LDS transpose read: within a 16-lane group, lane i receives byte (i % 8) of the
@@ -290,7 +299,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
     }
   };
 
-  f32x16 oacc[NDB], lacc = f32x16{};   // P''.V (in units of U) and the last tile's sum of rounded P''
+  f32x16 oacc[NDB];                    // P''.V (in units of U)
+  f32x4 lacc = f32x4{};                // the last tile's sum of rounded P''
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   // Running max M (log2 units), this lane's partial row sum of the unrounded
@@ -384,12 +394,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
 
   f32x16 Sa[NKB], Sb[NKB];
   int Pa[8] = {}, Pb[8] = {};
-  // all-ones A operand (E4M3 1.0) of the code-sum MFMA, kept in eight registers for the
-  // whole loop: eight distinct per-lane expressions (0 <= qrow < 2^31 - 8, so each shift
-  // adds 0) that the compiler can neither merge into one register nor fold to a constant
+  // A operand of the code-sum MFMA (16x16x128), which reads the P.V B operand as is. Seen
+  // as that MFMA's B, lane 16g + n holds 32 codes of query n + 16 (g % 2) (lanes l and
+  // l + 32 hold the two key halves of query l % 32); A row m is E4M3 1.0 on the k blocks
+  // g with g % 2 == (m / 4) % 2 and 0 elsewhere, so output rows 0-3 and 8-11 of column n
+  // hold the code sum of query n and rows 4-7 and 12-15 that of query n + 16: each lane
+  // receives its own query's sum (lane 16g + n gets rows 4g..4g+3). Kept in eight
+  // registers for the whole loop: eight distinct per-lane expressions (0 <= qrow < 2^31 - 8,
+  // so each shift adds 0) that the compiler can neither merge into one register nor fold.
   i32x8 ones;
+  const int ones_word = ((lane >> 4) & 1) == ((lane >> 2) & 1) ? 0x38383838 : 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) ones[k] = 0x38383838 + ((qrow + k) >> 31);
+  for (int k = 0; k < 8; ++k) ones[k] = ones_word + ((qrow + k) >> 31);
   bool pend = false;     // wave-uniform: an O rescale is owed
   // w of the tile whose code sum lacc holds, and of the tile whose softmax ran last; the
   // K and V block scales of the tile whose softmax runs next, loaded one step early so
@@ -434,7 +450,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
           if (db + 1 < NDB) vread(db + 1);
           const i32x8 pb = {P_use[0], P_use[1], P_use[2], P_use[3], P_use[4], P_use[5], P_use[6], P_use[7]};
           oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
-          if (db == NDB - 1) lacc = mfma_fp8(ones, pb, f32x16{});
+          if (db == NDB - 1) lacc = mfma_fp8_16(ones, pb, f32x4{});
         }
       } else {
       mask_tile(t + 1, S_soft);
@@ -498,7 +514,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_fp8_kernel(
         const i32x8 pb = {P_use[0], P_use[1], P_use[2], P_use[3], P_use[4], P_use[5], P_use[6], P_use[7]};
         oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
         if (db == NDB - 1) {
-          lacc = mfma_fp8(ones, pb, f32x16{});
+          lacc = mfma_fp8_16(ones, pb, f32x4{});
         }
         exps_slot(NQ - 2 + db);
       }
