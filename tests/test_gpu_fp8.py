@@ -434,3 +434,48 @@ def test_fp8_head_dim_64_every_row(causal):
     deq = [ofp8.dequantize_blocks(p[c], p[s_]) for c, s_ in (("q8", "sq"), ("k8", "sk"), ("v8", "sv"))]
     Oref, Lref = forward_pooled(*deq, causal, scale)
     compare(o_f.double().cpu().numpy(), l_f.double().cpu().numpy(), Oref, Lref, f"fp8 d64 causal={causal}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_row_dominated_by_one_key(causal, d):
+    # Closed form, no oracle. Key k is +-16 (E4M3) on channel k % d (+ for k < d, - above);
+    # query i is +-16 on the channel of its chosen key kappa(i) (kappa(i) <= i when causal),
+    # so kappa(i) scores 256, its sign twin -256 and every other key 0. Softmax then gives
+    # V's dequantised row kappa(i) up to N * exp(-256 * scale) * max|V| (every other key's
+    # weight is at most exp(-256 * scale) of kappa's), and LSE = 256 * scale. The kernel
+    # codes kappa's probability exactly (2^6) and carries keys seen before the row max
+    # reached kappa's tile down by the same rescale, so it meets that bound; a denominator
+    # summed over another row's codes would scale the row instead.
+    B, H, N = 1, 2, 2 * d - 3                      # d = 128: two V scale blocks, ragged tail
+    say(f"case fp8 row dominated by one key causal={causal} d={d} N={N}")
+    rng = np.random.default_rng(7800 + d + int(causal))
+    keys = np.arange(N)
+    q8 = np.zeros((B, H, N, d), np.uint8)
+    k8 = np.zeros((B, H, N, d), np.uint8)
+    v8 = rng.integers(0, 256, size=(B, H, N, d)).astype(np.uint8)
+    v8[(v8 & 0x7F) == 0x7F] = 0                    # no NaN codes
+    kappa = np.zeros((H, N), np.int64)
+    for h in range(H):
+        k8[0, h, keys, keys % d] = np.where(keys < d, 0x58, 0xD8).astype(np.uint8)
+        kappa[h] = (rng.random(N) * (keys + 1)).astype(np.int64) if causal else rng.integers(0, N, size=N)
+        q8[0, h, keys, kappa[h] % d] = np.where(kappa[h] < d, 0x58, 0xD8).astype(np.uint8)
+    nblk = (N + 127) // 128
+    ones = torch.ones((B, H, nblk), dtype=torch.float32)
+    sv = (0.5 * 6.0 ** torch.arange(nblk, dtype=torch.float32)).expand(B, H, nblk).contiguous()
+    scale = inputs.softmax_scale(d)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    O, L = attn_fwd_fp8(dev(q8), dev(k8), dev(v8), ones.cuda(), ones.cuda(), sv.cuda(), causal=causal,
+                        scale=scale)
+    torch.cuda.synchronize()
+    vdq = torch.from_numpy(v8).view(torch.float8_e4m3fn).double() * sv.double().repeat_interleave(128, dim=2)[:, :, :N, None]
+    expect = np.stack([vdq[0, h].numpy()[kappa[h]] for h in range(H)])[None]
+    got = O.double().cpu().numpy()
+    err = np.abs(got - expect).max()
+    bound = N * np.exp(-256.0 * float(scale)) * float(vdq.abs().max())
+    say(f"  max |O - V[kappa]| = {err:.3e} (softmax's own distance from V[kappa] <= {bound:.1e})")
+    assert np.all(np.abs(got - expect) <= 2.0 ** -8 * np.abs(expect) + bound), err
+    lse_expect = 256.0 * float(scale)
+    lerr = np.abs(L.double().cpu().numpy() - lse_expect).max()
+    say(f"  max |LSE - 256 scale| = {lerr:.3e}")
+    assert lerr <= LSE_REL * lse_expect, lerr
